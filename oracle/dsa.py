@@ -1,0 +1,171 @@
+"""Vectorised float64 oracle of the DSA forward path (test infrastructure only).
+
+Sources (page titles and sections; the pages print no code and no worked example):
+  [digest]  "DeepSeek-V3.2: Pushing the Frontier of Open Large Language Models", paper digest,
+            "Key claims" (paper section 2.1, Eq. 1-2 and Fig. 2) and "Method".
+  [36kr]    36kr article on DeepSeek-V3.2, section "02. Built on the final version of
+            DeepSeek-V3.1, DSA makes model computation smarter".
+  [blog]    aitoearn blog "DeepSeek V3.2 series", "Technical Innovations in V3.2" and
+            "Training Process", Phase 2 (2,048 key-value pairs per query token).
+
+Conventions (readings where the pages are silent; each is listed with its reason in the design
+notes of the repository):
+  * Sequence b has m_b query rows and n_b keys; query i of b sits at position pos = n_b - m_b + i
+    and its candidates are keys s = 0..pos (inclusive: "all preceding tokens" is read as the
+    causal prefix including the token itself, otherwise position 0 has nothing to attend to).
+  * Scores are float64; no scale factors are applied to the FP8 inputs.
+  * Top-k: the min(k, pos+1) candidates with the largest score; equal scores prefer the lower
+    position (+0 and -0 are equal); the chosen positions are returned in ascending order and the
+    list is padded to k with -1.
+  * Attention: key = all d_qk dims of the selected latent row, value = its first d_v dims;
+    logits = scale * q . key with a natural-base softmax; lse = max + ln(sum of exp).
+    Index -1 and indices outside [0, n_b) are skipped; a row with no valid index gives out = 0 and
+    lse = -inf. Repeated indices count as many times as they appear.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+from .numerics import decode
+
+
+@dataclass
+class Seqs:
+    """Ragged batch description: cumulative query / key row counts per sequence."""
+    cu_seqlens_q: np.ndarray
+    cu_seqlens_k: np.ndarray
+
+    def __post_init__(self):
+        self.cu_seqlens_q = np.asarray(self.cu_seqlens_q, np.int64)
+        self.cu_seqlens_k = np.asarray(self.cu_seqlens_k, np.int64)
+
+    @property
+    def num_seqs(self):
+        return len(self.cu_seqlens_q) - 1
+
+    @property
+    def T(self):
+        return int(self.cu_seqlens_q[-1])
+
+    def locate(self, r: int):
+        """Query row r -> (sequence b, position pos, first key row of b, n_b)."""
+        b = int(np.searchsorted(self.cu_seqlens_q, r, side="right") - 1)
+        m = self.cu_seqlens_q[b + 1] - self.cu_seqlens_q[b]
+        n = self.cu_seqlens_k[b + 1] - self.cu_seqlens_k[b]
+        i = r - self.cu_seqlens_q[b]
+        return b, int(n - m + i), int(self.cu_seqlens_k[b]), int(n)
+
+
+# ------------------------------------------------------------------ step 1: lightning indexer
+
+def indexer_scores_row(seqs: Seqs, qI, kI, w, r: int) -> np.ndarray:
+    """I[r, s] for s = 0..pos(r) ([digest] Key claims, Eq. 1; [36kr] section 02).
+
+    I[r, s] = sum_j w[r, j] * max(0, sum_d qI[r, j, d] * kI[s, d]).
+    qI: [T, H_I, d_I], kI: [Nk, d_I] (stored codes or floats), w: [T, H_I] float.
+    """
+    _, pos, k0, _ = seqs.locate(r)
+    q = decode(qI[r])                              # [H_I, d_I]
+    keys = decode(kI[k0:k0 + pos + 1])             # [pos+1, d_I]
+    dots = q @ keys.T                              # [H_I, pos+1]
+    return decode(w[r]) @ np.maximum(dots, 0.0)    # [pos+1]
+
+
+def indexer_scores(seqs: Seqs, qI, kI, w, rows=None) -> list:
+    """List of score rows (one float64 array of length pos+1 per requested row)."""
+    rows = range(seqs.T) if rows is None else rows
+    return [indexer_scores_row(seqs, qI, kI, w, int(r)) for r in rows]
+
+
+def indexer_error_bound_row(seqs: Seqs, qI, kI, w, r: int) -> np.ndarray:
+    """Forward error bound for an fp32 evaluation of I[r, :] in any summation order.
+
+    eps[s] = 4 * gamma(d_I + H_I + 1) * sum_j |w[r,j]| * sum_d |qI[r,j,d] * kI[s,d]|,
+    gamma(n) = n u / (1 - n u), u = 2^-24 (recursive-summation bound; factor 4 of margin for
+    the unknown accumulation order inside a matrix instruction).
+    """
+    _, pos, k0, _ = seqs.locate(r)
+    q = np.abs(decode(qI[r]))
+    keys = np.abs(decode(kI[k0:k0 + pos + 1]))
+    H_I, d_I = q.shape
+    u = 2.0 ** -24
+    n = d_I + H_I + 1
+    gamma = n * u / (1 - n * u)
+    return 4.0 * gamma * (np.abs(decode(w[r])) @ (q @ keys.T))
+
+
+# ------------------------------------------------------------------ step 2: top-k selection
+
+def topk_row(scores: np.ndarray, k: int) -> np.ndarray:
+    """Top-k of one causal score row ([36kr] section 02: keep the key-value entries with the
+    top-k index scores; [digest] Key claims, Eq. 2).
+
+    Candidates are ordered by (score descending, position ascending); the first min(k, n)
+    positions are returned sorted ascending and padded with -1 to length k.
+    """
+    scores = np.asarray(scores, np.float64)
+    n = scores.shape[0]
+    order = np.argsort(-scores, kind="stable")     # stable: equal scores keep position order
+    take = np.sort(order[:min(k, n)])
+    out = np.full(k, -1, np.int32)
+    out[:take.shape[0]] = take
+    return out
+
+
+def topk(score_rows: list, k: int) -> np.ndarray:
+    return np.stack([topk_row(s, k) for s in score_rows]) if score_rows else np.zeros((0, k), np.int32)
+
+
+# ------------------------------------------------------------------ step 3: sparse MLA attention
+
+def attn_row(seqs: Seqs, q, kv, indices_row, scale: float, d_v: int, r: int):
+    """Attention of every head of query row r over its selected latent rows.
+
+    MLA in MQA mode ([digest] Key claims, Fig. 2; Method): one latent row per key is shared by
+    all query heads of the token; key = the whole row, value = its first d_v dims.
+    Returns (out [H, d_v] float64, lse [H] float64).
+    """
+    _, _, k0, n = seqs.locate(r)
+    qr = decode(q[r])                                             # [H, d_qk]
+    idx = np.asarray(indices_row, np.int64)
+    idx = idx[(idx >= 0) & (idx < n)]
+    H = qr.shape[0]
+    if idx.shape[0] == 0:
+        return np.zeros((H, d_v)), np.full(H, -np.inf)
+    c = decode(kv[k0 + idx])                                      # [|S|, d_qk]
+    z = scale * (qr @ c.T)                                        # [H, |S|]
+    m = z.max(axis=1, keepdims=True)
+    e = np.exp(z - m)
+    l = e.sum(axis=1, keepdims=True)
+    out = (e / l) @ c[:, :d_v]
+    lse = (m + np.log(l))[:, 0]
+    return out, lse
+
+
+def sparse_mla_attn(seqs: Seqs, q, kv, indices, scale: float, d_v: int, rows=None):
+    """out [R, H, d_v], lse [R, H] for the requested rows (default: all)."""
+    rows = list(range(seqs.T)) if rows is None else [int(r) for r in rows]
+    outs, lses = [], []
+    for i, r in enumerate(rows):
+        o, l = attn_row(seqs, q, kv, indices[i], scale, d_v, r)
+        outs.append(o)
+        lses.append(l)
+    if not outs:
+        return np.zeros((0, 0, d_v)), np.zeros((0, 0))
+    return np.stack(outs), np.stack(lses)
+
+
+# ------------------------------------------------------------------ composition
+
+def forward_rows(seqs: Seqs, qI, kI, w, q, kv, k: int, scale: float, d_v: int, rows=None):
+    """Indexer -> top-k -> attention for the requested rows.
+
+    Returns dict(scores=list of rows, indices [R, k], out [R, H, d_v], lse [R, H]).
+    """
+    rows = list(range(seqs.T)) if rows is None else [int(r) for r in rows]
+    sc = indexer_scores(seqs, qI, kI, w, rows)
+    idx = topk(sc, k)
+    out, lse = sparse_mla_attn(seqs, q, kv, idx, scale, d_v, rows)
+    return dict(scores=sc, indices=idx, out=out, lse=lse)
