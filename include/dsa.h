@@ -1,0 +1,175 @@
+/*
+ * dsa.h -- C ABI of the DeepSeek Sparse Attention (DSA) forward path on MI355X (gfx950).
+ *
+ * The operation (DeepSeek-V3.2 paper digest, "Key claims", paper section 2.1, Eq. 1-2 and
+ * Fig. 2; "Method"; 36kr article, section "02. Built on the final version of DeepSeek-V3.1"):
+ *
+ *   1. lightning indexer: for each query token t and each key s at or before it,
+ *        I[t,s] = sum_j w[t,j] * ReLU(qI[t,j] . kI[s])        (H_I indexer heads, FP8 inputs)
+ *   2. fine-grained selection: keep the k keys with the largest I[t,:]
+ *   3. MLA in MQA mode: every one of the H query heads of token t attends (softmax) only to the
+ *      selected entries of one latent vector per key that all heads share; key = the whole
+ *      latent row (d_qk dims), value = its first d_v dims.
+ *
+ * Conventions used by every entry point
+ *   - Ragged batches. Sequence b has m_b query rows and n_b keys (m_b <= n_b). Query rows of all
+ *     sequences are stacked (T = sum m_b rows), keys likewise (Nk = sum n_b rows). Query i of
+ *     sequence b sits at position pos = n_b - m_b + i; its candidates are keys 0..pos of its own
+ *     sequence (inclusive). A prefill is m_b = n_b, a decode step m_b = 1.
+ *   - Positions in score rows and index lists are sequence-local (0..n_b-1).
+ *   - Tensor pointers are device pointers to dense row-major arrays, 16-byte aligned, unless
+ *     marked [host]. Shapes are given in brackets, innermost dimension last.
+ *   - Storage types: DSA_FP8_E4M3 = OCP FP8 E4M3 ("e4m3fn": bias 7, no infinities, max 448)
+ *     as one byte per value; DSA_BF16 = bfloat16; DSA_F32 = IEEE binary32. Inputs are taken as
+ *     they are: the library never quantises and applies no scale factors.
+ *   - Ownership. The caller allocates and frees every buffer, including workspaces. The
+ *     library does not allocate device memory and keeps no state between calls apart from a
+ *     cached device-property query. All work is enqueued on `stream` (a hipStream_t; NULL is
+ *     the default stream) and returns without waiting; results are valid once the stream has
+ *     reached that point, and inputs must stay untouched until then.
+ *   - Errors. Arguments are validated on the host before anything is enqueued; on failure the
+ *     call returns a non-zero status, enqueues nothing, and dsa_last_error() describes the
+ *     problem (thread-local text). A failed kernel launch returns DSA_ERR_HIP. Faults inside a
+ *     kernel surface at the caller's next stream synchronisation. No C++ exception crosses
+ *     this interface.
+ *   - Inputs must be finite; NaN or infinite inputs give unspecified results.
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSA_ABI_VERSION 1
+
+typedef enum {
+  DSA_OK = 0,
+  DSA_ERR_NULL = 1,        /* a required pointer is NULL                                     */
+  DSA_ERR_SHAPE = 2,       /* sizes inconsistent (negative, m_b > n_b, ld too small, ...)    */
+  DSA_ERR_DTYPE = 3,       /* storage type not allowed for this argument                     */
+  DSA_ERR_ALIGN = 4,       /* a device pointer is not 16-byte aligned                        */
+  DSA_ERR_WORKSPACE = 5,   /* workspace pointer NULL or smaller than the *_workspace_size    */
+  DSA_ERR_UNSUPPORTED = 6, /* valid request that this build does not implement              */
+  DSA_ERR_HIP = 7          /* a HIP runtime call or kernel launch failed                     */
+} dsa_status_t;
+
+typedef enum { DSA_F32 = 0, DSA_BF16 = 1, DSA_FP8_E4M3 = 2 } dsa_dtype_t;
+
+/* A ragged batch of sequences. The device and host arrays must hold the same values. The
+ * host copies are read during the call only (validation and launch planning); the device
+ * copies are read by the kernels. */
+typedef struct {
+  int32_t num_seqs;                    /* B >= 0; B == 0 makes every call a no-op            */
+  const int32_t* cu_seqlens_q;         /* [B+1] device: 0 = c_0 <= c_1 <= ... = T            */
+  const int32_t* cu_seqlens_k;         /* [B+1] device: 0 = c_0 <= c_1 <= ... = Nk           */
+  const int32_t* cu_seqlens_q_host;    /* [B+1] [host] same values                            */
+  const int32_t* cu_seqlens_k_host;    /* [B+1] [host] same values                            */
+  int32_t max_seqlen_q;                /* max m_b (must equal the true maximum)              */
+  int32_t max_seqlen_k;                /* max n_b (must equal the true maximum)              */
+} dsa_seqs_t;
+
+/* ---------------------------------------------------------------- step 1: lightning indexer
+ * I[r,s] = sum_{j<H_I} w[r,j] * max(0, sum_{d<d_I} qI[r,j,d] * kI[kofs_b + s, d])
+ * for every query row r (sequence b, position pos) and s = 0..pos.
+ * (paper digest, "Key claims": paper section 2.1, Eq. 1; ReLU, few heads, FP8.)
+ *
+ *   qk_dtype  DSA_FP8_E4M3 (H_I = 64, d_I = 128: FP8 matrix-core path) or DSA_F32 (any
+ *             1 <= H_I <= 128, 1 <= d_I <= 256: vector path). Accumulation is fp32.
+ *   q_idx     [T, H_I, d_I] of qk_dtype        indexer queries
+ *   k_idx     [Nk, d_I]     of qk_dtype        indexer keys, one per key token, shared by heads
+ *   w         [T, H_I] fp32                    per-token head weights
+ *   scores    [T, ld_scores] fp32 (output)     row r holds I[r, 0..pos]; entries beyond pos are
+ *             left unspecified (they may be overwritten). ld_scores >= max_seqlen_k, and a
+ *             multiple of 4.
+ */
+dsa_status_t dsa_indexer_scores(const dsa_seqs_t* seqs, int32_t H_I, int32_t d_I,
+                                dsa_dtype_t qk_dtype, const void* q_idx, const void* k_idx,
+                                const float* w, float* scores, int64_t ld_scores, void* stream);
+
+/* ---------------------------------------------------------------- step 2: top-k selection
+ * For each row r: the min(k, pos+1) positions s <= pos with the largest scores[r, s]
+ * (36kr article section 02: keep the entries with the top-k index scores; paper digest
+ * "Key claims", Eq. 2). Ties prefer the lower position; +0 and -0 are equal. The positions are
+ * written in ascending order to indices[r, 0..], and the rest of the row is filled with -1.
+ *
+ *   scores   [T, ld_scores] fp32, finite in 0..pos of every row (entries beyond are not read)
+ *   k        1 <= k <= 16384
+ *   indices  [T, k] int32 (output)
+ *   ws       device workspace of at least dsa_topk_workspace_size(seqs, k) bytes (may be NULL
+ *            when that size is 0); its contents on entry do not matter.
+ */
+size_t dsa_topk_workspace_size(const dsa_seqs_t* seqs, int32_t k);
+dsa_status_t dsa_topk(const dsa_seqs_t* seqs, const float* scores, int64_t ld_scores, int32_t k,
+                      int32_t* indices, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- step 3: sparse MLA attention
+ * For each row r (sequence b) and head h, over the selected set S = { s in indices[r, :] :
+ * 0 <= s < n_b } (entries -1 or out of range are skipped; repeats count as often as listed):
+ *   z_s        = softmax_scale * sum_{d<d_qk} q[r,h,d] * kv[kofs_b + s, d]
+ *   out[r,h,:] = sum_s softmax(z)_s * kv[kofs_b + s, 0:d_v]
+ *   lse[r,h]   = ln sum_s exp(z_s)
+ * A row with an empty S gives out = 0 and lse = -inf.
+ * (paper digest "Key claims", Fig. 2 and "Method": MLA in MQA mode, one latent row per key
+ * shared by all query heads, attended only at the selected entries.)
+ *
+ *   dtype    DSA_BF16 with (H, d_qk, d_v) = (128, 576, 512) (matrix-core path), or DSA_F32 with
+ *            1 <= H <= 128, 1 <= d_v <= d_qk <= 1024 (vector path)
+ *   q        [T, H, d_qk] of dtype         queries already in the latent space
+ *   kv       [Nk, d_qk] of dtype           latent cache (value = the first d_v dims)
+ *   indices  [T, k] int32                  1 <= k <= 16384
+ *   out      [T, H, d_v] of dtype (output; bf16 rounded to nearest even)
+ *   lse      [T, H] fp32 (output) or NULL
+ *   ws       device workspace of at least dsa_sparse_mla_attn_workspace_size(...) bytes
+ */
+size_t dsa_sparse_mla_attn_workspace_size(const dsa_seqs_t* seqs, int32_t H, int32_t d_qk,
+                                          int32_t d_v, int32_t k, dsa_dtype_t dtype);
+dsa_status_t dsa_sparse_mla_attn(const dsa_seqs_t* seqs, int32_t H, int32_t d_qk, int32_t d_v,
+                                 dsa_dtype_t dtype, const void* q, const void* kv,
+                                 const int32_t* indices, int32_t k, float softmax_scale,
+                                 void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- fused forward (1 -> 2 -> 3)
+ * Runs the three steps above on one stream for prefill and decode batches alike. Scores and
+ * indices live in the workspace unless the caller asks for them through scores_out /
+ * indices_out (then they are written there and also kept as the intermediate).
+ */
+typedef struct {
+  /* indexer */
+  int32_t H_I, d_I;
+  dsa_dtype_t qk_dtype;
+  const void* q_idx;            /* [T, H_I, d_I] */
+  const void* k_idx;            /* [Nk, d_I]     */
+  const float* w;               /* [T, H_I]      */
+  /* selection */
+  int32_t k;
+  /* attention */
+  int32_t H, d_qk, d_v;
+  dsa_dtype_t dtype;
+  const void* q;                /* [T, H, d_qk]  */
+  const void* kv;               /* [Nk, d_qk]    */
+  float softmax_scale;
+  void* out;                    /* [T, H, d_v]   */
+  float* lse;                   /* [T, H] or NULL */
+  /* optional intermediates */
+  float* scores_out;            /* [T, ld_scores_out] or NULL */
+  int64_t ld_scores_out;
+  int32_t* indices_out;         /* [T, k] or NULL */
+} dsa_forward_args_t;
+
+size_t dsa_forward_workspace_size(const dsa_seqs_t* seqs, const dsa_forward_args_t* args);
+dsa_status_t dsa_forward(const dsa_seqs_t* seqs, const dsa_forward_args_t* args, void* ws,
+                         size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- misc */
+const char* dsa_status_string(dsa_status_t status); /* static text, never NULL               */
+const char* dsa_last_error(void);                   /* thread-local detail of the last error */
+int32_t dsa_abi_version(void);                      /* DSA_ABI_VERSION of the built library  */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSA_H */

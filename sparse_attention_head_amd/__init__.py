@@ -1,0 +1,267 @@
+"""Python binding of libdsa.so, the MI355X (gfx950) DeepSeek Sparse Attention forward path.
+
+Argument marshalling only: every step runs in the HIP kernels behind the C ABI of
+include/dsa.h. Tensors are torch tensors on the GPU (PyTorch provides device memory and the
+current stream); sequence descriptions are cumulative row counts.
+
+    import sparse_attention_head_amd as dsa
+    seqs = dsa.Seqs(cu_seqlens_q, cu_seqlens_k)          # int32 lists / arrays
+    scores = dsa.indexer_scores(seqs, q_idx, k_idx, w)    # [T, ld] fp32
+    idx = dsa.topk(seqs, scores, k)                       # [T, k] int32
+    out, lse = dsa.sparse_mla_attn(seqs, q, kv, idx, scale)
+    out, lse = dsa.forward(seqs, q_idx, k_idx, w, q, kv, k, scale)
+
+FP8 tensors are passed as torch.float8_e4m3fn (or uint8 codes), bf16 as torch.bfloat16.
+If the library has not been built, importing this package raises ImportError: there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa.so")
+
+if not os.path.exists(_LIB_PATH):
+    raise ImportError(f"{_LIB_PATH} is missing; build it with `python -m sparse_attention_head_amd.build`")
+
+_lib = ctypes.CDLL(_LIB_PATH)
+
+# ---------------------------------------------------------------- C types
+
+DSA_OK, DSA_ERR_NULL, DSA_ERR_SHAPE, DSA_ERR_DTYPE, DSA_ERR_ALIGN, DSA_ERR_WORKSPACE, \
+    DSA_ERR_UNSUPPORTED, DSA_ERR_HIP = range(8)
+DSA_F32, DSA_BF16, DSA_FP8_E4M3 = 0, 1, 2
+
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_vp = ctypes.c_void_p
+
+
+class _Seqs(ctypes.Structure):
+    _fields_ = [("num_seqs", ctypes.c_int32),
+                ("cu_seqlens_q", _vp), ("cu_seqlens_k", _vp),
+                ("cu_seqlens_q_host", _vp), ("cu_seqlens_k_host", _vp),
+                ("max_seqlen_q", ctypes.c_int32), ("max_seqlen_k", ctypes.c_int32)]
+
+
+class _FwdArgs(ctypes.Structure):
+    _fields_ = [("H_I", ctypes.c_int32), ("d_I", ctypes.c_int32), ("qk_dtype", ctypes.c_int),
+                ("q_idx", _vp), ("k_idx", _vp), ("w", _vp),
+                ("k", ctypes.c_int32),
+                ("H", ctypes.c_int32), ("d_qk", ctypes.c_int32), ("d_v", ctypes.c_int32),
+                ("dtype", ctypes.c_int), ("q", _vp), ("kv", _vp), ("softmax_scale", ctypes.c_float),
+                ("out", _vp), ("lse", _vp),
+                ("scores_out", _vp), ("ld_scores_out", ctypes.c_int64), ("indices_out", _vp)]
+
+
+def _proto(name, res, args):
+    f = getattr(_lib, name)
+    f.restype = res
+    f.argtypes = args
+    return f
+
+
+_c_indexer = _proto("dsa_indexer_scores", ctypes.c_int,
+                    [ctypes.POINTER(_Seqs), ctypes.c_int32, ctypes.c_int32, ctypes.c_int, _vp, _vp, _vp,
+                     _vp, ctypes.c_int64, _vp])
+_c_topk_ws = _proto("dsa_topk_workspace_size", ctypes.c_size_t, [ctypes.POINTER(_Seqs), ctypes.c_int32])
+_c_topk = _proto("dsa_topk", ctypes.c_int,
+                 [ctypes.POINTER(_Seqs), _vp, ctypes.c_int64, ctypes.c_int32, _vp, _vp, ctypes.c_size_t, _vp])
+_c_attn_ws = _proto("dsa_sparse_mla_attn_workspace_size", ctypes.c_size_t,
+                    [ctypes.POINTER(_Seqs), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                     ctypes.c_int])
+_c_attn = _proto("dsa_sparse_mla_attn", ctypes.c_int,
+                 [ctypes.POINTER(_Seqs), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int, _vp, _vp,
+                  _vp, ctypes.c_int32, ctypes.c_float, _vp, _vp, _vp, ctypes.c_size_t, _vp])
+_c_fwd_ws = _proto("dsa_forward_workspace_size", ctypes.c_size_t, [ctypes.POINTER(_Seqs), ctypes.POINTER(_FwdArgs)])
+_c_fwd = _proto("dsa_forward", ctypes.c_int,
+                [ctypes.POINTER(_Seqs), ctypes.POINTER(_FwdArgs), _vp, ctypes.c_size_t, _vp])
+_c_status = _proto("dsa_status_string", ctypes.c_char_p, [ctypes.c_int])
+_c_last = _proto("dsa_last_error", ctypes.c_char_p, [])
+_c_abi = _proto("dsa_abi_version", ctypes.c_int32, [])
+
+EXPORTS = ("dsa_indexer_scores", "dsa_topk_workspace_size", "dsa_topk", "dsa_sparse_mla_attn_workspace_size",
+           "dsa_sparse_mla_attn", "dsa_forward_workspace_size", "dsa_forward", "dsa_status_string",
+           "dsa_last_error", "dsa_abi_version")
+
+
+class DSAError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        self.status = status
+        super().__init__(f"{call}: {_c_status(status).decode()} ({_c_last().decode()})")
+
+
+def _check(st, call):
+    if st != DSA_OK:
+        raise DSAError(st, call)
+
+
+def abi_version() -> int:
+    return int(_c_abi())
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+# ---------------------------------------------------------------- marshalling helpers
+
+def _torch():
+    import torch
+    return torch
+
+
+class Seqs:
+    """A ragged batch: cu_seqlens_q / cu_seqlens_k (length B+1, starting at 0).
+
+    Keeps host copies (read by the library for validation and planning) and device copies
+    (read by the kernels). `device` defaults to the current CUDA device.
+    """
+
+    def __init__(self, cu_seqlens_q, cu_seqlens_k, device=None):
+        torch = _torch()
+        self.cu_q_host = np.ascontiguousarray(np.asarray(cu_seqlens_q, dtype=np.int32))
+        self.cu_k_host = np.ascontiguousarray(np.asarray(cu_seqlens_k, dtype=np.int32))
+        self.B = len(self.cu_q_host) - 1
+        dev = device if device is not None else torch.device("cuda", torch.cuda.current_device())
+        self.cu_q = torch.from_numpy(self.cu_q_host).to(dev)
+        self.cu_k = torch.from_numpy(self.cu_k_host).to(dev)
+        m = np.diff(self.cu_q_host) if self.B > 0 else np.zeros(0, np.int32)
+        n = np.diff(self.cu_k_host) if self.B > 0 else np.zeros(0, np.int32)
+        self.max_m = int(m.max()) if self.B > 0 else 0
+        self.max_n = int(n.max()) if self.B > 0 else 0
+        self.T = int(self.cu_q_host[-1]) if self.B >= 0 and len(self.cu_q_host) else 0
+        self.Nk = int(self.cu_k_host[-1]) if len(self.cu_k_host) else 0
+
+    def c(self) -> _Seqs:
+        s = _Seqs()
+        s.num_seqs = self.B
+        s.cu_seqlens_q = self.cu_q.data_ptr() if self.B > 0 else None
+        s.cu_seqlens_k = self.cu_k.data_ptr() if self.B > 0 else None
+        s.cu_seqlens_q_host = self.cu_q_host.ctypes.data
+        s.cu_seqlens_k_host = self.cu_k_host.ctypes.data
+        s.max_seqlen_q = self.max_m
+        s.max_seqlen_k = self.max_n
+        return s
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream=None):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return DSA_F32
+    if t.dtype == torch.bfloat16:
+        return DSA_BF16
+    if t.dtype in (torch.float8_e4m3fn, torch.uint8):
+        return DSA_FP8_E4M3
+    raise TypeError(f"unsupported tensor dtype {t.dtype}")
+
+
+def scores_ld(max_seqlen_k: int) -> int:
+    return max(4, (max_seqlen_k + 3) // 4 * 4)
+
+
+# ---------------------------------------------------------------- the four calls
+
+def indexer_scores(seqs: Seqs, q_idx, k_idx, w, scores=None, stream=None):
+    """I[r, s] for s <= pos(r); returns scores [T, ld] fp32 (entries beyond pos unspecified)."""
+    torch = _torch()
+    H_I, d_I = int(q_idx.shape[1]), int(q_idx.shape[2])
+    if scores is None:
+        scores = torch.empty((seqs.T, scores_ld(seqs.max_n)), dtype=torch.float32, device=q_idx.device)
+    cs = seqs.c()
+    _check(_c_indexer(ctypes.byref(cs), H_I, d_I, _dtype_code(q_idx), _ptr(q_idx), _ptr(k_idx), _ptr(w),
+                      _ptr(scores), int(scores.stride(0)), _stream(stream)), "dsa_indexer_scores")
+    return scores
+
+
+def topk(seqs: Seqs, scores, k: int, indices=None, stream=None):
+    """Top-k positions per row: ascending, ties to the lower position, -1 padded."""
+    torch = _torch()
+    if indices is None:
+        indices = torch.empty((seqs.T, k), dtype=torch.int32, device=scores.device)
+    cs = seqs.c()
+    wsz = int(_c_topk_ws(ctypes.byref(cs), k))
+    ws = torch.empty(max(wsz, 1), dtype=torch.uint8, device=scores.device) if wsz else None
+    _check(_c_topk(ctypes.byref(cs), _ptr(scores), int(scores.stride(0)), k, _ptr(indices), _ptr(ws), wsz,
+                   _stream(stream)), "dsa_topk")
+    return indices
+
+
+def sparse_mla_attn(seqs: Seqs, q, kv, indices, scale: float, d_v: int = None, out=None, lse=None,
+                    with_lse=True, stream=None):
+    """Attention of every head over the selected latent rows; returns (out, lse)."""
+    torch = _torch()
+    T, H, d_qk = (int(x) for x in q.shape)
+    if d_v is None:
+        d_v = 512 if d_qk == 576 else d_qk
+    k = int(indices.shape[1])
+    if out is None:
+        out = torch.empty((T, H, d_v), dtype=q.dtype, device=q.device)
+    if lse is None and with_lse:
+        lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
+    cs = seqs.c()
+    dt = _dtype_code(q)
+    wsz = int(_c_attn_ws(ctypes.byref(cs), H, d_qk, d_v, k, dt))
+    ws = torch.empty(max(wsz, 1), dtype=torch.uint8, device=q.device) if wsz else None
+    _check(_c_attn(ctypes.byref(cs), H, d_qk, d_v, dt, _ptr(q), _ptr(kv), _ptr(indices), k, float(scale),
+                   _ptr(out), _ptr(lse), _ptr(ws), wsz, _stream(stream)), "dsa_sparse_mla_attn")
+    return out, lse
+
+
+class Forward:
+    """Fused indexer -> top-k -> attention with a reusable workspace (one allocation per shape)."""
+
+    def __init__(self, seqs: Seqs, q_idx, k_idx, w, q, kv, k: int, scale: float, d_v: int = None,
+                 keep_scores=False, keep_indices=False, with_lse=True):
+        torch = _torch()
+        self.seqs = seqs
+        T, H, d_qk = (int(x) for x in q.shape)
+        d_v = d_v if d_v is not None else (512 if d_qk == 576 else d_qk)
+        dev = q.device
+        self.out = torch.empty((T, H, d_v), dtype=q.dtype, device=dev)
+        self.lse = torch.empty((T, H), dtype=torch.float32, device=dev) if with_lse else None
+        self.scores = (torch.empty((T, scores_ld(seqs.max_n)), dtype=torch.float32, device=dev)
+                       if keep_scores else None)
+        self.indices = torch.empty((T, k), dtype=torch.int32, device=dev) if keep_indices else None
+        a = _FwdArgs()
+        a.H_I, a.d_I = int(q_idx.shape[1]), int(q_idx.shape[2])
+        a.qk_dtype = _dtype_code(q_idx)
+        a.q_idx, a.k_idx, a.w = _ptr(q_idx), _ptr(k_idx), _ptr(w)
+        a.k = k
+        a.H, a.d_qk, a.d_v = H, d_qk, d_v
+        a.dtype = _dtype_code(q)
+        a.q, a.kv = _ptr(q), _ptr(kv)
+        a.softmax_scale = float(scale)
+        a.out, a.lse = _ptr(self.out), _ptr(self.lse)
+        a.scores_out = _ptr(self.scores)
+        a.ld_scores_out = int(self.scores.stride(0)) if self.scores is not None else 0
+        a.indices_out = _ptr(self.indices)
+        self._args = a
+        self._keep = (q_idx, k_idx, w, q, kv)  # keep the inputs alive while the object lives
+        self._cs = seqs.c()
+        wsz = int(_c_fwd_ws(ctypes.byref(self._cs), ctypes.byref(a)))
+        self.ws_bytes = wsz
+        self.ws = torch.empty(max(wsz, 1), dtype=torch.uint8, device=dev)
+
+    def __call__(self, stream=None):
+        _check(_c_fwd(ctypes.byref(self._cs), ctypes.byref(self._args), _ptr(self.ws), self.ws_bytes,
+                      _stream(stream)), "dsa_forward")
+        return self.out, self.lse
+
+
+def forward(seqs: Seqs, q_idx, k_idx, w, q, kv, k: int, scale: float, d_v: int = None, stream=None):
+    """One fused forward; returns (out, lse)."""
+    f = Forward(seqs, q_idx, k_idx, w, q, kv, k, scale, d_v)
+    return f(stream)

@@ -1,0 +1,385 @@
+// Sparse MLA attention in MQA mode on gfx950.
+//
+// For each query row and head, softmax attention over the selected latent rows only; one latent
+// row per key is shared by all query heads of the token (DeepSeek-V3.2 paper digest, "Key
+// claims": paper section 2.1, Eq. 2 and Fig. 2; "Method": MLA's MQA mode, so every selected KV
+// entry is shared across the query heads). Key = the whole d_qk-dim row, value = its first d_v
+// dims.
+//
+// BF16 matrix path (H = 128, d_qk = 576, d_v = 512), one workgroup per query row, 4 waves, wave w
+// owns heads 32w..32w+31:
+//   * the selected rows are gathered 64 at a time from HBM straight into LDS with
+//     global_load_lds_dwordx4 (no register staging), double buffered: 2 x 72 KB;
+//   * S^T = K Q^T (M = 64 keys, N = 32 heads, K = 576) with v_mfma_f32_32x32x16_bf16; the query
+//     block of the wave stays in registers as the B operand for the whole row;
+//   * online softmax in fp32 on S^T (each lane owns one head, so the running max and sum are
+//     per lane); rescaling of the output is skipped while the running max grows by < 2^8;
+//   * O^T += V^T P^T (M = 512 value dims, N = 32 heads, K = 64 keys); P never leaves registers:
+//     the S^T accumulator layout is used directly as the B operand, and V^T is read from LDS with
+//     the same permutation of the key index.
+// LDS layout of a gathered block: 72 column chunks of 16 bytes; chunk c of key s lives in 16-byte
+// slot c*64 + (s ^ (c & 7)). The XOR spreads the value dims of one key over the banks for the
+// transposing V^T reads; for every read it splits into loop-invariant lane bits and compile-time
+// bits, so each LDS read is one of a few per-lane base registers plus an immediate offset.
+#include "dsa_internal.h"
+#include "device_common.h"
+
+namespace dsa {
+
+// ---------------------------------------------------------------------------- fp32 vector path
+
+constexpr int AF_THREADS = 256;
+
+__device__ __forceinline__ float block_reduce(float v, bool is_max, float* red) {
+  for (int off = 32; off > 0; off >>= 1) {
+    const float o = __shfl_xor(v, off);
+    v = is_max ? fmaxf(v, o) : v + o;
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  v = red[0];
+  for (int i = 1; i < AF_THREADS / 64; ++i) v = is_max ? fmaxf(v, red[i]) : v + red[i];
+  return v;
+}
+
+__global__ void __launch_bounds__(AF_THREADS)
+attn_f32_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int H,
+                int d_qk, int d_v, const float* __restrict__ q, const float* __restrict__ kv,
+                const int32_t* __restrict__ idx, int k, float scale, float* __restrict__ out,
+                float* __restrict__ lse) {
+  extern __shared__ float sm[];  // q vector [d_qk], logits [k], reduction [4]
+  float* qs = sm;
+  float* zs = sm + d_qk;
+  float* red = zs + k;
+  const int r = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const RowLoc L = locate_row(cu_q, cu_k, B, r);
+  const float* qr = q + ((int64_t)r * H + h) * d_qk;
+  for (int d = tid; d < d_qk; d += AF_THREADS) qs[d] = qr[d];
+  __syncthreads();
+  const int32_t* ir = idx + (int64_t)r * k;
+  float mloc = -INFINITY;
+  for (int j = tid; j < k; j += AF_THREADS) {
+    const int s = ir[j];
+    float z = -INFINITY;
+    if (s >= 0 && s < L.n) {
+      const float* c = kv + (int64_t)(L.kofs + s) * d_qk;
+      float acc = 0.f;
+      for (int d = 0; d < d_qk; ++d) acc = fmaf(qs[d], c[d], acc);
+      z = acc * scale;
+    }
+    zs[j] = z;
+    mloc = fmaxf(mloc, z);
+  }
+  const float m = block_reduce(mloc, true, red);
+  float* o = out + ((int64_t)r * H + h) * d_v;
+  if (m == -INFINITY) {  // no valid index
+    for (int d = tid; d < d_v; d += AF_THREADS) o[d] = 0.f;
+    if (lse && tid == 0) lse[(int64_t)r * H + h] = -INFINITY;
+    return;
+  }
+  float lloc = 0.f;
+  for (int j = tid; j < k; j += AF_THREADS) {
+    const float p = zs[j] == -INFINITY ? 0.f : expf(zs[j] - m);
+    zs[j] = p;
+    lloc += p;
+  }
+  const float l = block_reduce(lloc, false, red);  // its barriers also publish zs
+  const float inv = 1.f / l;
+  for (int d = tid; d < d_v; d += AF_THREADS) {
+    float acc = 0.f;
+    for (int j = 0; j < k; ++j) {
+      const float p = zs[j];
+      if (p != 0.f) acc = fmaf(p, kv[(int64_t)(L.kofs + ir[j]) * d_qk + d], acc);
+    }
+    o[d] = acc * inv;
+  }
+  if (lse && tid == 0) lse[(int64_t)r * H + h] = m + logf(l);
+}
+
+hipError_t launch_attn_f32(const SeqInfo& s, int H, int d_qk, int d_v, const float* q,
+                           const float* kv, const int32_t* idx, int k, float scale, float* out,
+                           float* lse, hipStream_t st) {
+  if (s.T == 0) return hipSuccess;
+  size_t lds = (size_t)(d_qk + k + 8) * sizeof(float);
+  hipLaunchKernelGGL(attn_f32_kernel, dim3(s.T, H), dim3(AF_THREADS), lds, st, s.B, s.cu_q,
+                     s.cu_k, H, d_qk, d_v, q, kv, idx, k, scale, out, lse);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------- BF16 matrix path
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int MH = 128;            // query heads
+constexpr int MDQK = 576;          // latent (key) dims
+constexpr int MDV = 512;           // value dims (leading part of the latent row)
+constexpr int MBLK = 64;           // keys per gathered block
+constexpr int MCH = MDQK / 8;      // 16-byte chunks per latent row (72)
+constexpr int MBUF = MBLK * MDQK * 2;   // bytes per LDS block buffer (73728)
+constexpr int MT = MDQK / 16;      // K steps of the logits product (36)
+
+__device__ __forceinline__ v16f mfma_bf16_32x32x16(const bf16x8& a, const bf16x8& b, const v16f& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// byte offset of (key s, 16-byte chunk c) inside a block buffer
+__device__ __forceinline__ int slot_off(int s, int c) { return ((c << 6) + (s ^ (c & 7))) << 4; }
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Issue the gather of one block into `buf`. Wave w copies chunks c = 4i + w (i = 0..17); lane l
+// copies key l ^ (c & 7) = l ^ (4(i & 1) + w), so that the DMA's lane-linear LDS writes land in
+// the swizzled slots. row_a / row_b are the latent rows of keys l ^ w and l ^ (w + 4).
+__device__ __forceinline__ void gather_block(uint8_t* buf, const uint8_t* __restrict__ kv,
+                                             int64_t row_a, int64_t row_b, int wave) {
+  const uint8_t* pa = kv + row_a * (MDQK * 2) + wave * 16;
+  const uint8_t* pb = kv + row_b * (MDQK * 2) + wave * 16;
+#pragma unroll
+  for (int i = 0; i < MCH / 4; ++i) {
+    const int c = 4 * i + wave;
+    const uint8_t* src = ((i & 1) ? pb : pa) + i * 64;
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
+                                     (__attribute__((address_space(3))) void*)(buf + c * 1024),
+                                     16, 0, 0);
+  }
+}
+
+struct SoftmaxState {
+  float m;     // reference max (log2 domain) used in the exponent; fixed during a pass
+  float seen;  // largest block max seen so far in this row (log2 domain)
+  float l;     // running sum of 2^(z - m) over this lane's keys
+};
+
+// Exponents above the reference max are allowed up to this many powers of two before the row
+// is restarted with a larger reference (2^64 keeps P, the sums and the output finite in fp32).
+constexpr float kHeadroom = 64.f;
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Transposing LDS read (ds_read_b64_tr_b16). Within each group of 16 lanes, lane i receives, as
+// its element j, element (i % 4) of the 8-byte row addressed by lane 4j + i/4 of the group.
+__device__ __forceinline__ s16x4 lds_read_tr16(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+}
+
+// One half block (32 keys starting at kbase inside the LDS block): logits, softmax weights,
+// value accumulation. Returns true (uniform over the wave) when some head's logits exceed its
+// reference max by more than kHeadroom; the caller then restarts the row. LDS operands are
+// prefetched one MFMA ahead; scheduling barriers keep the compiler from hoisting further
+// (which would cost registers the resident query block needs).
+__device__ __forceinline__ bool attend_half(const uint8_t* buf, int kbase, uint32_t vmask,
+                                            const bf16x8 (&qreg)[MT], v16f (&acc_o)[MDV / 32],
+                                            SoftmaxState& st, float sl2, int lane) {
+  const int g = lane >> 5, c32 = lane & 31;
+  // S^T = K Q^T: M = 32 keys, N = 32 heads; lane holds head c32, keys 8(i/4) + 4g + (i%4).
+  // chunk c = 2t + g of key kbase + c32 sits in slot c*64 + kbase + ((c32 ^ g) ^ (2t & 6))
+  const uint8_t* kb_lane = buf + ((g << 6) + kbase) * 16;
+  const int kx = c32 ^ g;
+  auto kop = [&](int t) -> bf16x8 {
+    return *reinterpret_cast<const bf16x8*>(kb_lane + (kx ^ (2 * t & 6)) * 16 + t * 2048);
+  };
+  v16f s = {};
+  {
+    bf16x8 ka[2];
+    ka[0] = kop(0);
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      if (t + 1 < MT) ka[(t + 1) & 1] = kop(t + 1);
+      s = mfma_bf16_32x32x16(ka[t & 1], qreg[t], s);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  float bmax = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int key = 8 * (i >> 2) + 4 * g + (i & 3);
+    const float z = ((vmask >> key) & 1u) ? s[i] * sl2 : -INFINITY;
+    s[i] = z;
+    bmax = fmaxf(bmax, z);
+  }
+  bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
+  if (st.m == -INFINITY) st.m = bmax;  // first non-empty block of the pass
+  st.seen = fmaxf(st.seen, bmax);
+  if (__any(bmax > st.m + kHeadroom)) return true;
+  bf16x8 pb[2];
+  float lsum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float p = __builtin_amdgcn_exp2f(s[i] - st.m);
+    lsum += p;
+    pb[i >> 3][i & 7] = (__bf16)p;
+  }
+  st.l += lsum;
+  // O^T[v, head] += V^T[v, keys] P^T[keys, head]. K step j covers keys 16j + 8h + 4g + jj
+  // (h = 0, 1; jj = 0..3): the lane's P values i = 8j + 4h + jj. The V^T operand comes from two
+  // transposing reads: lane (4jj + q) of each 16-lane group points at value dims
+  // v0 = 32vt + 16*(group & 1) + 4q .. +3 of key 16j + 8h + 4g + jj.
+  // chunk c = 4vt + 2grp + q/2 has swizzle c & 7 = 4(vt & 1) + 2grp + q/2, and the key's low 3
+  // bits are 4g + jj, so slot = c*64 + kbase + 16j + 8h + ((4g + jj) ^ (2grp + q/2) ^ 4(vt & 1)).
+  const int grp = (lane >> 4) & 1, li = lane & 15;
+  const int jj = li >> 2, q4 = li & 3;
+  const uint8_t* vb_lane = buf + ((2 * grp + (q4 >> 1)) * 64 + kbase) * 16 + (q4 & 1) * 8;
+  const int klo = (4 * g + jj) ^ (2 * grp + (q4 >> 1));
+  auto vop = [&](int step) -> bf16x8 {
+    const int j = step / (MDV / 32), vt = step % (MDV / 32);
+    const uint8_t* p = vb_lane + (klo ^ (4 * (vt & 1))) * 16 + vt * 4096 + j * 256;
+    const s16x4 lo = lds_read_tr16(p);
+    const s16x4 hi = lds_read_tr16(p + 128);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  constexpr int NSTEP = 2 * (MDV / 32);
+  bf16x8 va[2];
+  va[0] = vop(0);
+#pragma unroll
+  for (int step = 0; step < NSTEP; ++step) {
+    if (step + 1 < NSTEP) va[(step + 1) & 1] = vop(step + 1);
+    const int j = step / (MDV / 32), vt = step % (MDV / 32);
+    acc_o[vt] = mfma_bf16_32x32x16(va[step & 1], pb[j], acc_o[vt]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  return false;
+}
+
+// One gathered block of 64 keys, processed as two halves. Returns true if the row must restart.
+__device__ __forceinline__ bool attend_block(const uint8_t* buf, uint64_t vmask,
+                                             const bf16x8 (&qreg)[MT], v16f (&acc_o)[MDV / 32],
+                                             SoftmaxState& st, float sl2, int lane) {
+#pragma unroll 1
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t m32 = (uint32_t)(vmask >> (32 * h));
+    if (m32 && attend_half(buf, 32 * h, m32, qreg, acc_o, st, sl2, lane)) return true;
+  }
+  return false;
+}
+
+__global__ void __launch_bounds__(256, 1)
+attn_bf16_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
+                 const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv,
+                 const int32_t* __restrict__ idx, int k, float scale, uint16_t* __restrict__ out,
+                 float* __restrict__ lse) {
+  __shared__ __attribute__((aligned(1024))) uint8_t buf0[MBUF];
+  __shared__ __attribute__((aligned(1024))) uint8_t buf1[MBUF];
+  // restart requests: slot (step & 1) holds the id of the last step that asked for one
+  __shared__ int s_flag[2];
+  const int r = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 5, c32 = lane & 31;
+  const RowLoc L = locate_row(cu_q, cu_k, B, r);
+  const int32_t* ir = idx + (int64_t)r * k;
+  const int nblk = (k + MBLK - 1) / MBLK;
+
+  // query block of this wave as B operand: head 32w + c32, dims 16t + 8g .. +8
+  bf16x8 qreg[MT];
+  {
+    const uint16_t* qh = q + ((int64_t)r * MH + 32 * wave + c32) * MDQK + 8 * g;
+#pragma unroll
+    for (int t = 0; t < MT; ++t) qreg[t] = *reinterpret_cast<const bf16x8*>(qh + 16 * t);
+  }
+  v16f acc_o[MDV / 32];
+  SoftmaxState st{-INFINITY, -INFINITY, 0.f};
+  const float sl2 = scale * 1.4426950408889634f;
+  if (threadIdx.x == 0) s_flag[0] = s_flag[1] = -1;
+
+  // lane l's key of block blk is entry blk*64 + l of the index row
+  auto load_idx = [&](int blk) -> int {
+    const int j = blk * MBLK + lane;
+    return (blk < nblk && j < k) ? ir[j] : -1;
+  };
+  // latent rows of keys l ^ w and l ^ (w + 4) (see gather_block) and the block's valid mask
+  auto prep = [&](int sidx, int64_t& ra, int64_t& rb, uint64_t& vm) {
+    const bool valid = sidx >= 0 && sidx < L.n;
+    vm = __ballot(valid);
+    const int row = L.kofs + (valid ? sidx : 0);
+    ra = __shfl_xor(row, wave);
+    rb = __shfl_xor(row, wave + 4);
+  };
+
+  // Pipeline: wait for the block in flight, barrier (its LDS data is complete and every wave
+  // has finished with the other buffer), start gathering the next block into the other buffer,
+  // then compute on the current one while that gather is in flight.
+  // A wave that needs a restart records it in s_flag[step & 1] = step (before the next barrier);
+  // every wave reads the previous step's slot right after that barrier, so all waves agree.
+  int step = 0;
+  for (int pass = 0;; ++pass) {
+#pragma unroll
+    for (int vt = 0; vt < MDV / 32; ++vt) acc_o[vt] = (v16f){};
+    st.m = st.seen;  // -inf on the first pass, the largest block max seen on a restart
+    st.l = 0.f;
+    int64_t ra, rb;
+    uint64_t vm_cur, vm_next;
+    prep(load_idx(0), ra, rb, vm_cur);
+    if (vm_cur) gather_block(buf0, kv, ra, rb, wave);
+    int idx_next = load_idx(1);
+    bool restart = false;
+    for (int blk = 0; blk < nblk; blk += 2) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (blk > 0 && s_flag[(step - 1) & 1] == step - 1) { restart = true; break; }
+      prep(idx_next, ra, rb, vm_next);
+      if (blk + 1 < nblk && vm_next) gather_block(buf1, kv, ra, rb, wave);
+      idx_next = load_idx(blk + 2);
+      if (vm_cur && attend_block(buf0, vm_cur, qreg, acc_o, st, sl2, lane)) s_flag[step & 1] = step;
+      ++step;
+      vm_cur = vm_next;
+      if (blk + 1 >= nblk) break;
+
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (s_flag[(step - 1) & 1] == step - 1) { restart = true; break; }
+      prep(idx_next, ra, rb, vm_next);
+      if (blk + 2 < nblk && vm_next) gather_block(buf0, kv, ra, rb, wave);
+      idx_next = load_idx(blk + 3);
+      if (vm_cur && attend_block(buf1, vm_cur, qreg, acc_o, st, sl2, lane)) s_flag[step & 1] = step;
+      ++step;
+      vm_cur = vm_next;
+    }
+    // a request made during the last step is visible after one more barrier
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (!restart && s_flag[(step - 1) & 1] == step - 1) restart = true;
+    if (!restart) break;
+  }
+
+  // finish: combine the two lane halves' sums (same head), normalise, store
+  const float ltot = st.l + __shfl_xor(st.l, 32);
+  const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+  const int head = 32 * wave + c32;
+  uint16_t* orow = out + ((int64_t)r * MH + head) * MDV;
+#pragma unroll
+  for (int vt = 0; vt < MDV / 32; ++vt) {
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int v0 = 32 * vt + 8 * i4 + 4 * g;
+      uint2 pk;
+      pk.x = (uint32_t)f32_to_bf16_rne(acc_o[vt][4 * i4 + 0] * inv) |
+             ((uint32_t)f32_to_bf16_rne(acc_o[vt][4 * i4 + 1] * inv) << 16);
+      pk.y = (uint32_t)f32_to_bf16_rne(acc_o[vt][4 * i4 + 2] * inv) |
+             ((uint32_t)f32_to_bf16_rne(acc_o[vt][4 * i4 + 3] * inv) << 16);
+      *reinterpret_cast<uint2*>(orow + v0) = pk;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (lse && g == 0)
+    lse[(int64_t)r * MH + head] = ltot > 0.f ? (st.m + __log2f(ltot)) * 0.6931471805599453f : -INFINITY;
+}
+
+size_t attn_workspace_bytes(const SeqInfo&, int, int, int, int, bool) { return 0; }
+
+hipError_t launch_attn_bf16(const SeqInfo& s, const uint16_t* q, const uint16_t* kv,
+                            const int32_t* idx, int k, float scale, uint16_t* out, float* lse,
+                            void*, size_t, hipStream_t st) {
+  if (s.T == 0) return hipSuccess;
+  hipLaunchKernelGGL(attn_bf16_kernel, dim3(s.T), dim3(256), 0, st, s.B, s.cu_q, s.cu_k, q,
+                     reinterpret_cast<const uint8_t*>(kv), idx, k, scale, out, lse);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

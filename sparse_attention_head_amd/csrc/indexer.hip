@@ -1,0 +1,220 @@
+// Lightning-indexer scores on gfx950.
+//
+//   I[r, s] = sum_j w[r, j] * ReLU(qI[r, j] . kI[s])      for s = 0..pos(r)
+//
+// (DeepSeek-V3.2 paper digest, "Key claims": paper section 2.1, Eq. 1 -- few indexer heads,
+//  ReLU, FP8. 36kr article, section "02. Built on the final version of DeepSeek-V3.1": index
+//  scores between a query token and the tokens before it.)
+//
+// FP8 path (H_I = 64, d_I = 128). The score is a dense contraction: for a block of query rows the
+// products qI[r, j] . kI[s] form a GEMM of shape [rows * 64 heads, 128] x [128, keys]. d_I = 128
+// is exactly one K step of v_mfma_f32_16x16x128_f8f6f4, so every 16x16 output tile costs a single
+// matrix instruction; the ReLU and the weighted head sum run on the vector ALU straight out of the
+// accumulator registers (2 VALU ops per (row, head, key)), so nothing but the final score leaves
+// the registers.
+//
+// MFMA operand mapping. A 16x16x128 output tile has M = 16 (row, head) pairs and N = 16 keys.
+// Lane l holds output column l%16 and rows 4*(l/16)+v, v = 0..3. The M index is laid out as
+// (row-in-wave, head) so that a lane's 4 values belong to one query row: with RW rows per wave and
+// HPM = 16/RW heads per row in a tile, M index i = row * HPM + head_local. For RW = 4 every lane
+// owns one row and the head sum never leaves the lane; for RW = 2 / 1 the partial sums of 2 / 4
+// lane groups are added with cross-lane swaps at the end of each key block.
+// The K (d_I) index is split across lane groups identically for A (queries) and B (keys), so the
+// contraction does not depend on the hardware's byte order within a lane.
+#include "dsa_internal.h"
+#include "device_common.h"
+
+namespace dsa {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------- fp32 vector path
+
+__global__ void __launch_bounds__(256)
+indexer_f32_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
+                   int H_I, int d_I, const float* __restrict__ q, const float* __restrict__ k,
+                   const float* __restrict__ w, float* __restrict__ scores, int64_t ld) {
+  extern __shared__ float sm[];  // q row [H_I * d_I], then w row [H_I]
+  const int r = blockIdx.x;
+  const RowLoc L = locate_row(cu_q, cu_k, B, r);
+  const int s0 = blockIdx.y * 256;
+  if (s0 > L.pos) return;  // uniform over the block
+  float* qs = sm;
+  float* ws = sm + H_I * d_I;
+  for (int i = threadIdx.x; i < H_I * d_I; i += 256) qs[i] = q[(int64_t)r * H_I * d_I + i];
+  for (int i = threadIdx.x; i < H_I; i += 256) ws[i] = w[(int64_t)r * H_I + i];
+  __syncthreads();
+  const int s = s0 + threadIdx.x;
+  if (s > L.pos) return;
+  const float* kr = k + (int64_t)(L.kofs + s) * d_I;
+  float acc = 0.f;
+  for (int j = 0; j < H_I; ++j) {
+    float dot = 0.f;
+    for (int d = 0; d < d_I; ++d) dot = fmaf(qs[j * d_I + d], kr[d], dot);
+    acc = fmaf(ws[j], fmaxf(dot, 0.f), acc);
+  }
+  scores[(int64_t)r * ld + s] = acc;
+}
+
+hipError_t launch_indexer_f32(const SeqInfo& s, int H_I, int d_I, const float* q, const float* k,
+                              const float* w, float* scores, int64_t ld, hipStream_t st) {
+  if (s.T == 0 || s.max_n == 0) return hipSuccess;
+  dim3 grid(s.T, (s.max_n + 255) / 256);
+  size_t lds = (size_t)(H_I * d_I + H_I) * sizeof(float);
+  hipLaunchKernelGGL(indexer_f32_kernel, grid, dim3(256), lds, st, s.B, s.cu_q, s.cu_k, H_I, d_I,
+                     q, k, w, scores, ld);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------- FP8 matrix path
+
+constexpr int kHI = 64;     // indexer heads
+constexpr int kDI = 128;    // indexer head dim (bytes per FP8 vector)
+
+__device__ __forceinline__ v4f mfma_fp8_16x16x128(const v8i& a, const v8i& b) {
+  const v4f zero = {0.f, 0.f, 0.f, 0.f};
+  // format codes 0/0 = FP8 E4M3 for both operands; no block scaling
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 0, 0, 0);
+}
+
+// Computes the scores of RW query rows (one wave) against 16 keys held in `bop`.
+// Returns, per lane, the partial head sum for (row g*RW/4, key l%16) over the heads this lane
+// owns; the caller completes it across lane groups when RW < 4.
+template <int RW>
+__device__ __forceinline__ float score_block(const v8i (&a)[4 * RW], const v8i& bop,
+                                             const float (&wv)[16 * RW]) {
+  constexpr int NMF = 4 * RW;  // MFMAs per key block: RW rows * 64 heads / 16
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int mm = 0; mm < NMF; ++mm) {
+    v4f d = mfma_fp8_16x16x128(a[mm], bop);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) acc[v] = fmaf(wv[4 * mm + v], fmaxf(d[v], 0.f), acc[v]);
+  }
+  return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+}
+
+// Loads this lane's 32-byte slice (bytes 32*(l/16) .. +32) of a 128-byte FP8 vector.
+__device__ __forceinline__ v8i load_slice(const uint8_t* __restrict__ base, int64_t row, int g) {
+  return *reinterpret_cast<const v8i*>(base + row * kDI + g * 32);
+}
+
+// Prefill: one workgroup = W waves x RW rows of one sequence against a chunk of KC keys; all waves
+// walk the same keys. Decode (m_b == 1 everywhere): one workgroup = one row and a chunk of keys that
+// the W waves split in interleaved 16-key blocks.
+template <int RW, int W, bool DECODE, int PF>
+__global__ void __launch_bounds__(W * 64)
+indexer_fp8_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
+                   const uint8_t* __restrict__ q, const uint8_t* __restrict__ k,
+                   const float* __restrict__ w, float* __restrict__ scores, int64_t ld, int KC) {
+  constexpr int HPM = 16 / RW;      // heads of one row inside a 16x16 tile
+  constexpr int NMF = 4 * RW;       // tiles (MFMAs) per 16-key block
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = lane >> 4, c = lane & 15;
+
+  int b, chunk, i_base;
+  if (DECODE) {
+    b = blockIdx.y;
+    chunk = blockIdx.x;
+    i_base = 0;
+  } else {
+    b = blockIdx.z;
+    chunk = blockIdx.y;
+    i_base = blockIdx.x * (W * RW);
+  }
+  const int q0 = cu_q[b], m = cu_q[b + 1] - q0;
+  const int k0 = cu_k[b], n = cu_k[b + 1] - k0;
+  if (i_base >= m) return;
+  const int tile_last = min(m, i_base + W * RW) - 1;
+  const int kbeg = chunk * KC;
+  if (kbeg > n - m + tile_last) return;  // chunk entirely beyond the causal limit of the tile
+
+  // rows of this wave (prefill) or the single row (decode)
+  const int wrow0 = DECODE ? i_base : i_base + wave * RW;
+  if (wrow0 >= m) return;                // no barrier below: waves may leave independently
+  const int wrow_last = min(m, wrow0 + RW) - 1;
+  const int kend = min(kbeg + KC, n - m + wrow_last + 1);
+  if (kbeg >= kend) return;
+
+  // A operand: M index c -> (row c / HPM, head mm*HPM + c % HPM), K bytes of lane group g
+  v8i a[NMF];
+  {
+    const int ar = min(wrow0 + c / HPM, m - 1);
+    const uint8_t* qrow = q + (int64_t)(q0 + ar) * (kHI * kDI) + (c % HPM) * kDI + g * 32;
+#pragma unroll
+    for (int mm = 0; mm < NMF; ++mm) a[mm] = *reinterpret_cast<const v8i*>(qrow + mm * HPM * kDI);
+  }
+  // head weights for this lane's outputs: D row 4g+v -> (row (4g+v)/HPM, head mm*HPM + (4g+v)%HPM)
+  const int my_i = wrow0 + (4 * g) / HPM;      // all 4 v of a lane share the row
+  float wv[16 * RW];
+  {
+    const float* wr = w + (int64_t)(q0 + min(my_i, m - 1)) * kHI;
+#pragma unroll
+    for (int mm = 0; mm < NMF; ++mm)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) wv[4 * mm + v] = wr[mm * HPM + (4 * g + v) % HPM];
+  }
+  const bool row_ok = my_i < m;
+  const int my_pos = n - m + my_i;
+  float* srow = scores + (int64_t)(q0 + min(my_i, m - 1)) * ld;
+
+  // key blocks: prefill walks every block of [kbeg, kend); decode wave w takes blocks w, w+W, ...
+  const int step = DECODE ? 16 * W : 16;
+  const int first = DECODE ? kbeg + 16 * wave : kbeg;
+  v8i ring[PF];
+#pragma unroll
+  for (int p = 0; p < PF; ++p)
+    ring[p] = load_slice(k, k0 + min(first + p * step + c, n - 1), g);
+
+  for (int kb0 = first; kb0 < kend; kb0 += PF * step) {
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+      const int kb = kb0 + p * step;
+      const v8i cur = ring[p];
+      ring[p] = load_slice(k, k0 + min(kb + PF * step + c, n - 1), g);
+      if (kb < kend) {
+        float acc = score_block<RW>(a, cur, wv);
+        if (RW <= 2) acc += __shfl_xor(acc, 16);
+        if (RW == 1) acc += __shfl_xor(acc, 32);
+        const int s = kb + c;
+        const bool owner = (RW == 4) || (RW == 2 ? (g & 1) == 0 : g == 0);
+        if (owner && row_ok && s <= my_pos && s < kend) srow[s] = acc;
+      }
+    }
+  }
+}
+
+// Key-chunk length: long enough to amortise loading the query tile, short enough to give
+// several workgroups per compute unit.
+static int pick_chunk(int64_t tiles, int max_n, int cus, int align) {
+  int kc = 8192;
+  while (kc > 512 && tiles * ((max_n + kc - 1) / kc) < 4LL * cus) kc >>= 1;
+  return (kc / align) * align;
+}
+
+hipError_t launch_indexer_fp8_prefill(const SeqInfo& s, const uint8_t* q, const uint8_t* k,
+                                      const float* w, float* scores, int64_t ld, hipStream_t st) {
+  if (s.T == 0 || s.max_n == 0) return hipSuccess;
+  constexpr int RW = 4, W = 4, ROWS = RW * W;
+  const int tiles = (s.max_m + ROWS - 1) / ROWS;
+  const int kc = pick_chunk((int64_t)tiles * s.B, s.max_n, device_cu_count(), 64);
+  dim3 grid(tiles, (s.max_n + kc - 1) / kc, s.B);
+  hipLaunchKernelGGL((indexer_fp8_kernel<RW, W, false, 2>), grid, dim3(W * 64), 0, st, s.B,
+                     s.cu_q, s.cu_k, q, k, w, scores, ld, kc);
+  return hipGetLastError();
+}
+
+hipError_t launch_indexer_fp8_decode(const SeqInfo& s, const uint8_t* q, const uint8_t* k,
+                                     const float* w, float* scores, int64_t ld, hipStream_t st) {
+  if (s.T == 0 || s.max_n == 0) return hipSuccess;
+  constexpr int W = 4;
+  const int kc = 2048;
+  dim3 grid((s.max_n + kc - 1) / kc, s.B);
+  hipLaunchKernelGGL((indexer_fp8_kernel<1, W, true, 4>), grid, dim3(W * 64), 0, st, s.B, s.cu_q,
+                     s.cu_k, q, k, w, scores, ld, kc);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

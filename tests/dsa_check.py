@@ -1,0 +1,60 @@
+"""Comparison helpers for the parity tests (test infrastructure; uses the oracle only).
+
+Floating-point contracts checked here:
+  * indexer scores: |I_gpu - I*| <= eps[r, s] with
+        eps = 2 * (delta + gamma(H_I + 1)) * sum_j |w_j| sum_d |qI_jd kI_sd|,
+    delta = accumulation error of one d_I-term dot product relative to sum_d |q k|:
+    gamma(d_I) for sequential fp32, DELTA_FP8_MFMA for the FP8 matrix instruction, whose internal
+    sum of its 128 products is coarser than fp32 (see DELTA_FP8_MFMA).
+    On integer-valued inputs every partial sum is exact, so scores must match bit for bit.
+  * top-k: bit-exact on integer inputs; on N(0,1) inputs "eps-valid": ascending, unique,
+    in range, min(k, n) entries, and no candidate outside the set beats one inside it by more
+    than the two error bounds.
+  * attention: against the oracle evaluated on the GPU's own (validated) index set.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+from oracle.dsa import Seqs
+
+U = 2.0 ** -24
+
+
+def gamma(n):
+    return n * U / (1 - n * U)
+
+
+# The gfx950 FP8 MFMA (v_mfma_f32_16x16x128_f8f6f4) adds its 128 products with less than fp32
+# precision. Measured on full-range random e4m3 codes: max |err| / sum|ab| = 8.5e-5 (~2^-13.5).
+# The bound used in the tests is 2^-11, a factor ~6 above the worst measured ratio.
+DELTA_FP8_MFMA = 2.0 ** -11
+
+
+def score_bound_row(sq: Seqs, qI, kI, w, r, delta):
+    _, pos, k0, _ = sq.locate(r)
+    q = np.abs(oracle.decode(qI[r]))
+    keys = np.abs(oracle.decode(kI[k0:k0 + pos + 1]))
+    H_I = q.shape[0]
+    S = np.abs(oracle.decode(w[r])) @ (q @ keys.T)
+    return 2.0 * (delta + gamma(H_I + 1)) * S
+
+
+def check_topk_row(got, exact_scores, eps, k, pos):
+    """eps-valid check of one GPU top-k row. Returns overlap fraction with the oracle set."""
+    n = pos + 1
+    want = min(k, n)
+    got = np.asarray(got)
+    sel = got[:want]
+    assert np.all(got[want:] == -1), "padding must be -1"
+    assert np.all((sel >= 0) & (sel <= pos)), "index out of causal range"
+    assert np.all(np.diff(sel) > 0), "indices must be strictly ascending"
+    if want < n:
+        inside = np.zeros(n, bool)
+        inside[sel] = True
+        lo_in = np.min(exact_scores[inside] + eps[inside])
+        hi_out = np.max(exact_scores[~inside] - eps[~inside])
+        assert lo_in >= hi_out, f"a candidate outside the set beats one inside ({hi_out} > {lo_in})"
+    ref = oracle.topk_row(exact_scores, k)[:want]
+    return len(np.intersect1d(ref, sel)) / max(1, want)

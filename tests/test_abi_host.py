@@ -1,0 +1,163 @@
+"""Host-only checks of the C ABI (no GPU needed): the library loads, exports every symbol that
+include/dsa.h declares, and rejects invalid arguments with the documented status codes before
+any HIP call."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+LIB = os.path.join(ROOT, "sparse_attention_head_amd", "libdsa.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libdsa.so not built")
+
+
+@pytest.fixture(scope="module")
+def dsa():
+    import sparse_attention_head_amd as m
+    return m
+
+
+def declared_functions():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsa_[a-z_0-9]+)\s*\(", txt)))
+
+
+def test_exports_every_declared_symbol(dsa):
+    lib = ctypes.CDLL(LIB)
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in dsa.h but not exported"
+    assert set(names) == set(dsa.EXPORTS)
+
+
+def test_abi_version_and_status_strings(dsa):
+    assert dsa.abi_version() == 1
+    for st in range(8):
+        s = dsa._c_status(st)
+        assert s and len(s) >= 2
+    assert dsa._c_status(99) == b"unknown status"
+
+
+# ------------------------------------------------------------------ validation without a GPU
+
+class FakeSeqs:
+    """Host-side stand-in: device pointers are never dereferenced during validation."""
+
+    def __init__(self, dsa, cu_q, cu_k, max_m=None, max_n=None):
+        self.cu_q = np.asarray(cu_q, np.int32)
+        self.cu_k = np.asarray(cu_k, np.int32)
+        self.s = dsa._Seqs()
+        self.s.num_seqs = len(cu_q) - 1
+        self.s.cu_seqlens_q = self.cu_q.ctypes.data
+        self.s.cu_seqlens_k = self.cu_k.ctypes.data
+        self.s.cu_seqlens_q_host = self.cu_q.ctypes.data
+        self.s.cu_seqlens_k_host = self.cu_k.ctypes.data
+        m = np.diff(self.cu_q)
+        n = np.diff(self.cu_k)
+        self.s.max_seqlen_q = int(m.max()) if max_m is None else max_m
+        self.s.max_seqlen_k = int(n.max()) if max_n is None else max_n
+
+    @property
+    def ref(self):
+        return ctypes.byref(self.s)
+
+
+def buf(nbytes, misalign=0):
+    a = np.zeros(nbytes + 64, np.uint8)
+    p = a.ctypes.data
+    p += (-p) % 16 + misalign
+    return a, p
+
+
+def indexer(dsa, sq, H_I=64, d_I=128, dt=2, ptrs=None, ld=None):
+    keep, p = buf(64)
+    q, k, w, s = ptrs if ptrs else (p, p, p, p)
+    ld = ld if ld is not None else (sq.s.max_seqlen_k + 3) // 4 * 4
+    st = dsa._c_indexer(sq.ref, H_I, d_I, dt, q, k, w, s, ld, None)
+    return st
+
+
+def test_indexer_validation(dsa):
+    sq = FakeSeqs(dsa, [0, 10], [0, 10])
+    assert dsa._c_indexer(None, 64, 128, 2, 16, 16, 16, 16, 12, None) == dsa.DSA_ERR_NULL
+    assert indexer(dsa, sq, ld=8) == dsa.DSA_ERR_SHAPE                 # ld < max_seqlen_k
+    assert indexer(dsa, sq, ld=14) == dsa.DSA_ERR_SHAPE                # ld not a multiple of 4
+    assert indexer(dsa, sq, H_I=32) == dsa.DSA_ERR_UNSUPPORTED         # FP8 needs 64 x 128
+    assert indexer(dsa, sq, dt=1) == dsa.DSA_ERR_DTYPE                 # bf16 indexer inputs
+    assert indexer(dsa, sq, H_I=0) == dsa.DSA_ERR_SHAPE
+    assert indexer(dsa, sq, dt=0, H_I=200) == dsa.DSA_ERR_UNSUPPORTED  # fp32 path limits
+    keep, p = buf(64)
+    _, pm = buf(64, misalign=4)
+    assert indexer(dsa, sq, ptrs=(p, None, p, p)) == dsa.DSA_ERR_NULL
+    assert indexer(dsa, sq, ptrs=(p, p, pm, p)) == dsa.DSA_ERR_ALIGN
+
+
+def test_seqs_validation(dsa):
+    assert indexer(dsa, FakeSeqs(dsa, [0, 10], [0, 5])) == dsa.DSA_ERR_SHAPE             # m > n
+    assert indexer(dsa, FakeSeqs(dsa, [0, 3, 2], [0, 5, 9])) == dsa.DSA_ERR_SHAPE        # decreasing
+    assert indexer(dsa, FakeSeqs(dsa, [1, 3], [0, 5])) == dsa.DSA_ERR_SHAPE              # not from 0
+    assert indexer(dsa, FakeSeqs(dsa, [0, 3], [0, 5], max_n=6)) == dsa.DSA_ERR_SHAPE     # wrong max
+    neg = FakeSeqs(dsa, [0, 1], [0, 1])
+    neg.s.num_seqs = -1
+    assert indexer(dsa, neg) == dsa.DSA_ERR_SHAPE
+    nulls = FakeSeqs(dsa, [0, 1], [0, 1])
+    nulls.s.cu_seqlens_q_host = None
+    assert indexer(dsa, nulls) == dsa.DSA_ERR_NULL
+    empty = FakeSeqs(dsa, [0], [0], max_m=0, max_n=0)
+    assert indexer(dsa, empty) == dsa.DSA_OK                            # B = 0: no-op
+
+
+def test_topk_and_attention_validation(dsa):
+    sq = FakeSeqs(dsa, [0, 10], [0, 10])
+    keep, p = buf(64)
+    assert dsa._c_topk(sq.ref, p, 12, 0, p, None, 0, None) == dsa.DSA_ERR_UNSUPPORTED
+    assert dsa._c_topk(sq.ref, p, 12, 20000, p, None, 0, None) == dsa.DSA_ERR_UNSUPPORTED
+    assert dsa._c_topk(sq.ref, p, 8, 4, p, None, 0, None) == dsa.DSA_ERR_SHAPE
+    assert dsa._c_topk(sq.ref, None, 12, 4, p, None, 0, None) == dsa.DSA_ERR_NULL
+    # attention
+    A = dsa._c_attn
+    assert A(sq.ref, 128, 576, 512, 2, p, p, p, 64, 1.0, p, p, None, 0, None) == dsa.DSA_ERR_DTYPE
+    assert A(sq.ref, 128, 576, 600, 1, p, p, p, 64, 1.0, p, p, None, 0, None) == dsa.DSA_ERR_SHAPE
+    assert A(sq.ref, 64, 576, 512, 1, p, p, p, 64, 1.0, p, p, None, 0, None) == dsa.DSA_ERR_UNSUPPORTED
+    assert A(sq.ref, 8, 80, 64, 0, p, p, p, 8000, 1.0, p, p, None, 0, None) == dsa.DSA_ERR_UNSUPPORTED
+    assert A(sq.ref, 8, 80, 64, 0, p, None, p, 64, 1.0, p, p, None, 0, None) == dsa.DSA_ERR_NULL
+    _, pm = buf(64, misalign=8)
+    assert A(sq.ref, 8, 80, 64, 0, p, p, p, 64, 1.0, pm, p, None, 0, None) == dsa.DSA_ERR_ALIGN
+
+
+def test_forward_validation_and_workspace(dsa):
+    sq = FakeSeqs(dsa, [0, 100], [0, 100])
+    keep, p = buf(64)
+    a = dsa._FwdArgs()
+    a.H_I, a.d_I, a.qk_dtype = 64, 128, dsa.DSA_FP8_E4M3
+    a.q_idx = a.k_idx = a.w = p
+    a.k = 16
+    a.H, a.d_qk, a.d_v, a.dtype = 128, 576, 512, dsa.DSA_BF16
+    a.q = a.kv = a.out = a.lse = p
+    a.softmax_scale = 0.04
+    need = dsa._c_fwd_ws(sq.ref, ctypes.byref(a))
+    # scores [100, 100] fp32 + indices [100, 16] int32, each 256-byte aligned
+    assert need >= 100 * 100 * 4 + 100 * 16 * 4
+    assert dsa._c_fwd(sq.ref, ctypes.byref(a), None, 0, None) == dsa.DSA_ERR_WORKSPACE
+    assert dsa._c_fwd(sq.ref, ctypes.byref(a), p, need - 1, None) == dsa.DSA_ERR_WORKSPACE
+    assert dsa._c_fwd(sq.ref, None, p, need, None) == dsa.DSA_ERR_NULL
+    a.k = 0
+    assert dsa._c_fwd(sq.ref, ctypes.byref(a), p, need, None) == dsa.DSA_ERR_UNSUPPORTED
+    a.k = 16
+    # caller-provided intermediates shrink the workspace
+    a.scores_out, a.ld_scores_out, a.indices_out = p, 100, p
+    assert dsa._c_fwd_ws(sq.ref, ctypes.byref(a)) < need
+    a.ld_scores_out = 96
+    assert dsa._c_fwd(sq.ref, ctypes.byref(a), p, need, None) == dsa.DSA_ERR_SHAPE
+
+
+def test_last_error_is_descriptive(dsa):
+    sq = FakeSeqs(dsa, [0, 10], [0, 5])
+    indexer(dsa, sq)
+    assert b"queries" in dsa._c_last()

@@ -1,0 +1,211 @@
+"""GPU parity: every C-ABI entry point against the CPU oracle on the same seeded inputs.
+
+Bars (see tests/dsa_check.py for the derivations):
+  * integer-valued indexer inputs ("int" variant): scores and top-k indices bit-exact;
+  * N(0,1) inputs: scores within the accumulation error bound, top-k eps-valid;
+  * attention (bf16): max-abs <= 2e-2, mean-abs <= 2e-3 against the oracle evaluated on the GPU's
+    own validated index set; lse within 1e-3; fp32 path within 1e-4.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import dsa_datagen as dg
+import oracle
+from oracle.dsa import Seqs
+from tests.dsa_check import DELTA_FP8_MFMA, check_topk_row, gamma, score_bound_row
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev(x, kind=None):
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    if x.dtype == np.uint8:
+        t = t.view(torch.float8_e4m3fn)
+    elif x.dtype == np.uint16:
+        t = t.view(torch.int16).view(torch.bfloat16)
+    return t.cuda()
+
+
+def to_np_bf16(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def run_all(gpu, wl, x):
+    seqs = gpu.Seqs(wl.cu_seqlens_q, wl.cu_seqlens_k)
+    T = {k: dev(v) for k, v in x.items() if k not in ("cu_seqlens_q", "cu_seqlens_k")}
+    scores = gpu.indexer_scores(seqs, T["qI"], T["kI"], T["w"])
+    idx = gpu.topk(seqs, scores, wl.k)
+    out, lse = gpu.sparse_mla_attn(seqs, T["q"], T["kv"], idx, wl.scale, wl.d_v)
+    fwd = gpu.Forward(seqs, T["qI"], T["kI"], T["w"], T["q"], T["kv"], wl.k, wl.scale, wl.d_v,
+                      keep_scores=True, keep_indices=True)
+    fout, flse = fwd()
+    torch.cuda.synchronize()
+    return dict(scores=scores.cpu().numpy(), idx=idx.cpu().numpy(), out=out, lse=lse.cpu().numpy(),
+                fscores=fwd.scores.cpu().numpy(), fidx=fwd.indices.cpu().numpy(), fout=fout,
+                flse=flse.cpu().numpy())
+
+
+def out_np(t):
+    return to_np_bf16(t) if t.dtype == torch.bfloat16 else t.cpu().numpy()
+
+
+def check_rows(wl, x, res, rows, variant, delta):
+    sq = Seqs(wl.cu_seqlens_q, wl.cu_seqlens_k)
+    exact = variant == "int"
+    outs = out_np(res["out"])
+    fouts = out_np(res["fout"])
+    overlaps = []
+    for r in rows:
+        _, pos, _, _ = sq.locate(r)
+        ref = oracle.indexer_scores_row(sq, x["qI"], x["kI"], x["w"], r)
+        got = res["scores"][r, :pos + 1].astype(np.float64)
+        assert np.array_equal(res["fscores"][r, :pos + 1], res["scores"][r, :pos + 1]), "fused scores differ"
+        if exact:
+            assert np.array_equal(got, ref), f"row {r}: scores not bit-exact"
+            assert res["idx"][r].tolist() == oracle.topk_row(ref, wl.k).tolist(), f"row {r}: top-k differs"
+        else:
+            eps = score_bound_row(sq, x["qI"], x["kI"], x["w"], r, delta)
+            bad = np.abs(got - ref) > eps
+            assert not bad.any(), f"row {r}: {bad.sum()} scores outside the bound, worst {np.max(np.abs(got-ref)/eps)}"
+            overlaps.append(check_topk_row(res["idx"][r], ref, eps, wl.k, pos))
+        assert np.array_equal(res["fidx"][r], res["idx"][r]), "fused indices differ"
+        # attention on the GPU's own indices
+        o, l = oracle.attn_row(sq, x["q"], x["kv"], res["idx"][r], wl.scale, wl.d_v, r)
+        go = oracle.decode(outs[r])
+        err = np.abs(go - o)
+        if wl.attn_dtype == "bf16":
+            assert err.max() <= 2e-2 and err.mean() <= 2e-3, f"row {r}: attn max {err.max()} mean {err.mean()}"
+        else:
+            assert err.max() <= 1e-4, f"row {r}: fp32 attn max err {err.max()}"
+        fin = np.isfinite(l)
+        assert np.array_equal(fin, np.isfinite(res["lse"][r]))
+        assert np.all(np.abs(res["lse"][r][fin] - l[fin]) <= 1e-3)
+        assert np.array_equal(fouts[r], outs[r]), "fused output differs"
+        assert np.array_equal(res["flse"][r], res["lse"][r])
+    return overlaps
+
+
+SMALL = {
+    # name: (seqlens_q, seqlens_k, k)
+    "prefill300_k64": ([300], [300], 64),
+    "multiseq_k128": ([5, 37, 0, 130], [40, 37, 3, 700], 128),
+    "decode_ragged_k2048": ([1, 1, 1, 1, 1], [1, 17, 300, 2100, 5000], 2048),
+    "chunk_tail_k256": ([70], [1500], 256),
+}
+
+
+@pytest.mark.parametrize("variant", ["int", "normal"])
+@pytest.mark.parametrize("case", list(SMALL))
+def test_small_fp8_bf16(gpu, case, variant):
+    sqs, sks, k = SMALL[case]
+    wl = dg.custom(name=case, seqlens_q=sqs, seqlens_k=sks, H_I=64, d_I=128, k=k, H=128, d_qk=576,
+                   d_v=512, idx_dtype="fp8", attn_dtype="bf16", wid=20 + list(SMALL).index(case))
+    say(f"case {case} variant {variant} T={wl.T} Nk={wl.Nk}")
+    x = dg.gen_inputs(wl, variant, seed=7)
+    res = run_all(gpu, wl, x)
+    ov = check_rows(wl, x, res, range(wl.T), variant, DELTA_FP8_MFMA)
+    if ov:
+        say(f"  mean overlap with the oracle set {np.mean(ov):.4f}")
+
+
+@pytest.mark.parametrize("variant", ["int", "normal"])
+def test_tiny_fp32_all_rows(gpu, variant):
+    wl = dg.workload("tiny")
+    x = dg.gen_inputs(wl, variant, seed=0)
+    res = run_all(gpu, wl, x)
+    check_rows(wl, x, res, range(wl.T), variant, gamma(wl.d_I))
+
+
+def test_dense_special_case_bf16(gpu):
+    """k >= every candidate count: the selection is every causal key (exact), and the attention
+    is dense causal attention."""
+    wl = dg.custom(name="dense", seqlens_q=[96], seqlens_k=[96], H_I=64, d_I=128, k=128, H=128,
+                   d_qk=576, d_v=512, idx_dtype="fp8", attn_dtype="bf16", wid=30)
+    x = dg.gen_inputs(wl, "normal", seed=1)
+    res = run_all(gpu, wl, x)
+    for r in range(wl.T):
+        assert res["idx"][r].tolist() == list(range(r + 1)) + [-1] * (wl.k - r - 1)
+    check_rows(wl, x, res, range(wl.T), "normal", DELTA_FP8_MFMA)
+
+
+def test_attention_edge_indices(gpu):
+    """-1 and out-of-range indices are skipped, repeats count twice, an empty row gives 0 / -inf."""
+    wl = dg.custom(name="edge", seqlens_q=[4], seqlens_k=[50], H=128, d_qk=576, d_v=512,
+                   idx_dtype="fp8", attn_dtype="bf16", wid=31, k=70)
+    x = dg.gen_inputs(wl, "normal", seed=2, parts=("attn",))
+    rng = np.random.default_rng(3)
+    idx = np.full((4, 70), -1, np.int32)
+    idx[0, :40] = rng.integers(0, 50, 40)          # unsorted, with repeats
+    idx[1, 5:9] = [49, 50, 1000, -7]               # out of range entries
+    idx[2, 69] = 3                                 # single valid at the end
+    seqs = gpu.Seqs(wl.cu_seqlens_q, wl.cu_seqlens_k)
+    out, lse = gpu.sparse_mla_attn(seqs, dev(x["q"]), dev(x["kv"]), dev(idx), wl.scale, 512)
+    torch.cuda.synchronize()
+    sq = Seqs(wl.cu_seqlens_q, wl.cu_seqlens_k)
+    outs, lses = to_np_bf16(out), lse.cpu().numpy()
+    for r in range(4):
+        o, l = oracle.attn_row(sq, x["q"], x["kv"], idx[r], wl.scale, 512, r)
+        err = np.abs(oracle.decode(outs[r]) - o)
+        assert err.max() <= 2e-2 and err.mean() <= 2e-3
+        fin = np.isfinite(l)
+        assert np.array_equal(fin, np.isfinite(lses[r]))
+        assert np.all(np.abs(lses[r][fin] - l[fin]) <= 1e-3)
+    assert np.all(oracle.decode(outs[3]) == 0) and np.all(lses[3] == -np.inf)
+
+
+def test_topk_ties_and_zeros(gpu):
+    """Many equal scores and signed zeros: lower positions win, +0 == -0."""
+    T, n, k = 6, 3000, 100
+    rng = np.random.default_rng(4)
+    sc = rng.integers(-3, 4, size=(T, n)).astype(np.float32)
+    sc[1] = 0.0
+    sc[2] = np.where(rng.random(n) < 0.5, 0.0, -0.0).astype(np.float32)
+    sc[3] = 5.0
+    sc[4, :] = -1.0
+    sc[4, 2900:] = 2.0
+    cu_q, cu_k = [0, T], [0, n]
+    # T query rows at positions n-T .. n-1
+    seqs = gpu.Seqs(cu_q, cu_k)
+    idx = gpu.topk(seqs, torch.from_numpy(sc).cuda(), k).cpu().numpy()
+    for r in range(T):
+        pos = n - T + r
+        assert idx[r].tolist() == oracle.topk_row(sc[r, :pos + 1].astype(np.float64), k).tolist()
+
+
+def test_empty_batch_is_noop(gpu):
+    seqs = gpu.Seqs([0], [0])
+    z = torch.zeros(16, device="cuda")
+    gpu.indexer_scores(seqs, z.view(1, 1, 16)[:0], z.view(1, 16), z.view(1, 16), scores=z.view(4, 4))
+
+
+# ------------------------------------------------------------------ full-size workloads (sampled)
+
+FULL_ROWS = {
+    "prefill8k": [0, 1, 63, 2046, 2047, 2048, 4095, 5000, 8190, 8191],
+    "decode32k": [0, 17, 63],
+    "chunk128k": [0, 1, 2047, 4094, 4095],
+    "ragged": [0, 5, 64, 127],
+}
+
+
+@pytest.mark.parametrize("name", list(FULL_ROWS))
+def test_full_size_sampled_rows(gpu, name):
+    """The shapes and launch configuration the benchmark times, int variant for the indexer:
+    indices bit-exact and attention within tolerance on sampled rows."""
+    wl = dg.workload(name)
+    say(f"full {name}: generating T={wl.T} Nk={wl.Nk}")
+    x = dg.gen_inputs(wl, "int", seed=0)
+    say("  running")
+    res = run_all(gpu, wl, x)
+    say("  checking")
+    check_rows(wl, x, res, FULL_ROWS[name], "int", DELTA_FP8_MFMA)
