@@ -35,9 +35,15 @@ def hipcc():
     return "hipcc"
 
 
+# per-file code generation options: the indexer consumes every matrix-instruction result with
+# vector instructions, so its MFMAs write the architectural registers directly
+PER_FILE = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src, verbose):
     obj = os.path.join(BUILD, src + ".o")
-    cmd = [hipcc(), *COMMON, *DEVICE, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *COMMON, *DEVICE, *PER_FILE.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src),
+           "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -121,6 +121,8 @@ constexpr int MBLK = 64;           // keys per gathered block
 constexpr int MCH = MDQK / 8;      // 16-byte chunks per latent row (72)
 constexpr int MBUF = MBLK * MDQK * 2;   // bytes per LDS block buffer (73728)
 constexpr int MT = MDQK / 16;      // K steps of the logits product (36)
+constexpr int KRING = 4;           // LDS operand prefetch depth + 1 (logits)
+constexpr int VRING = 4;           // LDS operand prefetch depth + 1 (values)
 
 __device__ __forceinline__ v16f mfma_bf16_32x32x16(const bf16x8& a, const bf16x8& b, const v16f& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -173,7 +175,7 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const uint8_t* p) {
 // One half block (32 keys starting at kbase inside the LDS block): logits, softmax weights,
 // value accumulation. Returns true (uniform over the wave) when some head's logits exceed its
 // reference max by more than kHeadroom; the caller then restarts the row. LDS operands are
-// prefetched one MFMA ahead; scheduling barriers keep the compiler from hoisting further
+// prefetched several MFMAs ahead; scheduling barriers keep the compiler from hoisting further
 // (which would cost registers the resident query block needs).
 __device__ __forceinline__ bool attend_half(const uint8_t* buf, int kbase, uint32_t vmask,
                                             const bf16x8 (&qreg)[MT], v16f (&acc_o)[MDV / 32],
@@ -188,23 +190,27 @@ __device__ __forceinline__ bool attend_half(const uint8_t* buf, int kbase, uint3
   };
   v16f s = {};
   {
-    bf16x8 ka[2];
-    ka[0] = kop(0);
+    bf16x8 ka[KRING];
+#pragma unroll
+    for (int t = 0; t < KRING - 1; ++t) ka[t] = kop(t);
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
-      if (t + 1 < MT) ka[(t + 1) & 1] = kop(t + 1);
-      s = mfma_bf16_32x32x16(ka[t & 1], qreg[t], s);
+      if (t + KRING - 1 < MT) ka[(t + KRING - 1) % KRING] = kop(t + KRING - 1);
+      s = mfma_bf16_32x32x16(ka[t % KRING], qreg[t], s);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
   float bmax = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int key = 8 * (i >> 2) + 4 * g + (i & 3);
-    const float z = ((vmask >> key) & 1u) ? s[i] * sl2 : -INFINITY;
-    s[i] = z;
-    bmax = fmaxf(bmax, z);
+  for (int i = 0; i < 16; ++i) s[i] *= sl2;
+  if (vmask != 0xFFFFFFFFu) {  // uniform: only partly valid halves pay for the masking
+    const uint32_t mlane = vmask >> (4 * g);  // bit 8(i/4) + (i%4) <-> this lane's key i
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (!((mlane >> (8 * (i >> 2) + (i & 3))) & 1u)) s[i] = -INFINITY;
   }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) bmax = fmaxf(bmax, s[i]);
   bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
   if (st.m == -INFINITY) st.m = bmax;  // first non-empty block of the pass
   st.seen = fmaxf(st.seen, bmax);
@@ -236,13 +242,14 @@ __device__ __forceinline__ bool attend_half(const uint8_t* buf, int kbase, uint3
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
   constexpr int NSTEP = 2 * (MDV / 32);
-  bf16x8 va[2];
-  va[0] = vop(0);
+  bf16x8 va[VRING];
+#pragma unroll
+  for (int step = 0; step < VRING - 1; ++step) va[step] = vop(step);
 #pragma unroll
   for (int step = 0; step < NSTEP; ++step) {
-    if (step + 1 < NSTEP) va[(step + 1) & 1] = vop(step + 1);
+    if (step + VRING - 1 < NSTEP) va[(step + VRING - 1) % VRING] = vop(step + VRING - 1);
     const int j = step / (MDV / 32), vt = step % (MDV / 32);
-    acc_o[vt] = mfma_bf16_32x32x16(va[step & 1], pb[j], acc_o[vt]);
+    acc_o[vt] = mfma_bf16_32x32x16(va[step % VRING], pb[j], acc_o[vt]);
     __builtin_amdgcn_sched_barrier(0);
   }
   return false;

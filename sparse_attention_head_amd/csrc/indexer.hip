@@ -78,9 +78,18 @@ __device__ __forceinline__ v4f mfma_fp8_16x16x128(const v8i& a, const v8i& b) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 0, 0, 0);
 }
 
+// ReLU on the bit pattern: a non-negative IEEE float is a non-negative int32 and a negative one
+// (including -0) a negative int32, so max(bits, 0) is ReLU with one integer instruction (the
+// float max would first canonicalise its operand).
+__device__ __forceinline__ float relu_bits(float x) {
+  return __int_as_float(max(__float_as_int(x), 0));
+}
+
 // Computes the scores of RW query rows (one wave) against 16 keys held in `bop`.
 // Returns, per lane, the partial head sum for (row g*RW/4, key l%16) over the heads this lane
-// owns; the caller completes it across lane groups when RW < 4.
+// owns; the caller completes it across lane groups when RW < 4. Matrix instructions and the
+// ReLU/weight epilogue are interleaved, so only a few tiles are live at a time and the vector work
+// overlaps the matrix work (two waves share each SIMD and fill each other's dependency stalls).
 template <int RW>
 __device__ __forceinline__ float score_block(const v8i (&a)[4 * RW], const v8i& bop,
                                              const float (&wv)[16 * RW]) {
@@ -88,10 +97,19 @@ __device__ __forceinline__ float score_block(const v8i (&a)[4 * RW], const v8i& 
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int mm = 0; mm < NMF; ++mm) {
-    v4f d = mfma_fp8_16x16x128(a[mm], bop);
+    const v4f d = mfma_fp8_16x16x128(a[mm], bop);
 #pragma unroll
-    for (int v = 0; v < 4; ++v) acc[v] = fmaf(wv[4 * mm + v], fmaxf(d[v], 0.f), acc[v]);
+    for (int v = 0; v < 4; ++v) acc[v] = fmaf(wv[4 * mm + v], relu_bits(d[v]), acc[v]);
   }
+  // pipeline for the machine scheduler: matrix instructions run ahead of the epilogue, one
+  // matrix instruction per 8 vector instructions
+  __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+#pragma unroll
+  for (int i = 0; i < NMF - 2; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x002, 19, 0);
   return (acc[0] + acc[1]) + (acc[2] + acc[3]);
 }
 
@@ -104,7 +122,7 @@ __device__ __forceinline__ v8i load_slice(const uint8_t* __restrict__ base, int6
 // walk the same keys. Decode (m_b == 1 everywhere): one workgroup = one row and a chunk of keys that
 // the W waves split in interleaved 16-key blocks.
 template <int RW, int W, bool DECODE, int PF>
-__global__ void __launch_bounds__(W * 64)
+__global__ void __launch_bounds__(W * 64, 2)
 indexer_fp8_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
                    const uint8_t* __restrict__ q, const uint8_t* __restrict__ k,
                    const float* __restrict__ w, float* __restrict__ scores, int64_t ld, int KC) {
@@ -145,6 +163,10 @@ indexer_fp8_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __res
     const uint8_t* qrow = q + (int64_t)(q0 + ar) * (kHI * kDI) + (c % HPM) * kDI + g * 32;
 #pragma unroll
     for (int mm = 0; mm < NMF; ++mm) a[mm] = *reinterpret_cast<const v8i*>(qrow + mm * HPM * kDI);
+    // the query tiles are only ever read by the matrix instructions: keep them in the
+    // accumulation registers so the architectural ones hold the weights and the tile results
+#pragma unroll
+    for (int mm = 0; mm < NMF; ++mm) asm volatile("" : "+a"(a[mm]));
   }
   // head weights for this lane's outputs: D row 4g+v -> (row (4g+v)/HPM, head mm*HPM + (4g+v)%HPM)
   const int my_i = wrow0 + (4 * g) / HPM;      // all 4 v of a lane share the row
@@ -176,6 +198,9 @@ indexer_fp8_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __res
       ring[p] = load_slice(k, k0 + min(kb + PF * step + c, n - 1), g);
       if (kb < kend) {
         float acc = score_block<RW>(a, cur, wv);
+        // keep the epilogue in this block (it would otherwise sink into the store's branch and
+        // lose its interleaving with the matrix instructions)
+        asm volatile("" ::"v"(acc));
         if (RW <= 2) acc += __shfl_xor(acc, 16);
         if (RW == 1) acc += __shfl_xor(acc, 32);
         const int s = kb + c;

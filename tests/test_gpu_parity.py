@@ -182,6 +182,27 @@ def test_topk_ties_and_zeros(gpu):
         assert idx[r].tolist() == oracle.topk_row(sc[r, :pos + 1].astype(np.float64), k).tolist()
 
 
+@pytest.mark.parametrize("n", [5000, 30000, 131072, 140000])
+def test_topk_row_lengths_and_degenerate_rows(gpu, n):
+    """Every top-k code path (register-resident rows of 1, 2..8, 9..32 tiles of 4096 and the
+    multi-pass fallback beyond 131072), with degenerate rows: all equal, all +-0, one distinct
+    value, integer ties, and random floats."""
+    k = 2048
+    rng = np.random.default_rng(n)
+    rows = [np.full(n, 1.5, np.float32),
+            np.where(rng.random(n) < 0.5, 0.0, -0.0).astype(np.float32),
+            np.concatenate([np.full(n - 1, -2.0, np.float32), [3.0]]).astype(np.float32),
+            rng.integers(-4, 5, size=n).astype(np.float32),
+            rng.standard_normal(n).astype(np.float32)]
+    sc = np.stack(rows)
+    T = sc.shape[0]
+    seqs = gpu.Seqs([0, T], [0, n])
+    idx = gpu.topk(seqs, torch.from_numpy(sc).cuda(), k).cpu().numpy()
+    for r in range(T):
+        pos = n - T + r
+        assert idx[r].tolist() == oracle.topk_row(sc[r, :pos + 1].astype(np.float64), k).tolist(), f"row {r}"
+
+
 def test_empty_batch_is_noop(gpu):
     seqs = gpu.Seqs([0], [0])
     z = torch.zeros(16, device="cuda")
