@@ -17,10 +17,13 @@
 //   * O^T += V^T P^T (M = 512 value dims, N = 32 heads, K = 64 keys); P never leaves registers:
 //     the S^T accumulator layout is used directly as the B operand, and V^T is read from LDS with
 //     the same permutation of the key index.
-// LDS layout of a gathered block: 72 column chunks of 16 bytes; chunk c of key s lives in 16-byte
-// slot c*64 + (s ^ (c & 7)). The XOR spreads the value dims of one key over the banks for the
-// transposing V^T reads; for every read it splits into loop-invariant lane bits and compile-time
-// bits, so each LDS read is one of a few per-lane base registers plus an immediate offset.
+// LDS layout of a gathered block (16-byte slots): chunk c (dims 8c..8c+7) of key s lives in slot
+//   (c / 8) * 512 + (s / 8) * 64 + (s % 8) * 8 + ((c % 8) ^ (s % 8)).
+// One DMA instruction fills 64 consecutive slots = 8 chunks of 8 keys, i.e. 8 whole 128-byte
+// lines of the latent cache (fully coalesced). The XOR keeps the 32-key reads of one chunk (S^T)
+// and the transposing value reads (V^T) free of bank conflicts, and splits for every read into
+// loop-invariant lane bits plus compile-time bits, so each LDS read is one of a few per-lane base
+// registers plus an immediate offset.
 #include "dsa_internal.h"
 #include "device_common.h"
 
@@ -128,8 +131,6 @@ __device__ __forceinline__ v16f mfma_bf16_32x32x16(const bf16x8& a, const bf16x8
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// byte offset of (key s, 16-byte chunk c) inside a block buffer
-__device__ __forceinline__ int slot_off(int s, int c) { return ((c << 6) + (s ^ (c & 7))) << 4; }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
@@ -137,20 +138,22 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
-// Issue the gather of one block into `buf`. Wave w copies chunks c = 4i + w (i = 0..17); lane l
-// copies key l ^ (c & 7) = l ^ (4(i & 1) + w), so that the DMA's lane-linear LDS writes land in
-// the swizzled slots. row_a / row_b are the latent rows of keys l ^ w and l ^ (w + 4).
+// Issue the gather of one block into `buf`. Wave w copies key groups R = 2w + u (u = 0, 1; keys
+// 8R .. 8R+7) for chunk groups G = 0..8. In each instruction lane l covers key 8R + l/8 and chunk
+// 8G + ((l % 8) ^ (l / 8)), which lands in slot G*512 + R*64 + l: the lane-linear LDS writes of the
+// DMA match the swizzled layout. row_u is the latent row of key 8(2w + u) + l/8.
 __device__ __forceinline__ void gather_block(uint8_t* buf, const uint8_t* __restrict__ kv,
-                                             int64_t row_a, int64_t row_b, int wave) {
-  const uint8_t* pa = kv + row_a * (MDQK * 2) + wave * 16;
-  const uint8_t* pb = kv + row_b * (MDQK * 2) + wave * 16;
+                                             int64_t row0, int64_t row1, int wave, int lane) {
+  const int sw = ((lane & 7) ^ (lane >> 3)) * 16;
 #pragma unroll
-  for (int i = 0; i < MCH / 4; ++i) {
-    const int c = 4 * i + wave;
-    const uint8_t* src = ((i & 1) ? pb : pa) + i * 64;
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
-                                     (__attribute__((address_space(3))) void*)(buf + c * 1024),
-                                     16, 0, 0);
+  for (int u = 0; u < 2; ++u) {
+    const uint8_t* src = kv + (u ? row1 : row0) * (MDQK * 2) + sw;
+    const int R = 2 * wave + u;
+#pragma unroll
+    for (int G = 0; G < MCH / 8; ++G)
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src + G * 128),
+                                       (__attribute__((address_space(3))) void*)(buf + (G * 512 + R * 64) * 16),
+                                       16, 0, 0);
   }
 }
 
@@ -182,11 +185,14 @@ __device__ __forceinline__ bool attend_half(const uint8_t* buf, int kbase, uint3
                                             SoftmaxState& st, float sl2, int lane) {
   const int g = lane >> 5, c32 = lane & 31;
   // S^T = K Q^T: M = 32 keys, N = 32 heads; lane holds head c32, keys 8(i/4) + 4g + (i%4).
-  // chunk c = 2t + g of key kbase + c32 sits in slot c*64 + kbase + ((c32 ^ g) ^ (2t & 6))
-  const uint8_t* kb_lane = buf + ((g << 6) + kbase) * 16;
-  const int kx = c32 ^ g;
+  // chunk c = 2t + g of key s = kbase + c32: c/8 = t/4, c%8 = 2(t%4) + g, so the slot is
+  // (t/4)*512 + (s/8)*64 + (s%8)*8 + ((2(t%4) + g) ^ (s%8))
+  const uint8_t* kb_lane = buf + (((kbase + c32) >> 3) * 64 + (c32 & 7) * 8) * 16;
+  int kx[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) kx[q] = ((2 * q + g) ^ (c32 & 7)) * 16;
   auto kop = [&](int t) -> bf16x8 {
-    return *reinterpret_cast<const bf16x8*>(kb_lane + (kx ^ (2 * t & 6)) * 16 + t * 2048);
+    return *reinterpret_cast<const bf16x8*>(kb_lane + kx[t & 3] + (t >> 2) * 8192);
   };
   v16f s = {};
   {
@@ -228,17 +234,20 @@ __device__ __forceinline__ bool attend_half(const uint8_t* buf, int kbase, uint3
   // (h = 0, 1; jj = 0..3): the lane's P values i = 8j + 4h + jj. The V^T operand comes from two
   // transposing reads: lane (4jj + q) of each 16-lane group points at value dims
   // v0 = 32vt + 16*(group & 1) + 4q .. +3 of key 16j + 8h + 4g + jj.
-  // chunk c = 4vt + 2grp + q/2 has swizzle c & 7 = 4(vt & 1) + 2grp + q/2, and the key's low 3
-  // bits are 4g + jj, so slot = c*64 + kbase + 16j + 8h + ((4g + jj) ^ (2grp + q/2) ^ 4(vt & 1)).
+  // chunk c = 4vt + 2grp + q/2: c/8 = vt/2, c%8 = 4(vt%2) + 2grp + q/2; key s = kbase + 16j + 8h
+  // + 4g + jj: s/8 = kbase/8 + 2j + h, s%8 = 4g + jj. Slot (vt/2)*512 + (s/8)*64 + (s%8)*8 +
+  // ((c%8) ^ (s%8)), byte offset 8 * (q % 2) inside it.
   const int grp = (lane >> 4) & 1, li = lane & 15;
   const int jj = li >> 2, q4 = li & 3;
-  const uint8_t* vb_lane = buf + ((2 * grp + (q4 >> 1)) * 64 + kbase) * 16 + (q4 & 1) * 8;
-  const int klo = (4 * g + jj) ^ (2 * grp + (q4 >> 1));
+  const uint8_t* vb_lane = buf + ((kbase >> 3) * 64 + (4 * g + jj) * 8) * 16 + (q4 & 1) * 8;
+  int vx[2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) vx[p] = ((4 * p + 2 * grp + (q4 >> 1)) ^ (4 * g + jj)) * 16;
   auto vop = [&](int step) -> bf16x8 {
     const int j = step / (MDV / 32), vt = step % (MDV / 32);
-    const uint8_t* p = vb_lane + (klo ^ (4 * (vt & 1))) * 16 + vt * 4096 + j * 256;
+    const uint8_t* p = vb_lane + vx[vt & 1] + (vt >> 1) * 8192 + j * 2048;
     const s16x4 lo = lds_read_tr16(p);
-    const s16x4 hi = lds_read_tr16(p + 128);
+    const s16x4 hi = lds_read_tr16(p + 1024);
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
   constexpr int NSTEP = 2 * (MDV / 32);
@@ -300,13 +309,13 @@ attn_bf16_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restr
     const int j = blk * MBLK + lane;
     return (blk < nblk && j < k) ? ir[j] : -1;
   };
-  // latent rows of keys l ^ w and l ^ (w + 4) (see gather_block) and the block's valid mask
+  // latent rows of keys 16w + l/8 and 16w + 8 + l/8 (see gather_block) and the block's valid mask
   auto prep = [&](int sidx, int64_t& ra, int64_t& rb, uint64_t& vm) {
     const bool valid = sidx >= 0 && sidx < L.n;
     vm = __ballot(valid);
     const int row = L.kofs + (valid ? sidx : 0);
-    ra = __shfl_xor(row, wave);
-    rb = __shfl_xor(row, wave + 4);
+    ra = __shfl(row, 16 * wave + (lane >> 3));
+    rb = __shfl(row, 16 * wave + 8 + (lane >> 3));
   };
 
   // Pipeline: wait for the block in flight, barrier (its LDS data is complete and every wave
@@ -323,7 +332,7 @@ attn_bf16_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restr
     int64_t ra, rb;
     uint64_t vm_cur, vm_next;
     prep(load_idx(0), ra, rb, vm_cur);
-    if (vm_cur) gather_block(buf0, kv, ra, rb, wave);
+    if (vm_cur) gather_block(buf0, kv, ra, rb, wave, lane);
     int idx_next = load_idx(1);
     bool restart = false;
     for (int blk = 0; blk < nblk; blk += 2) {
@@ -331,7 +340,7 @@ attn_bf16_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restr
       __syncthreads();
       if (blk > 0 && s_flag[(step - 1) & 1] == step - 1) { restart = true; break; }
       prep(idx_next, ra, rb, vm_next);
-      if (blk + 1 < nblk && vm_next) gather_block(buf1, kv, ra, rb, wave);
+      if (blk + 1 < nblk && vm_next) gather_block(buf1, kv, ra, rb, wave, lane);
       idx_next = load_idx(blk + 2);
       if (vm_cur && attend_block(buf0, vm_cur, qreg, acc_o, st, sl2, lane)) s_flag[step & 1] = step;
       ++step;
@@ -342,7 +351,7 @@ attn_bf16_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restr
       __syncthreads();
       if (s_flag[(step - 1) & 1] == step - 1) { restart = true; break; }
       prep(idx_next, ra, rb, vm_next);
-      if (blk + 2 < nblk && vm_next) gather_block(buf0, kv, ra, rb, wave);
+      if (blk + 2 < nblk && vm_next) gather_block(buf0, kv, ra, rb, wave, lane);
       idx_next = load_idx(blk + 3);
       if (vm_cur && attend_block(buf1, vm_cur, qreg, acc_o, st, sl2, lane)) s_flag[step & 1] = step;
       ++step;

@@ -157,17 +157,6 @@ __device__ __forceinline__ uint32_t block_excl_scan2(uint32_t a, uint32_t b, uin
   return ba + xa - a;
 }
 
-// Inclusive scan of two small counts across the wave (packed in one 32-bit value).
-__device__ __forceinline__ uint32_t wave_incl_scan_packed(uint32_t x) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t t = __shfl_up(x, off);
-    if (lane >= off) x += t;
-  }
-  return x;
-}
-
 // Finds the bin holding the need-th largest key among the counted ones (suffix sums from the
 // top bin down). Called by all threads; wave 0 does the work.
 __device__ __forceinline__ void select_bin(const uint32_t* hist, int nb, uint32_t need,
@@ -204,17 +193,39 @@ __device__ __forceinline__ void select_bin(const uint32_t* hist, int nb, uint32_
   __syncthreads();
 }
 
-constexpr int TK_TILE = 4 * TK_THREADS;  // positions per tile
+constexpr int TK_TILE = 4 * TK_THREADS;      // positions per tile (one float4 per thread)
+constexpr int TK_CHUNK_TILES = 2;              // tiles per staged chunk (32 KB)
+constexpr int TK_RING = 4;                     // staged chunks in flight
 
+__device__ __forceinline__ uint32_t lanes_below_count(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Register-resident selection for rows of up to 4096 * NT candidates (one workgroup per row).
+//  1. The row streams through LDS (4 chunks of 32 KB in flight, DMA) into registers: thread t
+//     keeps the upper 16 bits of the keys of positions 4096j + 4t + c (c = 0..3), two per
+//     register. The histogram of digit 1 (key bits 31..21) is built on the way: fully for the
+//     first 8192 positions, and above a floor bin chosen from that sample for the rest (exact: if
+//     fewer than k keys turn out to lie above the floor, the histogram is rebuilt from registers).
+//  2. One pass over the registers marks each position "above" (digit 1 > d1) or "candidate"
+//     (digit 1 == d1) in per-thread bitmasks.
+//  3. The candidates -- the keys of one 11-bit bin, a small share of the row -- are refined by
+//     re-reading their full keys: digits 2 (bits 20..16), 3 (15..8) and 4 (7..0), then their
+//     class against the threshold T.
+//  4. Ordered compaction from the bitmasks: per (tile, wave) counts from ballots, one block-wide
+//     exclusive scan in (tile, wave) order -- which is position order -- and per-lane offsets
+//     from lanes-below popcounts.
 template <int NT>
 __global__ void __launch_bounds__(TK_THREADS)
 topk_reg_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
                 const float* __restrict__ scores, int64_t ld, int k, int32_t* __restrict__ idx) {
+  constexpr int NCH = (NT + TK_CHUNK_TILES - 1) / TK_CHUNK_TILES;  // staged chunks per row
   constexpr int NM = (4 * NT + 31) / 32;     // 32-bit words of per-thread position masks
+  __shared__ __attribute__((aligned(16))) float stage[TK_RING][TK_CHUNK_TILES * TK_TILE];
   __shared__ uint32_t hist[2048];
   __shared__ uint32_t cnt[NT * TK_WAVES][2];  // per (tile, wave): keys > T, keys == T
   __shared__ uint32_t sw[2 * TK_WAVES];
-  __shared__ uint32_t s_digit, s_above;
+  __shared__ uint32_t s_digit, s_above, s_floor;
 
   const int r = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -228,138 +239,239 @@ topk_reg_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restri
     return;
   }
   const int tiles = (n + TK_TILE - 1) / TK_TILE;  // <= NT
+  const int chunks = (tiles + TK_CHUNK_TILES - 1) / TK_CHUNK_TILES;
+  for (int i = tid; i < 2048; i += TK_THREADS) hist[i] = 0;
 
-  // Upper key halves: hk[2j] holds positions c = 0, 1 of tile j, hk[2j+1] c = 2, 3. Positions
-  // past the end of the row get key 0, below the key of every finite float (whose top 11 bits
-  // are >= 4), so they never reach the selection and need no bound checks later.
+  // Staging: chunk c (tiles 2c, 2c+1) is copied into stage[c % TK_RING] by 32 DMA instructions,
+  // two per wave; lane l of instruction i of wave w copies the float4 at chunk offset
+  // (2w + i)*256 + 4l. Float4s starting at or past the end of the row read the row start instead
+  // (their values are discarded; a float4 straddling the end stays inside ld >= round_up(n, 4)).
+  auto issue = [&](int c) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int off = (2 * wave + i) * 256;
+      const int e = c * TK_CHUNK_TILES * TK_TILE + off + 4 * lane;
+      const float* src = row + (e < n ? e : 0);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
+                                       (__attribute__((address_space(3))) void*)(&stage[c % TK_RING][off]),
+                                       16, 0, 0);
+    }
+  };
+#pragma unroll
+  for (int c = 0; c < TK_RING - 1; ++c)
+    if (c < chunks) issue(c);
+
   uint32_t hk[2 * NT];
+  uint32_t floor_bin = 0;
+  __syncthreads();  // hist cleared
 #pragma unroll
-  for (int j = 0; j < NT; ++j) {
-    const int e = j * TK_TILE + 4 * tid;
-    uint32_t k4[4] = {0u, 0u, 0u, 0u};
-    if (j < tiles) {
-      if (e + 3 < n) {
-        const float4 v = *reinterpret_cast<const float4*>(row + e);
-        k4[0] = float_to_ordered(v.x);
-        k4[1] = float_to_ordered(v.y);
-        k4[2] = float_to_ordered(v.z);
-        k4[3] = float_to_ordered(v.w);
+  for (int c = 0; c < NCH; ++c) {
+    if (c < chunks) {  // uniform
+      if (c + TK_RING - 1 < chunks) {
+        issue(c + TK_RING - 1);
+        asm volatile("s_waitcnt vmcnt(6)" ::: "memory");  // chunk c has landed (3 newer in flight)
       } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+      __syncthreads();
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-          if (e + c < n) k4[c] = float_to_ordered(row[e + c]);
+      for (int h = 0; h < TK_CHUNK_TILES; ++h) {
+        const int j = c * TK_CHUNK_TILES + h;
+        if (j < NT) {
+          const int e = j * TK_TILE + 4 * tid;
+          const float4 v = *reinterpret_cast<const float4*>(&stage[c % TK_RING][h * TK_TILE + 4 * tid]);
+          const float f[4] = {v.x, v.y, v.z, v.w};
+          uint32_t k4[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) k4[q] = e + q < n ? float_to_ordered(f[q]) : 0u;
+          hk[2 * j] = (k4[0] >> 16) | (k4[1] & 0xFFFF0000u);
+          hk[2 * j + 1] = (k4[2] >> 16) | (k4[3] & 0xFFFF0000u);
+          asm volatile("" : "+v"(hk[2 * j]), "+v"(hk[2 * j + 1]));
+          if (j < tiles)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const uint32_t d = k4[q] >> 21;
+              if (d >= floor_bin) atomicAdd(&hist[d], 1u);
+            }
+        }
+      }
+      if (c == 0 && chunks > 1) {
+        // floor bin: from the first 8192 positions (a sample), the bin holding the
+        // (4 k S / n + 64)-th largest key -- several times the expected share above the
+        // threshold; later keys below it are not binned
+        __syncthreads();
+        const uint32_t want = (uint32_t)min((int64_t)TK_CHUNK_TILES * TK_TILE,
+                                            4LL * k * (TK_CHUNK_TILES * TK_TILE) / n + 64);
+        select_bin(hist, 2048, want, &s_digit, &s_above);
+        if (tid == 0) s_floor = s_digit;
+        __syncthreads();
+        floor_bin = s_floor;
+      }
+      __syncthreads();  // stage[c % TK_RING] may be refilled
+    } else {
+#pragma unroll
+      for (int h = 0; h < TK_CHUNK_TILES; ++h) {
+        const int j = c * TK_CHUNK_TILES + h;
+        if (j < NT) { hk[2 * j] = 0u; hk[2 * j + 1] = 0u; }
       }
     }
-    hk[2 * j] = (k4[0] >> 16) | (k4[1] & 0xFFFF0000u);
-    hk[2 * j + 1] = (k4[2] >> 16) | (k4[3] & 0xFFFF0000u);
-    // opaque from here on: later digit extractions must use the packed halves, not the full
-    // keys (which the compiler would otherwise keep alive)
-    asm volatile("" : "+v"(hk[2 * j]), "+v"(hk[2 * j + 1]));
-    if ((j & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // bound the loads in flight
   }
 #define HI(j, c) ((hk[2 * (j) + ((c) >> 1)] >> (16 * ((c) & 1))) & 0xFFFFu)
 
   uint32_t need = (uint32_t)k;
-  // digit 1: key bits 31..21 = upper-half bits 15..5
-  for (int i = tid; i < 2048; i += TK_THREADS) hist[i] = 0;
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < NT; ++j)
-    if (j < tiles)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) atomicAdd(&hist[HI(j, c) >> 5], 1u);
+  // exact check of the floor: at least k keys must lie in bins >= floor_bin (only keys of the
+  // first chunk were binned below it, and those bins are never reached in that case)
+  if (tid == 0) s_digit = 0xFFFFFFFFu;
   __syncthreads();
   select_bin(hist, 2048, need, &s_digit, &s_above);
+  if (s_digit == 0xFFFFFFFFu || s_digit < floor_bin) {  // uniform: rebuild from registers
+    __syncthreads();
+    for (int i = tid; i < 2048; i += TK_THREADS) hist[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+      if (j < tiles)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) atomicAdd(&hist[HI(j, c) >> 5], 1u);
+    __syncthreads();
+    select_bin(hist, 2048, need, &s_digit, &s_above);
+  }
   const uint32_t d1 = s_digit;
   need -= s_above;
-  __syncthreads();
-  // digit 2: key bits 20..16 among upper halves whose digit 1 is d1
-  if (tid < 32) hist[tid] = 0;
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < NT; ++j)
-    if (j < tiles)
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        if ((HI(j, c) >> 5) == d1) atomicAdd(&hist[HI(j, c) & 31u], 1u);
-  __syncthreads();
-  select_bin(hist, 32, need, &s_digit, &s_above);
-  const uint32_t P16 = (d1 << 5) | s_digit;
-  need -= s_above;
-  __syncthreads();
 
-  // positions whose upper half equals P16 (bit 4j + c): only these need their low halves
-  uint32_t tie[NM];
+  // above / candidate bitmasks (bit 4j + c)
+  uint32_t abv[NM], cand[NM];
 #pragma unroll
-  for (int w = 0; w < NM; ++w) tie[w] = 0u;
+  for (int w = 0; w < NM; ++w) { abv[w] = 0u; cand[w] = 0u; }
 #pragma unroll
   for (int j = 0; j < NT; ++j)
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
-      if (HI(j, c) == P16) tie[(4 * j + c) >> 5] |= 1u << ((4 * j + c) & 31);
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t d = HI(j, c) >> 5;
+      abv[(4 * j + c) >> 5] |= (d > d1 ? 1u : 0u) << ((4 * j + c) & 31);
+      cand[(4 * j + c) >> 5] |= (d == d1 ? 1u : 0u) << ((4 * j + c) & 31);
+    }
   const float* mine = row + 4 * tid;  // position of bit b: (b / 4) * TK_TILE + 4 * tid + b % 4
-  // digits 3 and 4: bits 15..8 and 7..0 of those keys, re-read from memory (few of them)
-  uint32_t lo_prefix = 0, lo_mask = 0;
+  // The thread's first CK candidates: full keys loaded once into registers (independent loads,
+  // in flight together). Threads with more candidates re-read the rest in each pass below.
+  constexpr int CK = 4;
+  uint32_t ckey[CK], cbit[CK];
+  int ncand = 0;
+  uint32_t rest[NM];  // candidates beyond the first CK
+#pragma unroll
+  for (int w = 0; w < NM; ++w) rest[w] = cand[w];
+#pragma unroll
+  for (int i = 0; i < CK; ++i) {
+    cbit[i] = 0xFFFFFFFFu;
+    ckey[i] = 0u;
+#pragma unroll
+    for (int w = 0; w < NM; ++w) {
+      if (cbit[i] == 0xFFFFFFFFu && rest[w]) {
+        const int b = __ffs(rest[w]) - 1;
+        rest[w] &= rest[w] - 1;
+        cbit[i] = 32 * w + b;
+      }
+    }
+    if (cbit[i] != 0xFFFFFFFFu) {
+      ckey[i] = float_to_ordered(mine[(cbit[i] >> 2) * TK_TILE + (cbit[i] & 3)]);
+      ++ncand;
+    }
+  }
+  uint32_t rest_or = 0u;
+#pragma unroll
+  for (int w = 0; w < NM; ++w) rest_or |= rest[w];
+  const bool any_rest = __ballot(rest_or != 0u) != 0ull;  // uniform: rare
+
+  // digits 2, 3, 4 over the candidates' full keys (key bits 20..16, 15..8, 7..0)
+  uint32_t low_prefix = d1 << 21, low_mask = 0xFFE00000u;
 #pragma unroll 1
-  for (int pass = 0; pass < 2; ++pass) {
-    const int shift = pass == 0 ? 8 : 0;
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 16 : (pass == 1 ? 8 : 0);
+    const int nb = pass == 0 ? 32 : 256;
+    __syncthreads();
     if (tid < 256) hist[tid] = 0;
     __syncthreads();
+#pragma unroll
+    for (int i = 0; i < CK; ++i)
+      if (i < ncand && (ckey[i] & low_mask) == low_prefix)
+        atomicAdd(&hist[(ckey[i] >> shift) & (uint32_t)(nb - 1)], 1u);
+    if (any_rest) {
 #pragma unroll 1
-    for (int w = 0; w < NM; ++w) {
-      uint32_t m = tie[w];
-      while (m) {
-        const int bit = 32 * w + __ffs(m) - 1;
-        m &= m - 1;
-        const uint32_t lo = float_to_ordered(mine[(bit >> 2) * TK_TILE + (bit & 3)]) & 0xFFFFu;
-        if ((lo & lo_mask) == lo_prefix) atomicAdd(&hist[(lo >> shift) & 255u], 1u);
+      for (int w = 0; w < NM; ++w) {
+        uint32_t m = rest[w];
+        while (m) {
+          const int bit = 32 * w + __ffs(m) - 1;
+          m &= m - 1;
+          const uint32_t key = float_to_ordered(mine[(bit >> 2) * TK_TILE + (bit & 3)]);
+          if ((key & low_mask) == low_prefix) atomicAdd(&hist[(key >> shift) & (uint32_t)(nb - 1)], 1u);
+        }
       }
     }
     __syncthreads();
-    select_bin(hist, 256, need, &s_digit, &s_above);
-    lo_prefix |= s_digit << shift;
-    lo_mask |= 255u << shift;
+    select_bin(hist, nb, need, &s_digit, &s_above);
+    low_prefix |= s_digit << shift;
+    low_mask |= (uint32_t)(nb - 1) << shift;
     need -= s_above;
-    __syncthreads();
   }
-  const uint32_t T = (P16 << 16) | lo_prefix;  // the k-th largest key; `need` keys == T go in
+  const uint32_t T = low_prefix;  // the k-th largest key; `need` keys == T go in
 
-  // classes of the tied positions: above T / equal to T
-  uint32_t tgt[NM], teq[NM];
-#pragma unroll 1
+  // final classes: gt = above, or a candidate whose key > T; eq = a candidate whose key == T
+  uint32_t gtm[NM], eqm[NM];
+  uint32_t any_eq_lane = 0u;
+#pragma unroll
   for (int w = 0; w < NM; ++w) {
-    uint32_t m = tie[w], a = 0u, e = 0u;
-    while (m) {
-      const int b = __ffs(m) - 1;
-      m &= m - 1;
-      const int bit = 32 * w + b;
-      const uint32_t full = float_to_ordered(mine[(bit >> 2) * TK_TILE + (bit & 3)]);
-      a |= (full > T ? 1u : 0u) << b;
-      e |= (full == T ? 1u : 0u) << b;
-    }
-    tgt[w] = a;
-    teq[w] = e;
+    uint32_t a = 0u, e = 0u;
+#pragma unroll
+    for (int i = 0; i < CK; ++i)
+      if (i < ncand && (int)(cbit[i] >> 5) == w) {
+        a |= (ckey[i] > T ? 1u : 0u) << (cbit[i] & 31);
+        e |= (ckey[i] == T ? 1u : 0u) << (cbit[i] & 31);
+      }
+    gtm[w] = a;
+    eqm[w] = e;
   }
-  // class of position (j, c): bit 0 = key > T, bit 1 = key == T
-#define CLS(j, c)                                                                             \
-  (HI(j, c) > P16 ? 1u                                                                        \
-                  : ((((tgt[(4 * (j) + (c)) >> 5] >> ((4 * (j) + (c)) & 31)) & 1u)) |            \
-                     (((teq[(4 * (j) + (c)) >> 5] >> ((4 * (j) + (c)) & 31)) & 1u) << 1)))
+  if (any_rest) {
+#pragma unroll 1
+    for (int w = 0; w < NM; ++w) {
+      uint32_t m = rest[w], a = 0u, e = 0u;
+      while (m) {
+        const int b = __ffs(m) - 1;
+        m &= m - 1;
+        const int bit = 32 * w + b;
+        const uint32_t key = float_to_ordered(mine[(bit >> 2) * TK_TILE + (bit & 3)]);
+        a |= (key > T ? 1u : 0u) << b;
+        e |= (key == T ? 1u : 0u) << b;
+      }
+      // runtime word index: merge through a compile-time loop (keeps the arrays in registers)
+#pragma unroll
+      for (int v = 0; v < NM; ++v)
+        if (v == w) { gtm[v] |= a; eqm[v] |= e; }
+    }
+  }
+#pragma unroll
+  for (int w = 0; w < NM; ++w) {
+    any_eq_lane |= eqm[w];
+    gtm[w] |= abv[w];
+  }
+  const bool any_eq = __ballot(any_eq_lane != 0u) != 0ull;  // uniform
 
-  // counts (packed: > T in the low 16 bits, == T in the high 16 bits) per (tile, wave)
+  // counts per (tile, wave) from ballots
+#define NIB(msk, j) (((msk)[(j) >> 3] >> (4 * ((j) & 7))) & 15u)
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
     if (j < tiles) {
-      uint32_t pc = 0;
+      const uint32_t g4 = NIB(gtm, j);
+      uint32_t ng = 0u, nq = 0u;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const uint32_t cl = CLS(j, c);
-        pc += (cl & 1u) | ((cl >> 1) << 16);
+      for (int c = 0; c < 4; ++c) ng += (uint32_t)__popcll(__ballot((g4 >> c) & 1u));
+      if (any_eq) {
+        const uint32_t q4 = NIB(eqm, j);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) nq += (uint32_t)__popcll(__ballot((q4 >> c) & 1u));
       }
-      const uint32_t incl = wave_incl_scan_packed(pc);
-      if (lane == 63) {
-        cnt[j * TK_WAVES + wave][0] = incl & 0xFFFFu;
-        cnt[j * TK_WAVES + wave][1] = incl >> 16;
+      if (lane == 0) {
+        cnt[j * TK_WAVES + wave][0] = ng;
+        cnt[j * TK_WAVES + wave][1] = nq;
       }
     }
   }
@@ -379,26 +491,29 @@ topk_reg_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restri
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
     if (j < tiles) {
-      uint32_t cls[4], pc = 0;
+      const uint32_t gt4 = NIB(gtm, j), eq4 = any_eq ? NIB(eqm, j) : 0u;
+      if (__ballot((gt4 | eq4) != 0u)) {  // uniform: skip tiles with nothing selected in this wave
+        uint32_t gb = cnt[j * TK_WAVES + wave][0], qb = cnt[j * TK_WAVES + wave][1];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        cls[c] = CLS(j, c);
-        pc += (cls[c] & 1u) | ((cls[c] >> 1) << 16);
-      }
-      const uint32_t excl = wave_incl_scan_packed(pc) - pc;
-      uint32_t gb = cnt[j * TK_WAVES + wave][0] + (excl & 0xFFFFu);
-      uint32_t qb = cnt[j * TK_WAVES + wave][1] + (excl >> 16);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const bool gt = cls[c] == 1u, eq = cls[c] == 2u;
-        const uint32_t at = gb + min(qb, need);
-        if ((gt || (eq && qb < need)) && at < (uint32_t)k) out[at] = j * TK_TILE + 4 * tid + c;
-        gb += gt;
-        qb += eq;
+        for (int c = 0; c < 4; ++c) {
+          gb += lanes_below_count(__ballot((gt4 >> c) & 1u));
+          if (any_eq) qb += lanes_below_count(__ballot((eq4 >> c) & 1u));
+        }
+        uint32_t m = gt4 | eq4;
+        while (m) {  // the lane's few selected positions of this tile, in position order
+          const int c = __ffs(m) - 1;
+          m &= m - 1;
+          const uint32_t below = (1u << c) - 1u;
+          const uint32_t g_at = gb + (uint32_t)__popc(gt4 & below);
+          const uint32_t q_at = qb + (uint32_t)__popc(eq4 & below);
+          const bool take = ((gt4 >> c) & 1u) || q_at < need;
+          const uint32_t at = g_at + min(q_at, need);
+          if (take && at < (uint32_t)k) out[at] = j * TK_TILE + 4 * tid + c;
+        }
       }
     }
   }
-#undef CLS
+#undef NIB
 #undef HI
 }
 
