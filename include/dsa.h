@@ -1,8 +1,11 @@
 /*
  * dsa.h -- C ABI of the DeepSeek Sparse Attention (DSA) forward path on MI355X (gfx950).
  *
- * The operation (DeepSeek-V3.2 paper digest, "Key claims", paper section 2.1, Eq. 1-2 and
- * Fig. 2; "Method"; 36kr article, section "02. Built on the final version of DeepSeek-V3.1"):
+ * The operation, as the pages define it -- page "DeepSeek-V3.2: Pushing the Frontier of Open Large
+ * Language Models" (paper digest), sections "Key claims" (paper section 2.1, Eq. 1-2, Fig. 2) and
+ * "Method"; page "A paper signed by Liang Wenfeng: The most powerful open-source Agent model of
+ * DeepSeek has made a big splash" (36kr), section "02. Built on the final version of
+ * DeepSeek-V3.1, DSA makes model computation smarter":
  *
  *   1. lightning indexer: for each query token t and each key s at or before it,
  *        I[t,s] = sum_j w[t,j] * ReLU(qI[t,j] . kI[s])        (H_I indexer heads, FP8 inputs)
@@ -75,7 +78,7 @@ typedef struct {
 /* ---------------------------------------------------------------- step 1: lightning indexer
  * I[r,s] = sum_{j<H_I} w[r,j] * max(0, sum_{d<d_I} qI[r,j,d] * kI[kofs_b + s, d])
  * for every query row r (sequence b, position pos) and s = 0..pos.
- * (paper digest, "Key claims": paper section 2.1, Eq. 1; ReLU, few heads, FP8.)
+ * (paper digest page, "Key claims": paper section 2.1, Eq. 1; ReLU, few heads, FP8.)
  *
  *   qk_dtype  DSA_FP8_E4M3 (H_I = 64, d_I = 128: FP8 matrix-core path) or DSA_F32 (any
  *             1 <= H_I <= 128, 1 <= d_I <= 256: vector path). Accumulation is fp32.
@@ -92,7 +95,7 @@ dsa_status_t dsa_indexer_scores(const dsa_seqs_t* seqs, int32_t H_I, int32_t d_I
 
 /* ---------------------------------------------------------------- step 2: top-k selection
  * For each row r: the min(k, pos+1) positions s <= pos with the largest scores[r, s]
- * (36kr article section 02: keep the entries with the top-k index scores; paper digest
+ * (36kr page, section 02: keep the entries with the top-k index scores; paper digest page,
  * "Key claims", Eq. 2). Ties prefer the lower position; +0 and -0 are equal. The positions are
  * written in ascending order to indices[r, 0..], and the rest of the row is filled with -1.
  *

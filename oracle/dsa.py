@@ -3,16 +3,18 @@
 Sources (page titles and sections; the pages print no code and no worked example):
   [digest]  "DeepSeek-V3.2: Pushing the Frontier of Open Large Language Models", paper digest,
             "Key claims" (paper section 2.1, Eq. 1-2 and Fig. 2) and "Method".
-  [36kr]    36kr article on DeepSeek-V3.2, section "02. Built on the final version of
+  [36kr]    "A paper signed by Liang Wenfeng: The most powerful open-source Agent model of
+            DeepSeek has made a big splash" (36kr), section "02. Built on the final version of
             DeepSeek-V3.1, DSA makes model computation smarter".
-  [blog]    aitoearn blog "DeepSeek V3.2 series", "Technical Innovations in V3.2" and
-            "Training Process", Phase 2 (2,048 key-value pairs per query token).
+  [blog]    "DeepSeek-V3.2 Series Open Source, Performance Rivals Gemini-3.0-Pro" (aitoearn),
+            "Technical Innovations in V3.2" and "Training Process", Phase 2 (each query token
+            selects 2,048 key-value entries).
 
 Conventions (readings where the pages are silent; each is listed with its reason in the design
 notes of the repository):
   * Sequence b has m_b query rows and n_b keys; query i of b sits at position pos = n_b - m_b + i
-    and its candidates are keys s = 0..pos (inclusive: "all preceding tokens" is read as the
-    causal prefix including the token itself, otherwise position 0 has nothing to attend to).
+    and its candidates are keys s = 0..pos (inclusive: the tokens before the query are read as
+    the causal prefix including the token itself, otherwise position 0 has nothing to attend to).
   * Scores are float64; no scale factors are applied to the FP8 inputs.
   * Top-k: the min(k, pos+1) candidates with the largest score; equal scores prefer the lower
     position (+0 and -0 are equal); the chosen positions are returned in ascending order and the

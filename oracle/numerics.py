@@ -1,9 +1,11 @@
 """Decoding of the stored number formats into float64 (oracle side; test infrastructure only).
 
-The DSA pages say the lightning indexer runs in FP8 (36kr article, section "02. Built on the
-final version of DeepSeek-V3.1": the indexer "can be implemented in FP8"; paper digest, "Key
-claims", paper section 2.1: "FP8 implementation"). They do not name the format; the workloads
-fix OCP FP8 E4M3 ("e4m3fn": no infinities, 0x7F/0xFF are NaN, bias 7, largest finite 448).
+The DSA pages say the lightning indexer runs in FP8 (page "A paper signed by Liang Wenfeng: The
+most powerful open-source Agent model of DeepSeek has made a big splash" (36kr), section "02. Built
+on the final version of DeepSeek-V3.1, DSA makes model computation smarter"; page "DeepSeek-V3.2:
+Pushing the Frontier of Open Large Language Models" (paper digest), section "Key claims", paper
+section 2.1). They do not name the format; the workloads fix OCP FP8 E4M3 (e4m3fn: no
+infinities, 0x7F/0xFF are NaN, bias 7, largest finite 448).
 
 Inputs are given already encoded; the oracle never quantises. Encodings:
   uint8   -> OCP FP8 e4m3fn code

@@ -1,9 +1,10 @@
 // Sparse MLA attention in MQA mode on gfx950.
 //
 // For each query row and head, softmax attention over the selected latent rows only; one latent
-// row per key is shared by all query heads of the token (DeepSeek-V3.2 paper digest, "Key
-// claims": paper section 2.1, Eq. 2 and Fig. 2; "Method": MLA's MQA mode, so every selected KV
-// entry is shared across the query heads). Key = the whole d_qk-dim row, value = its first d_v
+// row per key is shared by all query heads of the token (page "DeepSeek-V3.2: Pushing the
+// Frontier of Open Large Language Models" (paper digest), section "Key claims": paper section 2.1,
+// Eq. 2 and Fig. 2; section "Method": MLA's MQA mode, so every selected KV entry is shared across
+// the query heads). Key = the whole d_qk-dim row, value = its first d_v
 // dims.
 //
 // BF16 matrix path (H = 128, d_qk = 576, d_v = 512), one workgroup per query row, 4 waves, wave w

@@ -2,9 +2,11 @@
 //
 //   I[r, s] = sum_j w[r, j] * ReLU(qI[r, j] . kI[s])      for s = 0..pos(r)
 //
-// (DeepSeek-V3.2 paper digest, "Key claims": paper section 2.1, Eq. 1 -- few indexer heads,
-//  ReLU, FP8. 36kr article, section "02. Built on the final version of DeepSeek-V3.1": index
-//  scores between a query token and the tokens before it.)
+// (page "DeepSeek-V3.2: Pushing the Frontier of Open Large Language Models" (paper digest),
+//  section "Key claims": paper section 2.1, Eq. 1 -- few indexer heads, ReLU, FP8. Page "A paper
+//  signed by Liang Wenfeng: The most powerful open-source Agent model of DeepSeek has made a big
+//  splash" (36kr), section "02. Built on the final version of DeepSeek-V3.1, DSA makes model
+//  computation smarter": index scores between a query token and the tokens before it.)
 //
 // FP8 path (H_I = 64, d_I = 128). The score is a dense contraction: for a block of query rows the
 // products qI[r, j] . kI[s] form a GEMM of shape [rows * 64 heads, 128] x [128, keys]. d_I = 128

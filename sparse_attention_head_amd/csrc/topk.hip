@@ -1,8 +1,11 @@
 // Causal per-row top-k selection on gfx950.
 //
 // For each query row: the min(k, pos+1) positions s <= pos with the largest index scores
-// (36kr article, section "02. Built on the final version of DeepSeek-V3.1": retrieve only the
-// entries with the top-k index scores; paper digest, "Key claims", paper section 2.1, Eq. 2).
+// (page "A paper signed by Liang Wenfeng: The most powerful open-source Agent model of DeepSeek
+// has made a big splash" (36kr), section "02. Built on the final version of DeepSeek-V3.1, DSA
+// makes model computation smarter": retrieve only the entries with the top-k index scores; page
+// "DeepSeek-V3.2: Pushing the Frontier of Open Large Language Models" (paper digest), section "Key
+// claims", paper section 2.1, Eq. 2).
 // Ties prefer the lower position, +0 equals -0, output ascending and padded with -1.
 //
 // Method (exact, deterministic): scores map to order-preserving 32-bit keys. A radix select over
