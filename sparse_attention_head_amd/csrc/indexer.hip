@@ -30,6 +30,7 @@ namespace dsa {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef int v4i __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------- fp32 vector path
 
@@ -213,6 +214,116 @@ indexer_fp8_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __res
   }
 }
 
+// ---------------------------------------------------------------------------- prefill, LDS-staged keys
+// Workgroup = 8 waves x 4 rows = 32 query rows of one sequence against a chunk of keys. The keys
+// stream through a ring of LDS stages (256 keys = 32 KB each) filled by DMA (global_load_lds); all
+// waves share them. Inside a stage, key s occupies 128 bytes whose 16-byte chunk c sits at
+// position c ^ (s % 8): the B-operand reads of 16 consecutive keys (lane l: key l%16, chunks
+// 2(l/16), 2(l/16)+1) then spread over all banks.
+constexpr int PF_W = 8;                 // waves per workgroup
+constexpr int PF_RW = 4;                // rows per wave
+constexpr int PF_ROWS = PF_W * PF_RW;   // 32
+constexpr int PF_SK = 256;              // keys per stage
+constexpr int PF_NR = 3;                // stages in the ring
+
+__global__ void __launch_bounds__(PF_W * 64, 1)
+indexer_fp8_prefill_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
+                           const uint8_t* __restrict__ q, const uint8_t* __restrict__ k,
+                           const float* __restrict__ w, float* __restrict__ scores, int64_t ld,
+                           int KC) {
+  __shared__ __attribute__((aligned(1024))) uint8_t kst[PF_NR][PF_SK * kDI];
+  constexpr int RW = PF_RW, HPM = 16 / RW, NMF = 4 * RW;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const int b = blockIdx.z, chunk = blockIdx.y, i_base = blockIdx.x * PF_ROWS;
+  const int q0 = cu_q[b], m = cu_q[b + 1] - q0;
+  const int k0 = cu_k[b], n = cu_k[b + 1] - k0;
+  if (i_base >= m) return;
+  const int tile_last = min(m, i_base + PF_ROWS) - 1;
+  const int kbeg = chunk * KC;
+  if (kbeg > n - m + tile_last) return;                     // uniform over the workgroup
+  const int kend = min(kbeg + KC, n - m + tile_last + 1);   // workgroup's key range end
+  const int nst = (kend - kbeg + PF_SK - 1) / PF_SK;
+
+  // this wave's rows (may be past m in the tile tail: computed on clamped rows, never stored)
+  const int wrow0 = i_base + wave * RW;
+  const int wrow_last = min(m - 1, wrow0 + RW - 1);
+  const int wkend = wrow0 < m ? min(kend, n - m + wrow_last + 1) : kbeg;
+
+  v8i a[NMF];
+  {
+    const int ar = min(wrow0 + c / HPM, m - 1);
+    const uint8_t* qrow = q + (int64_t)(q0 + ar) * (kHI * kDI) + (c % HPM) * kDI + g * 32;
+#pragma unroll
+    for (int mm = 0; mm < NMF; ++mm) a[mm] = *reinterpret_cast<const v8i*>(qrow + mm * HPM * kDI);
+#pragma unroll
+    for (int mm = 0; mm < NMF; ++mm) asm volatile("" : "+a"(a[mm]));
+  }
+  const int my_i = wrow0 + (4 * g) / HPM;
+  float wv[16 * RW];
+  {
+    const float* wr = w + (int64_t)(q0 + min(my_i, m - 1)) * kHI;
+#pragma unroll
+    for (int mm = 0; mm < NMF; ++mm)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) wv[4 * mm + v] = wr[mm * HPM + (4 * g + v) % HPM];
+  }
+  const bool row_ok = my_i < m;
+  const int my_pos = n - m + my_i;
+  float* srow = scores + (int64_t)(q0 + min(my_i, m - 1)) * ld;
+
+  // DMA of stage st: 32 instructions of 1 KB (8 keys each), 4 per wave; lane l covers key
+  // (instruction*8 + l/8) and the logical chunk (l%8) ^ (key%8) of it.
+  const int dch = ((lane & 7) ^ ((lane >> 3) & 7)) * 16;
+  auto issue = [&](int st) {
+    uint8_t* dst = kst[st % PF_NR];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int inst = wave * 4 + i;
+      const int key = kbeg + st * PF_SK + inst * 8 + (lane >> 3);
+      const uint8_t* src = k + (int64_t)(k0 + min(key, n - 1)) * kDI + dch;
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
+                                       (__attribute__((address_space(3))) void*)(dst + inst * 1024),
+                                       16, 0, 0);
+    }
+  };
+#pragma unroll
+  for (int st = 0; st < PF_NR - 1; ++st)
+    if (st < nst) issue(st);
+
+  // B operand of 16 keys starting at stage-local key kl: lane's key kl + c, chunks 2g, 2g+1
+  const int bx0 = ((2 * g) ^ (c & 7)) * 16, bx1 = ((2 * g + 1) ^ (c & 7)) * 16;
+  auto load_b = [&](const uint8_t* buf, int kl) -> v8i {
+    const uint8_t* rowp = buf + (kl + c) * kDI;
+    const v4i lo = *reinterpret_cast<const v4i*>(rowp + bx0);
+    const v4i hi = *reinterpret_cast<const v4i*>(rowp + bx1);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+
+  for (int st = 0; st < nst; ++st) {
+    // stage st landed (and the previous stage's score stores completed); every wave is done
+    // with the buffer the next DMA refills
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (st + PF_NR - 1 < nst) issue(st + PF_NR - 1);
+    const uint8_t* buf = kst[st % PF_NR];
+    const int sbase = kbeg + st * PF_SK;
+    const int nblk = min(PF_SK, wkend - sbase) > 0 ? (min(PF_SK, wkend - sbase) + 15) / 16 : 0;
+    if (nblk > 0) {
+      v8i cur = load_b(buf, 0);
+      for (int blk = 0; blk < nblk; ++blk) {
+        const v8i nxt = load_b(buf, min(blk + 1, PF_SK / 16 - 1) * 16);
+        float acc = score_block<RW>(a, cur, wv);
+        asm volatile("" ::"v"(acc));
+        const int s = sbase + blk * 16 + c;
+        if (row_ok && s <= my_pos && s < wkend) srow[s] = acc;
+        cur = nxt;
+      }
+    }
+  }
+}
+
 // Key-chunk length: long enough to amortise loading the query tile, short enough to give
 // several workgroups per compute unit.
 static int pick_chunk(int64_t tiles, int max_n, int cus, int align) {
@@ -224,12 +335,11 @@ static int pick_chunk(int64_t tiles, int max_n, int cus, int align) {
 hipError_t launch_indexer_fp8_prefill(const SeqInfo& s, const uint8_t* q, const uint8_t* k,
                                       const float* w, float* scores, int64_t ld, hipStream_t st) {
   if (s.T == 0 || s.max_n == 0) return hipSuccess;
-  constexpr int RW = 4, W = 4, ROWS = RW * W;
-  const int tiles = (s.max_m + ROWS - 1) / ROWS;
-  const int kc = pick_chunk((int64_t)tiles * s.B, s.max_n, device_cu_count(), 64);
+  const int tiles = (s.max_m + PF_ROWS - 1) / PF_ROWS;
+  const int kc = pick_chunk((int64_t)tiles * s.B, s.max_n, device_cu_count(), PF_SK);
   dim3 grid(tiles, (s.max_n + kc - 1) / kc, s.B);
-  hipLaunchKernelGGL((indexer_fp8_kernel<RW, W, false, 2>), grid, dim3(W * 64), 0, st, s.B,
-                     s.cu_q, s.cu_k, q, k, w, scores, ld, kc);
+  hipLaunchKernelGGL(indexer_fp8_prefill_kernel, grid, dim3(PF_W * 64), 0, st, s.B, s.cu_q, s.cu_k,
+                     q, k, w, scores, ld, kc);
   return hipGetLastError();
 }
 
