@@ -100,10 +100,12 @@ def measure(torch, dsa, wl, T, seqs, steps, warmup):
     idx = torch.empty((wl.T, wl.k), dtype=torch.int32, device="cuda")
     out = torch.empty((wl.T, wl.H, wl.d_v), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((wl.T, wl.H), dtype=torch.float32, device="cuda")
+    iws_n = dsa.indexer_workspace_size(seqs, wl.H_I, wl.d_I, dsa._dtype_code(T["qI"]))
+    iws = torch.empty(max(iws_n, 1), dtype=torch.uint8, device="cuda")
     # the stages alone (each on its own, inputs produced by the previous stage)
-    dsa.indexer_scores(seqs, T["qI"], T["kI"], T["w"], scores=scores)
+    dsa.indexer_scores(seqs, T["qI"], T["kI"], T["w"], scores=scores, ws=iws)
     dsa.topk(seqs, scores, wl.k, indices=idx)
-    t_idx = time_loop(torch, lambda: dsa.indexer_scores(seqs, T["qI"], T["kI"], T["w"], scores=scores),
+    t_idx = time_loop(torch, lambda: dsa.indexer_scores(seqs, T["qI"], T["kI"], T["w"], scores=scores, ws=iws),
                       steps, warmup)
     t_topk = time_loop(torch, lambda: dsa.topk(seqs, scores, wl.k, indices=idx), steps, warmup)
     t_attn = time_loop(torch, lambda: dsa.sparse_mla_attn(seqs, T["q"], T["kv"], idx, wl.scale, wl.d_v,

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 1
+#define DSA_ABI_VERSION 2
 
 typedef enum {
   DSA_OK = 0,
@@ -88,10 +88,17 @@ typedef struct {
  *   scores    [T, ld_scores] fp32 (output)     row r holds I[r, 0..pos]; entries beyond pos are
  *             left unspecified (they may be overwritten). ld_scores >= max_seqlen_k, and a
  *             multiple of 4.
+ *   ws        device workspace of at least dsa_indexer_workspace_size(seqs, H_I, d_I, qk_dtype)
+ *             bytes, 16-byte aligned (may be NULL when that size is 0); contents on entry do not
+ *             matter. The FP8 path for batches with more than one query row per sequence keeps
+ *             per-row data of the query side there (T * 516 bytes, rounded up).
  */
+size_t dsa_indexer_workspace_size(const dsa_seqs_t* seqs, int32_t H_I, int32_t d_I,
+                                  dsa_dtype_t qk_dtype);
 dsa_status_t dsa_indexer_scores(const dsa_seqs_t* seqs, int32_t H_I, int32_t d_I,
                                 dsa_dtype_t qk_dtype, const void* q_idx, const void* k_idx,
-                                const float* w, float* scores, int64_t ld_scores, void* stream);
+                                const float* w, float* scores, int64_t ld_scores, void* ws,
+                                size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------- step 2: top-k selection
  * For each row r: the min(k, pos+1) positions s <= pos with the largest scores[r, s]

@@ -25,7 +25,7 @@ import numpy as np
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa.so")
 
 if not os.path.exists(_LIB_PATH):
-    raise ImportError(f"{_LIB_PATH} is missing; build it with `python -m sparse_attention_head_amd.build`")
+    raise ImportError(f"{_LIB_PATH} is missing; build it with `python sparse_attention_head_amd/build.py`")
 
 _lib = ctypes.CDLL(_LIB_PATH)
 
@@ -63,9 +63,11 @@ def _proto(name, res, args):
     return f
 
 
+_c_indexer_ws = _proto("dsa_indexer_workspace_size", ctypes.c_size_t,
+                       [ctypes.POINTER(_Seqs), ctypes.c_int32, ctypes.c_int32, ctypes.c_int])
 _c_indexer = _proto("dsa_indexer_scores", ctypes.c_int,
                     [ctypes.POINTER(_Seqs), ctypes.c_int32, ctypes.c_int32, ctypes.c_int, _vp, _vp, _vp,
-                     _vp, ctypes.c_int64, _vp])
+                     _vp, ctypes.c_int64, _vp, ctypes.c_size_t, _vp])
 _c_topk_ws = _proto("dsa_topk_workspace_size", ctypes.c_size_t, [ctypes.POINTER(_Seqs), ctypes.c_int32])
 _c_topk = _proto("dsa_topk", ctypes.c_int,
                  [ctypes.POINTER(_Seqs), _vp, ctypes.c_int64, ctypes.c_int32, _vp, _vp, ctypes.c_size_t, _vp])
@@ -82,7 +84,7 @@ _c_status = _proto("dsa_status_string", ctypes.c_char_p, [ctypes.c_int])
 _c_last = _proto("dsa_last_error", ctypes.c_char_p, [])
 _c_abi = _proto("dsa_abi_version", ctypes.c_int32, [])
 
-EXPORTS = ("dsa_indexer_scores", "dsa_topk_workspace_size", "dsa_topk", "dsa_sparse_mla_attn_workspace_size",
+EXPORTS = ("dsa_indexer_workspace_size", "dsa_indexer_scores", "dsa_topk_workspace_size", "dsa_topk", "dsa_sparse_mla_attn_workspace_size",
            "dsa_sparse_mla_attn", "dsa_forward_workspace_size", "dsa_forward", "dsa_status_string",
            "dsa_last_error", "dsa_abi_version")
 
@@ -174,15 +176,28 @@ def scores_ld(max_seqlen_k: int) -> int:
 
 # ---------------------------------------------------------------- the four calls
 
-def indexer_scores(seqs: Seqs, q_idx, k_idx, w, scores=None, stream=None):
-    """I[r, s] for s <= pos(r); returns scores [T, ld] fp32 (entries beyond pos unspecified)."""
+def indexer_workspace_size(seqs: Seqs, H_I: int, d_I: int, qk_dtype: int) -> int:
+    cs = seqs.c()
+    return int(_c_indexer_ws(ctypes.byref(cs), H_I, d_I, qk_dtype))
+
+
+def indexer_scores(seqs: Seqs, q_idx, k_idx, w, scores=None, ws=None, stream=None):
+    """I[r, s] for s <= pos(r); returns scores [T, ld] fp32 (entries beyond pos unspecified).
+    `ws` (uint8 device tensor of indexer_workspace_size bytes) is allocated when not given."""
     torch = _torch()
     H_I, d_I = int(q_idx.shape[1]), int(q_idx.shape[2])
     if scores is None:
         scores = torch.empty((seqs.T, scores_ld(seqs.max_n)), dtype=torch.float32, device=q_idx.device)
     cs = seqs.c()
-    _check(_c_indexer(ctypes.byref(cs), H_I, d_I, _dtype_code(q_idx), _ptr(q_idx), _ptr(k_idx), _ptr(w),
-                      _ptr(scores), int(scores.stride(0)), _stream(stream)), "dsa_indexer_scores")
+    dt = _dtype_code(q_idx)
+    wsz = int(_c_indexer_ws(ctypes.byref(cs), H_I, d_I, dt))
+    if ws is None and wsz:
+        ws = torch.empty(wsz, dtype=torch.uint8, device=q_idx.device)
+    elif ws is not None:
+        wsz = ws.numel()
+    _check(_c_indexer(ctypes.byref(cs), H_I, d_I, dt, _ptr(q_idx), _ptr(k_idx), _ptr(w),
+                      _ptr(scores), int(scores.stride(0)), _ptr(ws), wsz, _stream(stream)),
+           "dsa_indexer_scores")
     return scores
 
 

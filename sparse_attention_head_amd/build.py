@@ -1,6 +1,8 @@
 """Builds libdsa.so (HIP kernels + C ABI) for gfx950 in-tree with hipcc.
 
-    python -m sparse_attention_head_amd.build [-v]
+    python sparse_attention_head_amd/build.py [-v]
+
+(run as a script: importing the package would load the library before it is rebuilt)
 
 Every call recompiles all sources. Objects go to <repo>/_build/, the library to
 sparse_attention_head_amd/libdsa.so.

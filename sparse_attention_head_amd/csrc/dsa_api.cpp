@@ -132,9 +132,14 @@ dsa_status_t check_attn(const dsa::SeqInfo& s, int32_t H, int32_t d_qk, int32_t 
   return ok();
 }
 
+// Bytes of indexer workspace: the FP8 prefill path keeps per-row data of the query side there.
+size_t indexer_ws_bytes(const dsa::SeqInfo& s, dsa_dtype_t dt) {
+  return (dt == DSA_FP8_E4M3 && s.max_m > 1) ? dsa::indexer_workspace_bytes(s, true) : 0;
+}
+
 dsa_status_t run_indexer(const dsa::SeqInfo& s, int32_t H_I, int32_t d_I, dsa_dtype_t dt,
                          const void* q, const void* k, const float* w, float* scores, int64_t ld,
-                         hipStream_t st) {
+                         void* ws, hipStream_t st) {
   if (s.T == 0) return ok();
   hipError_t e;
   if (dt == DSA_F32)
@@ -145,7 +150,7 @@ dsa_status_t run_indexer(const dsa::SeqInfo& s, int32_t H_I, int32_t d_I, dsa_dt
                                        static_cast<const uint8_t*>(k), w, scores, ld, st);
   else
     e = dsa::launch_indexer_fp8_prefill(s, static_cast<const uint8_t*>(q),
-                                        static_cast<const uint8_t*>(k), w, scores, ld, st);
+                                        static_cast<const uint8_t*>(k), w, scores, ld, ws, st);
   return hip_status(e, "indexer launch");
 }
 
@@ -166,6 +171,7 @@ dsa_status_t run_attn(const dsa::SeqInfo& s, int32_t H, int32_t d_qk, int32_t d_
 
 struct ForwardPlan {
   int64_t ld;
+  size_t index_off, index_bytes;
   size_t scores_off, scores_bytes;
   size_t idx_off, idx_bytes;
   size_t topk_off, topk_bytes;
@@ -178,6 +184,9 @@ ForwardPlan plan_forward(const dsa::SeqInfo& s, const dsa_forward_args_t* a) {
   p.ld = ((int64_t)s.max_n + 3) / 4 * 4;
   if (p.ld == 0) p.ld = 4;
   size_t off = 0;
+  p.index_bytes = align_up(indexer_ws_bytes(s, a->qk_dtype));
+  p.index_off = off;
+  off += p.index_bytes;
   p.scores_bytes = a->scores_out ? 0 : align_up((size_t)s.T * p.ld * sizeof(float));
   p.scores_off = off;
   off += p.scores_bytes;
@@ -218,16 +227,28 @@ int device_cu_count() {
 
 extern "C" {
 
+size_t dsa_indexer_workspace_size(const dsa_seqs_t* seqs, int32_t H_I, int32_t d_I,
+                                  dsa_dtype_t qk_dtype) {
+  dsa::SeqInfo s;
+  if (check_seqs(seqs, s) != DSA_OK || s.B == 0 || H_I <= 0 || d_I <= 0) return 0;
+  return indexer_ws_bytes(s, qk_dtype);
+}
+
 dsa_status_t dsa_indexer_scores(const dsa_seqs_t* seqs, int32_t H_I, int32_t d_I,
                                 dsa_dtype_t qk_dtype, const void* q_idx, const void* k_idx,
-                                const float* w, float* scores, int64_t ld_scores, void* stream) {
+                                const float* w, float* scores, int64_t ld_scores, void* ws,
+                                size_t ws_bytes, void* stream) {
   dsa::SeqInfo s;
   dsa_status_t st = check_seqs(seqs, s);
   if (st != DSA_OK) return st;
   if (s.B == 0) return ok();
   st = check_indexer(s, H_I, d_I, qk_dtype, q_idx, k_idx, w, scores, ld_scores);
   if (st != DSA_OK) return st;
-  return run_indexer(s, H_I, d_I, qk_dtype, q_idx, k_idx, w, scores, ld_scores,
+  const size_t need = indexer_ws_bytes(s, qk_dtype);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(DSA_ERR_WORKSPACE, "indexer workspace needs %zu bytes, got %zu", need, ws_bytes);
+  if (ws && !aligned16(ws)) return fail(DSA_ERR_ALIGN, "workspace must be 16-byte aligned");
+  return run_indexer(s, H_I, d_I, qk_dtype, q_idx, k_idx, w, scores, ld_scores, ws,
                      static_cast<hipStream_t>(stream));
 }
 
@@ -310,7 +331,8 @@ dsa_status_t dsa_forward(const dsa_seqs_t* seqs, const dsa_forward_args_t* a, vo
   float* scores = a->scores_out ? a->scores_out : reinterpret_cast<float*>(base + p.scores_off);
   int32_t* idx = a->indices_out ? a->indices_out : reinterpret_cast<int32_t*>(base + p.idx_off);
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  st = run_indexer(s, a->H_I, a->d_I, a->qk_dtype, a->q_idx, a->k_idx, a->w, scores, ld, hs);
+  st = run_indexer(s, a->H_I, a->d_I, a->qk_dtype, a->q_idx, a->k_idx, a->w, scores, ld,
+                   base ? base + p.index_off : nullptr, hs);
   if (st != DSA_OK) return st;
   st = hip_status(dsa::launch_topk(s, scores, ld, a->k, idx, base ? base + p.topk_off : nullptr,
                                    p.topk_bytes, hs),

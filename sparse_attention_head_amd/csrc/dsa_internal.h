@@ -24,8 +24,10 @@ struct SeqInfo {
 // ---------------------------------------------------------------- indexer
 hipError_t launch_indexer_f32(const SeqInfo& s, int H_I, int d_I, const float* q, const float* k,
                               const float* w, float* scores, int64_t ld, hipStream_t st);
+size_t indexer_workspace_bytes(const SeqInfo& s, bool fp8);
 hipError_t launch_indexer_fp8_prefill(const SeqInfo& s, const uint8_t* q, const uint8_t* k,
-                                      const float* w, float* scores, int64_t ld, hipStream_t st);
+                                      const float* w, float* scores, int64_t ld, void* ws,
+                                      hipStream_t st);
 hipError_t launch_indexer_fp8_decode(const SeqInfo& s, const uint8_t* q, const uint8_t* k,
                                      const float* w, float* scores, int64_t ld, hipStream_t st);
 

@@ -215,6 +215,226 @@ indexer_fp8_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __res
 }
 
 // ---------------------------------------------------------------------------- prefill, LDS-staged keys
+// The epilogue above costs two vector instructions (max, fma) per (row, head, key), as much vector
+// time as the matrix instruction that produced the 4 values takes, so it, not the matrix core,
+// bounded the kernel. The prefill path halves it with the identity
+//
+//   sum_j w_j max(0, x_j) = 1/2 sum_j w_j |x_j|  +  1/2 sum_j w_j x_j ,
+//
+// whose first sum is one fma per value (|x| is a free source modifier) and whose second sum is
+// linear in the key: sum_j w_j (qI_j . k) = u . k with u = sum_j w_j qI_j, one 128-long vector
+// per query row. That dot product runs on the matrix core as one extra 16x16x128 tile per 16 keys:
+// u is split into 4 FP8 pieces, u * 2^-e = sum_p c_p 16^-p + residual (e per row makes
+// max|u * 2^-e| fall in [128, 256); each piece is the round-to-nearest-even E4M3 value of the
+// previous remainder times 16), and the tile's M index is (row, piece). The remainder after 4
+// pieces is at most 2^-16 |u_d| + 2^-22 * 2^e per component; integer-valued inputs split exactly.
+
+// Round to the nearest (ties to even) value of the E4M3 grid; |r| < 448.
+__device__ __forceinline__ float round_e4m3(float r) {
+  uint32_t b = __float_as_uint(r);
+  b = (b + 0x7FFFFu + ((b >> 20) & 1u)) & ~0xFFFFFu;           // 3 fraction bits, normal range
+  const float sub = rintf(r * 512.f) * (1.f / 512.f);           // subnormal grid, multiples of 2^-9
+  return fabsf(r) < 0x1p-6f ? sub : __uint_as_float(b);
+}
+
+// E4M3 code of a value that lies on the E4M3 grid.
+__device__ __forceinline__ uint32_t encode_e4m3(float v) {
+  const uint32_t b = __float_as_uint(v);
+  const float a = fabsf(v);
+  const uint32_t mag = a < 0x1p-6f ? (uint32_t)(a * 512.f)
+                                   : ((((b >> 23) & 0xFFu) - 120u) << 3) | ((b >> 20) & 7u);
+  return ((b >> 24) & 0x80u) | mag;
+}
+
+// Value of an E4M3 code: the code's low 7 bits placed at the top of an fp32 fraction give the
+// value times 2^-120 for normal and subnormal codes alike.
+__device__ __forceinline__ float decode_e4m3(uint32_t c) {
+  return __uint_as_float(((c & 0x80u) << 24) | ((c & 0x7Fu) << 20)) * 0x1p120f;
+}
+
+constexpr int LIN_BYTES = 4 * kDI;   // pieces of one row: [4][128] codes
+
+// One thread per (row, 8 dims): u = sum_j w_j qI_j, the row's exponent e and the 4 pieces.
+// pieces [T][4][128] codes, half_scale [T] = 2^(e-1).
+__global__ void __launch_bounds__(256)
+indexer_fp8_linear_kernel(int T, const uint8_t* __restrict__ q, const float* __restrict__ w,
+                          uint8_t* __restrict__ pieces, float* __restrict__ half_scale) {
+  const int r = min(blockIdx.x * 16 + (threadIdx.x >> 4), T - 1);
+  const int d0 = (threadIdx.x & 15) * 8;
+  const uint8_t* qr = q + (int64_t)r * (kHI * kDI) + d0;
+  const float* wr = w + (int64_t)r * kHI;
+  float u[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < kHI; ++j) {
+    const uint2 c = *reinterpret_cast<const uint2*>(qr + j * kDI);
+    const float wj = wr[j];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      u[i] = fmaf(wj, decode_e4m3(c.x >> (8 * i)), u[i]);
+      u[4 + i] = fmaf(wj, decode_e4m3(c.y >> (8 * i)), u[4 + i]);
+    }
+  }
+  float mx = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) mx = fmaxf(mx, fabsf(u[i]));
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 16));
+  int ex = 0;
+  if (mx > 0.f) {
+    frexpf(mx, &ex);   // mx = f * 2^ex, f in [0.5, 1)
+    ex -= 8;           // max |u| * 2^-ex in [128, 256)
+  }
+  uint32_t code[4][2] = {{0u, 0u}, {0u, 0u}, {0u, 0u}, {0u, 0u}};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float rem = ldexpf(u[i], -ex);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const float v = round_e4m3(rem);
+      code[p][i >> 2] |= encode_e4m3(v) << (8 * (i & 3));
+      rem = (rem - v) * 16.f;
+    }
+  }
+  if (blockIdx.x * 16 + (threadIdx.x >> 4) < T) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+      *reinterpret_cast<uint2*>(pieces + (int64_t)r * LIN_BYTES + p * kDI + d0) =
+          make_uint2(code[p][0], code[p][1]);
+    if (d0 == 0) half_scale[r] = ldexpf(0.5f, ex);
+  }
+}
+
+// Scores of 16 keys against the wave's 4 rows. The keys are the A operand (M index = key) and the
+// query tiles the B operand (N index c -> row c/4 and head 4*mm + c%4, or piece c%4 for the linear
+// tile), so lane (g, c) receives keys 4g+v, v = 0..3, for one (row, head) pair per tile and needs
+// one weight per tile: wt[mm] = w[row c/4, head 4mm + c%4] / 2. The 4 lanes of a quad (c%4) then
+// hold partial sums of the same row; two cross-lane steps add them so that lane (g, c) ends with
+// the score of row c/4 and key 4g + c%4. ls = 2^(e-1) * 16^-(c%4) weights the lane's piece.
+__device__ __forceinline__ float score_block_t(const v8i (&qa)[16], const v8i& ql, const v8i& key,
+                                               const float (&wt)[16], float ls, bool hi2, bool hi1) {
+  const v4f dl = mfma_fp8_16x16x128(key, ql);
+  float acc[4];
+#pragma unroll
+  for (int mm = 0; mm < 16; ++mm) {
+    const v4f d = mfma_fp8_16x16x128(key, qa[mm]);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) acc[v] = mm == 0 ? wt[0] * fabsf(d[v]) : fmaf(wt[mm], fabsf(d[v]), acc[v]);
+  }
+#pragma unroll
+  for (int v = 0; v < 4; ++v) acc[v] = fmaf(ls, dl[v], acc[v]);
+  // quad reduce-scatter: lanes with c&2 keep keys 2,3 (else 0,1), then c&1 picks one of the two
+  const float k0 = hi2 ? acc[2] : acc[0], k1 = hi2 ? acc[3] : acc[1];
+  const float s0 = hi2 ? acc[0] : acc[2], s1 = hi2 ? acc[1] : acc[3];
+  const float n0 = k0 + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(s0), 0x4E, 0xF, 0xF, true));
+  const float n1 = k1 + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(s1), 0x4E, 0xF, 0xF, true));
+  const float kk = hi1 ? n1 : n0, ss = hi1 ? n0 : n1;
+  const float r = kk + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(ss), 0xB1, 0xF, 0xF, true));
+  // the matrix instructions run ahead of their epilogues, 4 vector instructions apart
+  __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+#pragma unroll
+  for (int i = 0; i < 14; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x002, 24, 0);
+  return r;
+}
+
+// A whole stage of NB key blocks as one software pipeline of NB * 17 matrix instructions: step t
+// issues matrix instruction t and the 4 vector instructions that consume the result of
+// instruction t - 3 (by then complete); the cross-lane reduction of a finished block is spread
+// over the next three steps. The keys of block b+1 are read from LDS while block b runs.
+// Steps are instantiated at compile time (every register index is a constant) and
+// sched_barrier keeps them in order.
+struct PipeState {
+  const uint8_t* buf;   // stage buffer + this lane's key row
+  int kb0, kb1;         // this lane's two 16-byte chunks within a key row
+  const v8i* qa;        // [16] head tiles
+  v8i ql;               // linear tile
+  const float* wt;      // [16] halved weights
+  float ls;
+  bool hi2, hi1;
+  float* sp;            // this lane's first score of the stage
+  v8i key[2];
+  v4f d[4];
+  float acc[4], red[4], n0, n1, kk, ss;
+};
+
+template <int NB, int T>
+__device__ __forceinline__ void pipe_step(PipeState& P) {
+  constexpr int NM = 17, LAG = 3, TOT = NB * NM;
+  if constexpr (T < TOT) {
+    constexpr int blk = T / NM, j = T % NM;
+    if constexpr (j == 1 && blk + 1 < NB) {
+      const uint8_t* rowp = P.buf + (blk + 1) * 16 * kDI;
+      const v4i lo = *reinterpret_cast<const v4i*>(rowp + P.kb0);
+      const v4i hi = *reinterpret_cast<const v4i*>(rowp + P.kb1);
+      P.key[(blk + 1) & 1] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+    if constexpr (j == 0)
+      P.d[T % 4] = mfma_fp8_16x16x128(P.key[blk & 1], P.ql);
+    else
+      P.d[T % 4] = mfma_fp8_16x16x128(P.key[blk & 1], P.qa[j - 1]);
+  }
+  constexpr int e = T - LAG;
+  if constexpr (e >= 0 && e < TOT) {
+    constexpr int j = e % NM;
+    const v4f de = P.d[e % 4];
+    if constexpr (j == 0) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) P.acc[v] = P.ls * de[v];
+    } else {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) P.acc[v] = fmaf(P.wt[j - 1], fabsf(de[v]), P.acc[v]);
+    }
+    if constexpr (j == NM - 1) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) P.red[v] = P.acc[v];
+    }
+  }
+  // reduction of block b: its last epilogue ran at step b*NM + NM-1 + LAG; r = 1..3 steps later
+  constexpr int f = T - LAG - (NM - 1);
+  if constexpr (f >= 1 && (f - 1) % NM == 0 && (f - 1) / NM < NB) {
+    const float k0 = P.hi2 ? P.red[2] : P.red[0], k1 = P.hi2 ? P.red[3] : P.red[1];
+    const float s0 = P.hi2 ? P.red[0] : P.red[2], s1 = P.hi2 ? P.red[1] : P.red[3];
+    P.n0 = k0 + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(s0), 0x4E, 0xF, 0xF, true));
+    P.n1 = k1 + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(s1), 0x4E, 0xF, 0xF, true));
+  }
+  if constexpr (f >= 2 && (f - 2) % NM == 0 && (f - 2) / NM < NB) {
+    P.kk = P.hi1 ? P.n1 : P.n0;
+    P.ss = P.hi1 ? P.n0 : P.n1;
+  }
+  if constexpr (f >= 3 && (f - 3) % NM == 0 && (f - 3) / NM < NB) {
+    constexpr int blk = (f - 3) / NM;
+    P.sp[blk * 16] = P.kk + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(P.ss), 0xB1, 0xF, 0xF, true));
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (T + 1 < TOT + LAG + 3) pipe_step<NB, T + 1>(P);
+}
+
+template <int NB>
+__device__ __forceinline__ void stage_pipeline(const uint8_t* __restrict__ buf, int kb0, int kb1,
+                                               const v8i (&qa)[16], const v8i& ql,
+                                               const float (&wt)[16], float ls, bool hi2, bool hi1,
+                                               float* __restrict__ sp) {
+  PipeState P;
+  P.buf = buf;
+  P.kb0 = kb0;
+  P.kb1 = kb1;
+  P.qa = qa;
+  P.ql = ql;
+  P.wt = wt;
+  P.ls = ls;
+  P.hi2 = hi2;
+  P.hi1 = hi1;
+  P.sp = sp;
+  {
+    const v4i lo = *reinterpret_cast<const v4i*>(buf + kb0);
+    const v4i hi = *reinterpret_cast<const v4i*>(buf + kb1);
+    P.key[0] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+  pipe_step<NB, 0>(P);
+}
+
 // Workgroup = 8 waves x 4 rows = 32 query rows of one sequence against a chunk of keys. The keys
 // stream through a ring of LDS stages (256 keys = 32 KB each) filled by DMA (global_load_lds); all
 // waves share them. Inside a stage, key s occupies 128 bytes whose 16-byte chunk c sits at
@@ -229,10 +449,11 @@ constexpr int PF_NR = 3;                // stages in the ring
 __global__ void __launch_bounds__(PF_W * 64, 1)
 indexer_fp8_prefill_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
                            const uint8_t* __restrict__ q, const uint8_t* __restrict__ k,
-                           const float* __restrict__ w, float* __restrict__ scores, int64_t ld,
-                           int KC) {
+                           const float* __restrict__ w, const uint8_t* __restrict__ lin,
+                           const float* __restrict__ lin_half_scale, float* __restrict__ scores,
+                           int64_t ld, int KC) {
   __shared__ __attribute__((aligned(1024))) uint8_t kst[PF_NR][PF_SK * kDI];
-  constexpr int RW = PF_RW, HPM = 16 / RW, NMF = 4 * RW;
+  constexpr int HPM = 4, NMF = 16;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int g = lane >> 4, c = lane & 15;
@@ -247,31 +468,10 @@ indexer_fp8_prefill_kernel(int B, const int32_t* __restrict__ cu_q, const int32_
   const int nst = (kend - kbeg + PF_SK - 1) / PF_SK;
 
   // this wave's rows (may be past m in the tile tail: computed on clamped rows, never stored)
-  const int wrow0 = i_base + wave * RW;
-  const int wrow_last = min(m - 1, wrow0 + RW - 1);
+  const int wrow0 = i_base + wave * PF_RW;
+  const int wrow_last = min(m - 1, wrow0 + PF_RW - 1);
   const int wkend = wrow0 < m ? min(kend, n - m + wrow_last + 1) : kbeg;
-
-  v8i a[NMF];
-  {
-    const int ar = min(wrow0 + c / HPM, m - 1);
-    const uint8_t* qrow = q + (int64_t)(q0 + ar) * (kHI * kDI) + (c % HPM) * kDI + g * 32;
-#pragma unroll
-    for (int mm = 0; mm < NMF; ++mm) a[mm] = *reinterpret_cast<const v8i*>(qrow + mm * HPM * kDI);
-#pragma unroll
-    for (int mm = 0; mm < NMF; ++mm) asm volatile("" : "+a"(a[mm]));
-  }
-  const int my_i = wrow0 + (4 * g) / HPM;
-  float wv[16 * RW];
-  {
-    const float* wr = w + (int64_t)(q0 + min(my_i, m - 1)) * kHI;
-#pragma unroll
-    for (int mm = 0; mm < NMF; ++mm)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) wv[4 * mm + v] = wr[mm * HPM + (4 * g + v) % HPM];
-  }
-  const bool row_ok = my_i < m;
-  const int my_pos = n - m + my_i;
-  float* srow = scores + (int64_t)(q0 + min(my_i, m - 1)) * ld;
+  const bool all_rows = wrow0 + PF_RW <= m;
 
   // DMA of stage st: 32 instructions of 1 KB (8 keys each), 4 per wave; lane l covers key
   // (instruction*8 + l/8) and the logical chunk (l%8) ^ (key%8) of it.
@@ -292,6 +492,33 @@ indexer_fp8_prefill_kernel(int B, const int32_t* __restrict__ cu_q, const int32_
   for (int st = 0; st < PF_NR - 1; ++st)
     if (st < nst) issue(st);
 
+  // query operands: head tiles (lane c -> row c/4, head 4*mm + c%4) and the linear tile (lane c ->
+  // row c/4, piece c%4), K bytes 32g..32g+31; 136 registers, all architectural (the kernel uses no
+  // accumulation registers, so two waves per SIMD get 256 each).
+  v8i a[NMF], al;
+  {
+    const int ar = min(wrow0 + c / HPM, m - 1);
+    const uint8_t* qrow = q + (int64_t)(q0 + ar) * (kHI * kDI) + (c % HPM) * kDI + g * 32;
+#pragma unroll
+    for (int mm = 0; mm < NMF; ++mm) a[mm] = *reinterpret_cast<const v8i*>(qrow + mm * HPM * kDI);
+    al = *reinterpret_cast<const v8i*>(lin + (int64_t)(q0 + ar) * LIN_BYTES + (c % 4) * kDI + g * 32);
+  }
+  // lane (g, c) finishes row c/4 of the wave at key 4g + c%4 of each block
+  const int my_i = wrow0 + (c >> 2);
+  const int my_r = q0 + min(my_i, m - 1);
+  float wt[16];
+  {
+    const float* wr = w + (int64_t)my_r * kHI + (c & 3);
+#pragma unroll
+    for (int mm = 0; mm < 16; ++mm) wt[mm] = 0.5f * wr[4 * mm];
+  }
+  const float ls = lin_half_scale[my_r] * (1.0f / float(1 << (4 * (c & 3))));
+  const bool hi2 = (c & 2) != 0, hi1 = (c & 1) != 0;
+  const bool row_ok = my_i < m;
+  const int my_pos = n - m + my_i;
+  const int kofs = 4 * g + (c & 3);   // this lane's key within a 16-key block
+  float* srow = scores + (int64_t)my_r * ld;
+
   // B operand of 16 keys starting at stage-local key kl: lane's key kl + c, chunks 2g, 2g+1
   const int bx0 = ((2 * g) ^ (c & 7)) * 16, bx1 = ((2 * g + 1) ^ (c & 7)) * 16;
   auto load_b = [&](const uint8_t* buf, int kl) -> v8i {
@@ -309,19 +536,26 @@ indexer_fp8_prefill_kernel(int B, const int32_t* __restrict__ cu_q, const int32_
     if (st + PF_NR - 1 < nst) issue(st + PF_NR - 1);
     const uint8_t* buf = kst[st % PF_NR];
     const int sbase = kbeg + st * PF_SK;
-    const int nblk = min(PF_SK, wkend - sbase) > 0 ? (min(PF_SK, wkend - sbase) + 15) / 16 : 0;
-    if (nblk > 0) {
-      v8i cur = load_b(buf, 0);
+    if (all_rows && sbase + PF_SK <= wkend) {
+      // whole stage for 4 valid rows: every score lands below wkend <= n <= ld (keys past a row's
+      // own position fall in the part of the row the interface leaves unspecified)
+      stage_pipeline<PF_SK / 16>(buf + c * kDI, bx0, bx1, a, al, wt, ls, hi2, hi1,
+                                 srow + sbase + kofs);
+    } else {
+      const int nblk = min(PF_SK, wkend - sbase) > 0 ? (min(PF_SK, wkend - sbase) + 15) / 16 : 0;
       for (int blk = 0; blk < nblk; ++blk) {
-        const v8i nxt = load_b(buf, min(blk + 1, PF_SK / 16 - 1) * 16);
-        float acc = score_block<RW>(a, cur, wv);
+        const float acc = score_block_t(a, al, load_b(buf, blk * 16), wt, ls, hi2, hi1);
         asm volatile("" ::"v"(acc));
-        const int s = sbase + blk * 16 + c;
+        const int s = sbase + blk * 16 + kofs;
         if (row_ok && s <= my_pos && s < wkend) srow[s] = acc;
-        cur = nxt;
       }
     }
   }
+}
+
+size_t indexer_workspace_bytes(const SeqInfo& s, bool fp8) {
+  if (!fp8 || s.T == 0) return 0;
+  return (size_t)s.T * LIN_BYTES + ((size_t)s.T * sizeof(float) + 255) / 256 * 256;
 }
 
 // Key-chunk length: long enough to amortise loading the query tile, short enough to give
@@ -333,13 +567,18 @@ static int pick_chunk(int64_t tiles, int max_n, int cus, int align) {
 }
 
 hipError_t launch_indexer_fp8_prefill(const SeqInfo& s, const uint8_t* q, const uint8_t* k,
-                                      const float* w, float* scores, int64_t ld, hipStream_t st) {
+                                      const float* w, float* scores, int64_t ld, void* ws,
+                                      hipStream_t st) {
   if (s.T == 0 || s.max_n == 0) return hipSuccess;
+  uint8_t* pieces = static_cast<uint8_t*>(ws);
+  float* half_scale = reinterpret_cast<float*>(pieces + (size_t)s.T * LIN_BYTES);
+  hipLaunchKernelGGL(indexer_fp8_linear_kernel, dim3((s.T + 15) / 16), dim3(256), 0, st, s.T, q, w,
+                     pieces, half_scale);
   const int tiles = (s.max_m + PF_ROWS - 1) / PF_ROWS;
   const int kc = pick_chunk((int64_t)tiles * s.B, s.max_n, device_cu_count(), PF_SK);
   dim3 grid(tiles, (s.max_n + kc - 1) / kc, s.B);
   hipLaunchKernelGGL(indexer_fp8_prefill_kernel, grid, dim3(PF_W * 64), 0, st, s.B, s.cu_q, s.cu_k,
-                     q, k, w, scores, ld, kc);
+                     q, k, w, pieces, half_scale, scores, ld, kc);
   return hipGetLastError();
 }
 

@@ -6,6 +6,10 @@ Floating-point contracts checked here:
     delta = accumulation error of one d_I-term dot product relative to sum_d |q k|:
     gamma(d_I) for sequential fp32, DELTA_FP8_MFMA for the FP8 matrix instruction, whose internal
     sum of its 128 products is coarser than fp32 (see DELTA_FP8_MFMA).
+    plus 2^-29 * max_d |u_d| * sum_d |kI_sd| with u = sum_j w_j qI_j: the FP8 prefill kernel takes
+    the score as (sum_j w_j |x_j| + u . k) / 2 and splits u * 2^-e (max |u| * 2^-e in [128, 256))
+    into 4 FP8 pieces, leaving at most 2^-16 |u_d| + 2^-22 * 2^e per component; the relative part
+    and the extra roundings fit inside the first term, the absolute part is this one.
     On integer-valued inputs every partial sum is exact, so scores must match bit for bit.
   * top-k: bit-exact on integer inputs; on N(0,1) inputs "eps-valid": ascending, unique,
     in range, min(k, n) entries, and no candidate outside the set beats one inside it by more
@@ -37,8 +41,10 @@ def score_bound_row(sq: Seqs, qI, kI, w, r, delta):
     q = np.abs(oracle.decode(qI[r]))
     keys = np.abs(oracle.decode(kI[k0:k0 + pos + 1]))
     H_I = q.shape[0]
-    S = np.abs(oracle.decode(w[r])) @ (q @ keys.T)
-    return 2.0 * (delta + gamma(H_I + 1)) * S
+    wr = oracle.decode(w[r])
+    S = np.abs(wr) @ (q @ keys.T)
+    u = wr @ oracle.decode(qI[r])
+    return 2.0 * (delta + gamma(H_I + 1)) * S + 2.0 ** -29 * np.max(np.abs(u)) * keys.sum(axis=1)
 
 
 def check_topk_row(got, exact_scores, eps, k, pos):

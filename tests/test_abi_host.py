@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(dsa):
 
 
 def test_abi_version_and_status_strings(dsa):
-    assert dsa.abi_version() == 1
+    assert dsa.abi_version() == 2
     for st in range(8):
         s = dsa._c_status(st)
         assert s and len(s) >= 2
@@ -75,17 +75,17 @@ def buf(nbytes, misalign=0):
     return a, p
 
 
-def indexer(dsa, sq, H_I=64, d_I=128, dt=2, ptrs=None, ld=None):
+def indexer(dsa, sq, H_I=64, d_I=128, dt=2, ptrs=None, ld=None, ws=None, ws_bytes=0):
     keep, p = buf(64)
     q, k, w, s = ptrs if ptrs else (p, p, p, p)
     ld = ld if ld is not None else (sq.s.max_seqlen_k + 3) // 4 * 4
-    st = dsa._c_indexer(sq.ref, H_I, d_I, dt, q, k, w, s, ld, None)
+    st = dsa._c_indexer(sq.ref, H_I, d_I, dt, q, k, w, s, ld, ws, ws_bytes, None)
     return st
 
 
 def test_indexer_validation(dsa):
     sq = FakeSeqs(dsa, [0, 10], [0, 10])
-    assert dsa._c_indexer(None, 64, 128, 2, 16, 16, 16, 16, 12, None) == dsa.DSA_ERR_NULL
+    assert dsa._c_indexer(None, 64, 128, 2, 16, 16, 16, 16, 12, None, 0, None) == dsa.DSA_ERR_NULL
     assert indexer(dsa, sq, ld=8) == dsa.DSA_ERR_SHAPE                 # ld < max_seqlen_k
     assert indexer(dsa, sq, ld=14) == dsa.DSA_ERR_SHAPE                # ld not a multiple of 4
     assert indexer(dsa, sq, H_I=32) == dsa.DSA_ERR_UNSUPPORTED         # FP8 needs 64 x 128
@@ -96,6 +96,21 @@ def test_indexer_validation(dsa):
     _, pm = buf(64, misalign=4)
     assert indexer(dsa, sq, ptrs=(p, None, p, p)) == dsa.DSA_ERR_NULL
     assert indexer(dsa, sq, ptrs=(p, p, pm, p)) == dsa.DSA_ERR_ALIGN
+
+
+def test_indexer_workspace(dsa):
+    """The FP8 prefill path needs T * 516 bytes (rounded up) of workspace; decode and fp32 need
+    none."""
+    sq = FakeSeqs(dsa, [0, 10], [0, 10])
+    need = dsa._c_indexer_ws(sq.ref, 64, 128, dsa.DSA_FP8_E4M3)
+    assert need >= 10 * 516
+    assert dsa._c_indexer_ws(sq.ref, 64, 128, dsa.DSA_F32) == 0
+    assert dsa._c_indexer_ws(FakeSeqs(dsa, [0, 1, 2], [0, 5, 9]).ref, 64, 128, dsa.DSA_FP8_E4M3) == 0
+    assert indexer(dsa, sq) == dsa.DSA_ERR_WORKSPACE
+    keep, p = buf(need)
+    assert indexer(dsa, sq, ws=p, ws_bytes=need - 1) == dsa.DSA_ERR_WORKSPACE
+    _, pm = buf(need, misalign=4)
+    assert indexer(dsa, sq, ws=pm, ws_bytes=need) == dsa.DSA_ERR_ALIGN
 
 
 def test_seqs_validation(dsa):
