@@ -81,6 +81,13 @@ __device__ __forceinline__ v4f mfma_fp8_16x16x128(const v8i& a, const v8i& b) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 0, 0, 0);
 }
 
+// Same with the B operand scaled per lane: 2^(b_scale - 127) on lane l's column (l % 16) and its
+// K block (l / 16); A unscaled (127 = 1.0).
+__device__ __forceinline__ v4f mfma_fp8_16x16x128_bscale(const v8i& a, const v8i& b, int b_scale) {
+  const v4f zero = {0.f, 0.f, 0.f, 0.f};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 127, 0, b_scale);
+}
+
 // ReLU on the bit pattern: a non-negative IEEE float is a non-negative int32 and a negative one
 // (including -0) a negative int32, so max(bits, 0) is ReLU with one integer instruction (the
 // float max would first canonicalise its operand).
@@ -255,10 +262,11 @@ __device__ __forceinline__ float decode_e4m3(uint32_t c) {
 constexpr int LIN_BYTES = 4 * kDI;   // pieces of one row: [4][128] codes
 
 // One thread per (row, 8 dims): u = sum_j w_j qI_j, the row's exponent e and the 4 pieces.
-// pieces [T][4][128] codes, half_scale [T] = 2^(e-1).
+// pieces [T][4][128] codes; piece_exp [T] = 126 + e, the E8M0 code of 2^(e-1) (the matrix
+// instruction applies 2^(e-1) * 16^-p to piece p through its per-column scale operand).
 __global__ void __launch_bounds__(256)
 indexer_fp8_linear_kernel(int T, const uint8_t* __restrict__ q, const float* __restrict__ w,
-                          uint8_t* __restrict__ pieces, float* __restrict__ half_scale) {
+                          uint8_t* __restrict__ pieces, int32_t* __restrict__ piece_exp) {
   const int r = min(blockIdx.x * 16 + (threadIdx.x >> 4), T - 1);
   const int d0 = (threadIdx.x & 15) * 8;
   const uint8_t* qr = q + (int64_t)r * (kHI * kDI) + d0;
@@ -281,7 +289,10 @@ indexer_fp8_linear_kernel(int T, const uint8_t* __restrict__ q, const float* __r
   int ex = 0;
   if (mx > 0.f) {
     frexpf(mx, &ex);   // mx = f * 2^ex, f in [0.5, 1)
-    ex -= 8;           // max |u| * 2^-ex in [128, 256)
+    // max |u| * 2^-ex in [128, 256); the floor keeps every piece scale 2^(ex-1-4p) in the E8M0
+    // range (rows with max |u| < 2^-105 then split a smaller multiple of u, still exactly
+    // accounted for: the remainder stays below 2^-22 * 2^ex)
+    ex = max(ex - 8, -112);
   }
   uint32_t code[4][2] = {{0u, 0u}, {0u, 0u}, {0u, 0u}, {0u, 0u}};
 #pragma unroll
@@ -299,7 +310,7 @@ indexer_fp8_linear_kernel(int T, const uint8_t* __restrict__ q, const float* __r
     for (int p = 0; p < 4; ++p)
       *reinterpret_cast<uint2*>(pieces + (int64_t)r * LIN_BYTES + p * kDI + d0) =
           make_uint2(code[p][0], code[p][1]);
-    if (d0 == 0) half_scale[r] = ldexpf(0.5f, ex);
+    if (d0 == 0) piece_exp[r] = 126 + ex;
   }
 }
 
@@ -308,19 +319,18 @@ indexer_fp8_linear_kernel(int T, const uint8_t* __restrict__ q, const float* __r
 // tile), so lane (g, c) receives keys 4g+v, v = 0..3, for one (row, head) pair per tile and needs
 // one weight per tile: wt[mm] = w[row c/4, head 4mm + c%4] / 2. The 4 lanes of a quad (c%4) then
 // hold partial sums of the same row; two cross-lane steps add them so that lane (g, c) ends with
-// the score of row c/4 and key 4g + c%4. ls = 2^(e-1) * 16^-(c%4) weights the lane's piece.
+// the score of row c/4 and key 4g + c%4. The linear tile's column scale lsc (E8M0) applies
+// 2^(e-1) * 16^-(c%4) to the lane's piece, so its result starts the accumulation as is.
 __device__ __forceinline__ float score_block_t(const v8i (&qa)[16], const v8i& ql, const v8i& key,
-                                               const float (&wt)[16], float ls, bool hi2, bool hi1) {
-  const v4f dl = mfma_fp8_16x16x128(key, ql);
-  float acc[4];
+                                               const float (&wt)[16], int lsc, bool hi2, bool hi1) {
+  const v4f dl = mfma_fp8_16x16x128_bscale(key, ql, lsc);
+  float acc[4] = {dl[0], dl[1], dl[2], dl[3]};
 #pragma unroll
   for (int mm = 0; mm < 16; ++mm) {
     const v4f d = mfma_fp8_16x16x128(key, qa[mm]);
 #pragma unroll
-    for (int v = 0; v < 4; ++v) acc[v] = mm == 0 ? wt[0] * fabsf(d[v]) : fmaf(wt[mm], fabsf(d[v]), acc[v]);
+    for (int v = 0; v < 4; ++v) acc[v] = fmaf(wt[mm], fabsf(d[v]), acc[v]);
   }
-#pragma unroll
-  for (int v = 0; v < 4; ++v) acc[v] = fmaf(ls, dl[v], acc[v]);
   // quad reduce-scatter: lanes with c&2 keep keys 2,3 (else 0,1), then c&1 picks one of the two
   const float k0 = hi2 ? acc[2] : acc[0], k1 = hi2 ? acc[3] : acc[1];
   const float s0 = hi2 ? acc[0] : acc[2], s1 = hi2 ? acc[1] : acc[3];
@@ -335,7 +345,7 @@ __device__ __forceinline__ float score_block_t(const v8i (&qa)[16], const v8i& q
     __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
   }
-  __builtin_amdgcn_sched_group_barrier(0x002, 24, 0);
+  __builtin_amdgcn_sched_group_barrier(0x002, 20, 0);
   return r;
 }
 
@@ -351,7 +361,7 @@ struct PipeState {
   const v8i* qa;        // [16] head tiles
   v8i ql;               // linear tile
   const float* wt;      // [16] halved weights
-  float ls;
+  int lsc;              // E8M0 column scale of the linear tile
   bool hi2, hi1;
   float* sp;            // this lane's first score of the stage
   v8i key[2];
@@ -371,7 +381,7 @@ __device__ __forceinline__ void pipe_step(PipeState& P) {
       P.key[(blk + 1) & 1] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     }
     if constexpr (j == 0)
-      P.d[T % 4] = mfma_fp8_16x16x128(P.key[blk & 1], P.ql);
+      P.d[T % 4] = mfma_fp8_16x16x128_bscale(P.key[blk & 1], P.ql, P.lsc);
     else
       P.d[T % 4] = mfma_fp8_16x16x128(P.key[blk & 1], P.qa[j - 1]);
   }
@@ -381,7 +391,7 @@ __device__ __forceinline__ void pipe_step(PipeState& P) {
     const v4f de = P.d[e % 4];
     if constexpr (j == 0) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) P.acc[v] = P.ls * de[v];
+      for (int v = 0; v < 4; ++v) P.acc[v] = de[v];
     } else {
 #pragma unroll
       for (int v = 0; v < 4; ++v) P.acc[v] = fmaf(P.wt[j - 1], fabsf(de[v]), P.acc[v]);
@@ -414,7 +424,7 @@ __device__ __forceinline__ void pipe_step(PipeState& P) {
 template <int NB>
 __device__ __forceinline__ void stage_pipeline(const uint8_t* __restrict__ buf, int kb0, int kb1,
                                                const v8i (&qa)[16], const v8i& ql,
-                                               const float (&wt)[16], float ls, bool hi2, bool hi1,
+                                               const float (&wt)[16], int lsc, bool hi2, bool hi1,
                                                float* __restrict__ sp) {
   PipeState P;
   P.buf = buf;
@@ -423,7 +433,7 @@ __device__ __forceinline__ void stage_pipeline(const uint8_t* __restrict__ buf, 
   P.qa = qa;
   P.ql = ql;
   P.wt = wt;
-  P.ls = ls;
+  P.lsc = lsc;
   P.hi2 = hi2;
   P.hi1 = hi1;
   P.sp = sp;
@@ -438,8 +448,11 @@ __device__ __forceinline__ void stage_pipeline(const uint8_t* __restrict__ buf, 
 // Workgroup = 8 waves x 4 rows = 32 query rows of one sequence against a chunk of keys. The keys
 // stream through a ring of LDS stages (256 keys = 32 KB each) filled by DMA (global_load_lds); all
 // waves share them. Inside a stage, key s occupies 128 bytes whose 16-byte chunk c sits at
-// position c ^ (s % 8): the B-operand reads of 16 consecutive keys (lane l: key l%16, chunks
-// 2(l/16), 2(l/16)+1) then spread over all banks.
+// position c ^ key_swz(s % 16). A B-operand read of 16 consecutive keys (lane l: key l%16, one
+// chunk per lane) then touches distinct banks both within each group of 8 lanes (32 four-byte
+// banks cover one key row) and within each group of 16 lanes (64 banks cover two rows).
+__device__ __forceinline__ int key_swz(int s16) { return ((s16 >> 1) ^ ((s16 & 1) << 2)) & 7; }
+
 constexpr int PF_W = 8;                 // waves per workgroup
 constexpr int PF_RW = 4;                // rows per wave
 constexpr int PF_ROWS = PF_W * PF_RW;   // 32
@@ -450,12 +463,12 @@ __global__ void __launch_bounds__(PF_W * 64, 1)
 indexer_fp8_prefill_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
                            const uint8_t* __restrict__ q, const uint8_t* __restrict__ k,
                            const float* __restrict__ w, const uint8_t* __restrict__ lin,
-                           const float* __restrict__ lin_half_scale, float* __restrict__ scores,
+                           const int32_t* __restrict__ piece_exp, float* __restrict__ scores,
                            int64_t ld, int KC) {
   __shared__ __attribute__((aligned(1024))) uint8_t kst[PF_NR][PF_SK * kDI];
   constexpr int HPM = 4, NMF = 16;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int g = lane >> 4, c = lane & 15;
   const int b = blockIdx.z, chunk = blockIdx.y, i_base = blockIdx.x * PF_ROWS;
   const int q0 = cu_q[b], m = cu_q[b + 1] - q0;
@@ -473,16 +486,18 @@ indexer_fp8_prefill_kernel(int B, const int32_t* __restrict__ cu_q, const int32_
   const int wkend = wrow0 < m ? min(kend, n - m + wrow_last + 1) : kbeg;
   const bool all_rows = wrow0 + PF_RW <= m;
 
-  // DMA of stage st: 32 instructions of 1 KB (8 keys each), 4 per wave; lane l covers key
-  // (instruction*8 + l/8) and the logical chunk (l%8) ^ (key%8) of it.
-  const int dch = ((lane & 7) ^ ((lane >> 3) & 7)) * 16;
+  // DMA of stage st: 32 instructions of 1 KB (8 keys each), 4 per wave; lane l of instruction i
+  // covers key (i*8 + l/8) of the stage, whose 16 mod 16 is 8*(i%2) + l/8, and writes physical
+  // chunk l%8, i.e. logical chunk (l%8) ^ key_swz(key % 16).
+  const int dch0 = ((lane & 7) ^ key_swz(lane >> 3)) * 16;
+  const int dch1 = ((lane & 7) ^ key_swz(8 | (lane >> 3))) * 16;
   auto issue = [&](int st) {
     uint8_t* dst = kst[st % PF_NR];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int inst = wave * 4 + i;
       const int key = kbeg + st * PF_SK + inst * 8 + (lane >> 3);
-      const uint8_t* src = k + (int64_t)(k0 + min(key, n - 1)) * kDI + dch;
+      const uint8_t* src = k + (int64_t)(k0 + min(key, n - 1)) * kDI + ((i & 1) ? dch1 : dch0);
       __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
                                        (__attribute__((address_space(3))) void*)(dst + inst * 1024),
                                        16, 0, 0);
@@ -512,7 +527,7 @@ indexer_fp8_prefill_kernel(int B, const int32_t* __restrict__ cu_q, const int32_
 #pragma unroll
     for (int mm = 0; mm < 16; ++mm) wt[mm] = 0.5f * wr[4 * mm];
   }
-  const float ls = lin_half_scale[my_r] * (1.0f / float(1 << (4 * (c & 3))));
+  const int lsc = piece_exp[my_r] - 4 * (c & 3);
   const bool hi2 = (c & 2) != 0, hi1 = (c & 1) != 0;
   const bool row_ok = my_i < m;
   const int my_pos = n - m + my_i;
@@ -520,7 +535,7 @@ indexer_fp8_prefill_kernel(int B, const int32_t* __restrict__ cu_q, const int32_
   float* srow = scores + (int64_t)my_r * ld;
 
   // B operand of 16 keys starting at stage-local key kl: lane's key kl + c, chunks 2g, 2g+1
-  const int bx0 = ((2 * g) ^ (c & 7)) * 16, bx1 = ((2 * g + 1) ^ (c & 7)) * 16;
+  const int bx0 = ((2 * g) ^ key_swz(c)) * 16, bx1 = ((2 * g + 1) ^ key_swz(c)) * 16;
   auto load_b = [&](const uint8_t* buf, int kl) -> v8i {
     const uint8_t* rowp = buf + (kl + c) * kDI;
     const v4i lo = *reinterpret_cast<const v4i*>(rowp + bx0);
@@ -528,23 +543,39 @@ indexer_fp8_prefill_kernel(int B, const int32_t* __restrict__ cu_q, const int32_
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   };
 
+  // Vector memory operations complete in issue order, so the wait for stage st's DMA may leave
+  // the operations issued after it in flight: the score stores of a whole stage (16 per wave),
+  // the next stage's DMA (4), the stores of the stage after. `fast1`/`fast2`: stage st-1 / st-2
+  // ran the whole-stage path, whose 16 stores are certain (other stages count as 0).
+  bool fast1 = false, fast2 = false;
   for (int st = 0; st < nst; ++st) {
-    // stage st landed (and the previous stage's score stores completed); every wave is done
-    // with the buffer the next DMA refills
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+    const int after = (st == 0) ? 0 : 16 * fast2 + 16 * fast1 + 4 * (st + 1 < nst);
+    switch (after) {
+      case 36: asm volatile("s_waitcnt vmcnt(36)" ::: "memory"); break;
+      case 32: asm volatile("s_waitcnt vmcnt(32)" ::: "memory"); break;
+      case 20: asm volatile("s_waitcnt vmcnt(20)" ::: "memory"); break;
+      case 16: asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); break;
+      case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+      default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    }
+    // stage st landed in every wave's part; every wave is done with the buffer the next DMA
+    // refills (its reads were consumed by its matrix instructions)
+    __builtin_amdgcn_s_barrier();
     if (st + PF_NR - 1 < nst) issue(st + PF_NR - 1);
     const uint8_t* buf = kst[st % PF_NR];
     const int sbase = kbeg + st * PF_SK;
-    if (all_rows && sbase + PF_SK <= wkend) {
+    const bool fast = all_rows && sbase + PF_SK <= wkend;
+    fast2 = fast1;
+    fast1 = fast;
+    if (fast) {
       // whole stage for 4 valid rows: every score lands below wkend <= n <= ld (keys past a row's
       // own position fall in the part of the row the interface leaves unspecified)
-      stage_pipeline<PF_SK / 16>(buf + c * kDI, bx0, bx1, a, al, wt, ls, hi2, hi1,
+      stage_pipeline<PF_SK / 16>(buf + c * kDI, bx0, bx1, a, al, wt, lsc, hi2, hi1,
                                  srow + sbase + kofs);
     } else {
       const int nblk = min(PF_SK, wkend - sbase) > 0 ? (min(PF_SK, wkend - sbase) + 15) / 16 : 0;
       for (int blk = 0; blk < nblk; ++blk) {
-        const float acc = score_block_t(a, al, load_b(buf, blk * 16), wt, ls, hi2, hi1);
+        const float acc = score_block_t(a, al, load_b(buf, blk * 16), wt, lsc, hi2, hi1);
         asm volatile("" ::"v"(acc));
         const int s = sbase + blk * 16 + kofs;
         if (row_ok && s <= my_pos && s < wkend) srow[s] = acc;
@@ -571,14 +602,14 @@ hipError_t launch_indexer_fp8_prefill(const SeqInfo& s, const uint8_t* q, const 
                                       hipStream_t st) {
   if (s.T == 0 || s.max_n == 0) return hipSuccess;
   uint8_t* pieces = static_cast<uint8_t*>(ws);
-  float* half_scale = reinterpret_cast<float*>(pieces + (size_t)s.T * LIN_BYTES);
+  int32_t* piece_exp = reinterpret_cast<int32_t*>(pieces + (size_t)s.T * LIN_BYTES);
   hipLaunchKernelGGL(indexer_fp8_linear_kernel, dim3((s.T + 15) / 16), dim3(256), 0, st, s.T, q, w,
-                     pieces, half_scale);
+                     pieces, piece_exp);
   const int tiles = (s.max_m + PF_ROWS - 1) / PF_ROWS;
   const int kc = pick_chunk((int64_t)tiles * s.B, s.max_n, device_cu_count(), PF_SK);
   dim3 grid(tiles, (s.max_n + kc - 1) / kc, s.B);
   hipLaunchKernelGGL(indexer_fp8_prefill_kernel, grid, dim3(PF_W * 64), 0, st, s.B, s.cu_q, s.cu_k,
-                     q, k, w, pieces, half_scale, scores, ld, kc);
+                     q, k, w, pieces, piece_exp, scores, ld, kc);
   return hipGetLastError();
 }
 
