@@ -126,8 +126,9 @@ dsa_status_t dsa_topk(const dsa_seqs_t* seqs, const float* scores, int64_t ld_sc
  * (paper digest "Key claims", Fig. 2 and "Method": MLA in MQA mode, one latent row per key
  * shared by all query heads, attended only at the selected entries.)
  *
- *   dtype    DSA_BF16 with (H, d_qk, d_v) = (128, 576, 512) (matrix-core path), or DSA_F32 with
- *            1 <= H <= 128, 1 <= d_v <= d_qk <= 1024 (vector path)
+ *   dtype    DSA_BF16 with (H, d_qk, d_v) = (128, 576, 512) and max_seqlen_k <= 1864135 (byte
+ *            offsets within one sequence's latent rows fit 31 bits; matrix-core path), or DSA_F32
+ *            with 1 <= H <= 128, 1 <= d_v <= d_qk <= 1024, k <= 4096 (vector path)
  *   q        [T, H, d_qk] of dtype         queries already in the latent space
  *   kv       [Nk, d_qk] of dtype           latent cache (value = the first d_v dims)
  *   indices  [T, k] int32                  1 <= k <= 16384

@@ -19,12 +19,13 @@
 //     the S^T accumulator layout is used directly as the B operand, and V^T is read from LDS with
 //     the same permutation of the key index.
 // LDS layout of a gathered block (16-byte slots): chunk c (dims 8c..8c+7) of key s lives in slot
-//   (c / 8) * 512 + (s / 8) * 64 + (s % 8) * 8 + ((c % 8) ^ (s % 8)).
+//   (c / 8) * 512 + (s / 8) * 64 + (s % 8) * 8 + ((c % 8) ^ kv_swz(s % 16)).
 // One DMA instruction fills 64 consecutive slots = 8 chunks of 8 keys, i.e. 8 whole 128-byte
-// lines of the latent cache (fully coalesced). The XOR keeps the 32-key reads of one chunk (S^T)
-// and the transposing value reads (V^T) free of bank conflicts, and splits for every read into
-// loop-invariant lane bits plus compile-time bits, so each LDS read is one of a few per-lane base
-// registers plus an immediate offset.
+// lines of the latent cache (fully coalesced). kv_swz keeps both read patterns free of bank
+// conflicts whether the LDS serves 8 or 16 lanes of 16 bytes per cycle: the reads of one chunk of
+// 16 consecutive keys (S^T) and the transposing value reads (V^T, 8 bytes per lane, 4 keys x 4
+// quarter-chunks per 16 lanes). Every read splits into loop-invariant lane bits plus compile-time
+// bits, so each LDS read is one of a few per-lane base registers plus an immediate offset.
 #include "dsa_internal.h"
 #include "device_common.h"
 
@@ -139,22 +140,33 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// Bank swizzle of the 8 chunk positions of key s (s16 = s % 16): a GF(2)-linear map whose values
+// are distinct over any 8 consecutive keys and over the 8 even (odd) keys of 16, and which sends
+// keys s, s+1, s+2, s+3 (s % 4 == 0) to 4 different chunk pairs, with keys s and s+2 in different
+// chunk halves.
+__device__ __forceinline__ int kv_swz(int s16) {
+  const int b0 = (s16 >> 1) & 1, b1 = (s16 ^ (s16 >> 3)) & 1, b2 = ((s16 >> 1) ^ (s16 >> 2)) & 1;
+  return b0 | (b1 << 1) | (b2 << 2);
+}
+
 // Issue the gather of one block into `buf`. Wave w copies key groups R = 2w + u (u = 0, 1; keys
-// 8R .. 8R+7) for chunk groups G = 0..8. In each instruction lane l covers key 8R + l/8 and chunk
-// 8G + ((l % 8) ^ (l / 8)), which lands in slot G*512 + R*64 + l: the lane-linear LDS writes of the
-// DMA match the swizzled layout. row_u is the latent row of key 8(2w + u) + l/8.
-__device__ __forceinline__ void gather_block(uint8_t* buf, const uint8_t* __restrict__ kv,
-                                             int64_t row0, int64_t row1, int wave, int lane) {
-  const int sw = ((lane & 7) ^ (lane >> 3)) * 16;
+// 8R .. 8R+7) for chunk groups G = 0..8. In each instruction lane l covers key 8R + l/8 (key % 16
+// = 8u + l/8) and chunk 8G + ((l % 8) ^ kv_swz(8u + l/8)), which lands in slot G*512 + R*64 + l:
+// the lane-linear LDS writes of the DMA match the swizzled layout. row_u is the sequence-local
+// latent row of key 8(2w + u) + l/8; `seq` addresses the sequence's rows (n * 1152 bytes).
+// Buffer (not global) loads: the compiler then keeps exact LDS-read waits while they are in flight.
+__device__ __forceinline__ void gather_block(uint8_t* buf, __amdgpu_buffer_rsrc_t seq, int row0,
+                                             int row1, int wave, int lane) {
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    const uint8_t* src = kv + (u ? row1 : row0) * (MDQK * 2) + sw;
+    const int sw = ((lane & 7) ^ kv_swz(8 * u + (lane >> 3))) * 16;
+    const int voff = (u ? row1 : row0) * (MDQK * 2) + sw;
     const int R = 2 * wave + u;
 #pragma unroll
     for (int G = 0; G < MCH / 8; ++G)
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src + G * 128),
-                                       (__attribute__((address_space(3))) void*)(buf + (G * 512 + R * 64) * 16),
-                                       16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          seq, (__attribute__((address_space(3))) void*)(buf + (G * 512 + R * 64) * 16), 16,
+          voff + G * 128, 0, 0, 0);
   }
 }
 
@@ -187,11 +199,13 @@ __device__ __forceinline__ bool attend_half(const uint8_t* buf, int kbase, uint3
   const int g = lane >> 5, c32 = lane & 31;
   // S^T = K Q^T: M = 32 keys, N = 32 heads; lane holds head c32, keys 8(i/4) + 4g + (i%4).
   // chunk c = 2t + g of key s = kbase + c32: c/8 = t/4, c%8 = 2(t%4) + g, so the slot is
-  // (t/4)*512 + (s/8)*64 + (s%8)*8 + ((2(t%4) + g) ^ (s%8))
+  // (t/4)*512 + (s/8)*64 + (s%8)*8 + ((2(t%4) + g) ^ kv_swz(s%16)), s%16 = c32%16 (kbase is a
+  // multiple of 32)
   const uint8_t* kb_lane = buf + (((kbase + c32) >> 3) * 64 + (c32 & 7) * 8) * 16;
+  const int ksw = kv_swz(c32 & 15);
   int kx[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) kx[q] = ((2 * q + g) ^ (c32 & 7)) * 16;
+  for (int q = 0; q < 4; ++q) kx[q] = ((2 * q + g) ^ ksw) * 16;
   auto kop = [&](int t) -> bf16x8 {
     return *reinterpret_cast<const bf16x8*>(kb_lane + kx[t & 3] + (t >> 2) * 8192);
   };
@@ -236,19 +250,22 @@ __device__ __forceinline__ bool attend_half(const uint8_t* buf, int kbase, uint3
   // transposing reads: lane (4jj + q) of each 16-lane group points at value dims
   // v0 = 32vt + 16*(group & 1) + 4q .. +3 of key 16j + 8h + 4g + jj.
   // chunk c = 4vt + 2grp + q/2: c/8 = vt/2, c%8 = 4(vt%2) + 2grp + q/2; key s = kbase + 16j + 8h
-  // + 4g + jj: s/8 = kbase/8 + 2j + h, s%8 = 4g + jj. Slot (vt/2)*512 + (s/8)*64 + (s%8)*8 +
-  // ((c%8) ^ (s%8)), byte offset 8 * (q % 2) inside it.
+  // + 4g + jj: s/8 = kbase/8 + 2j + h, s%8 = 4g + jj, s%16 = 8h + 4g + jj. Slot (vt/2)*512 +
+  // (s/8)*64 + (s%8)*8 + ((c%8) ^ kv_swz(s%16)), byte offset 8 * (q % 2) inside it.
   const int grp = (lane >> 4) & 1, li = lane & 15;
   const int jj = li >> 2, q4 = li & 3;
   const uint8_t* vb_lane = buf + ((kbase >> 3) * 64 + (4 * g + jj) * 8) * 16 + (q4 & 1) * 8;
-  int vx[2];
+  int vx[2][2];   // [vt % 2][h]
 #pragma unroll
-  for (int p = 0; p < 2; ++p) vx[p] = ((4 * p + 2 * grp + (q4 >> 1)) ^ (4 * g + jj)) * 16;
+  for (int p = 0; p < 2; ++p)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      vx[p][h] = h * 1024 + ((4 * p + 2 * grp + (q4 >> 1)) ^ kv_swz(8 * h + 4 * g + jj)) * 16;
   auto vop = [&](int step) -> bf16x8 {
     const int j = step / (MDV / 32), vt = step % (MDV / 32);
-    const uint8_t* p = vb_lane + vx[vt & 1] + (vt >> 1) * 8192 + j * 2048;
-    const s16x4 lo = lds_read_tr16(p);
-    const s16x4 hi = lds_read_tr16(p + 1024);
+    const uint8_t* p = vb_lane + (vt >> 1) * 8192 + j * 2048;
+    const s16x4 lo = lds_read_tr16(p + vx[vt & 1][0]);
+    const s16x4 hi = lds_read_tr16(p + vx[vt & 1][1]);
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
   constexpr int NSTEP = 2 * (MDV / 32);
@@ -310,11 +327,16 @@ attn_bf16_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restr
     const int j = blk * MBLK + lane;
     return (blk < nblk && j < k) ? ir[j] : -1;
   };
-  // latent rows of keys 16w + l/8 and 16w + 8 + l/8 (see gather_block) and the block's valid mask
-  auto prep = [&](int sidx, int64_t& ra, int64_t& rb, uint64_t& vm) {
+  // the sequence's latent rows as a buffer (byte offsets fit 32 bits: n * 1152 < 2^31 is checked
+  // on the host); out-of-range offsets would read as zero
+  const __amdgpu_buffer_rsrc_t seq = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(kv + (int64_t)L.kofs * (MDQK * 2)), 0, L.n * (MDQK * 2), 0x00020000);
+  // sequence-local rows of keys 16w + l/8 and 16w + 8 + l/8 (see gather_block) and the block's
+  // valid mask
+  auto prep = [&](int sidx, int& ra, int& rb, uint64_t& vm) {
     const bool valid = sidx >= 0 && sidx < L.n;
     vm = __ballot(valid);
-    const int row = L.kofs + (valid ? sidx : 0);
+    const int row = valid ? sidx : 0;
     ra = __shfl(row, 16 * wave + (lane >> 3));
     rb = __shfl(row, 16 * wave + 8 + (lane >> 3));
   };
@@ -330,10 +352,10 @@ attn_bf16_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restr
     for (int vt = 0; vt < MDV / 32; ++vt) acc_o[vt] = (v16f){};
     st.m = st.seen;  // -inf on the first pass, the largest block max seen on a restart
     st.l = 0.f;
-    int64_t ra, rb;
+    int ra, rb;
     uint64_t vm_cur, vm_next;
     prep(load_idx(0), ra, rb, vm_cur);
-    if (vm_cur) gather_block(buf0, kv, ra, rb, wave, lane);
+    if (vm_cur) gather_block(buf0, seq, ra, rb, wave, lane);
     int idx_next = load_idx(1);
     bool restart = false;
     for (int blk = 0; blk < nblk; blk += 2) {
@@ -341,7 +363,7 @@ attn_bf16_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restr
       __syncthreads();
       if (blk > 0 && s_flag[(step - 1) & 1] == step - 1) { restart = true; break; }
       prep(idx_next, ra, rb, vm_next);
-      if (blk + 1 < nblk && vm_next) gather_block(buf1, kv, ra, rb, wave, lane);
+      if (blk + 1 < nblk && vm_next) gather_block(buf1, seq, ra, rb, wave, lane);
       idx_next = load_idx(blk + 2);
       if (vm_cur && attend_block(buf0, vm_cur, qreg, acc_o, st, sl2, lane)) s_flag[step & 1] = step;
       ++step;
@@ -352,7 +374,7 @@ attn_bf16_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restr
       __syncthreads();
       if (s_flag[(step - 1) & 1] == step - 1) { restart = true; break; }
       prep(idx_next, ra, rb, vm_next);
-      if (blk + 2 < nblk && vm_next) gather_block(buf0, kv, ra, rb, wave, lane);
+      if (blk + 2 < nblk && vm_next) gather_block(buf0, seq, ra, rb, wave, lane);
       idx_next = load_idx(blk + 3);
       if (vm_cur && attend_block(buf1, vm_cur, qreg, acc_o, st, sl2, lane)) s_flag[step & 1] = step;
       ++step;

@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <climits>
 #include <cstdarg>
 #include <cstdio>
 #include <mutex>
@@ -127,6 +128,9 @@ dsa_status_t check_attn(const dsa::SeqInfo& s, int32_t H, int32_t d_qk, int32_t 
     return fail(DSA_ERR_ALIGN, "attention tensors must be 16-byte aligned");
   if (dt == DSA_BF16 && !(H == 128 && d_qk == 576 && d_v == 512))
     return fail(DSA_ERR_UNSUPPORTED, "bf16 attention needs (H, d_qk, d_v) = (128, 576, 512)");
+  if (dt == DSA_BF16 && (int64_t)s.max_n * d_qk * 2 > INT32_MAX)
+    return fail(DSA_ERR_UNSUPPORTED, "bf16 attention needs max_seqlen_k * 1152 < 2^31 (got %d keys)",
+                s.max_n);
   if (dt == DSA_F32 && (H > 128 || d_qk > 1024 || k > 4096))
     return fail(DSA_ERR_UNSUPPORTED, "fp32 attention supports H <= 128, d_qk <= 1024, k <= 4096");
   return ok();
