@@ -156,9 +156,9 @@ __device__ __forceinline__ int kv_swz(int s16) {
 // latent row of key 8(2w + u) + l/8; `seq` addresses the sequence's rows (n * 1152 bytes).
 // Buffer (not global) loads: the compiler then keeps exact LDS-read waits while they are in flight.
 __device__ __forceinline__ void gather_block(uint8_t* buf, __amdgpu_buffer_rsrc_t seq, int row0,
-                                             int row1, int wave, int lane) {
+                                             int row1, int wave, int lane, int u0 = 0, int u1 = 2) {
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
+  for (int u = u0; u < u1; ++u) {
     const int sw = ((lane & 7) ^ kv_swz(8 * u + (lane >> 3))) * 16;
     const int voff = (u ? row1 : row0) * (MDQK * 2) + sw;
     const int R = 2 * wave + u;
@@ -195,7 +195,9 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const uint8_t* p) {
 // (which would cost registers the resident query block needs).
 __device__ __forceinline__ bool attend_half(const uint8_t* buf, int kbase, uint32_t vmask,
                                             const bf16x8 (&qreg)[MT], v16f (&acc_o)[MDV / 32],
-                                            SoftmaxState& st, float sl2, int lane) {
+                                            SoftmaxState& st, float sl2, int lane,
+                                            __amdgpu_buffer_rsrc_t gseq, uint8_t* gdst, int gvoff0,
+                                            int gvoff1) {
   const int g = lane >> 5, c32 = lane & 31;
   // S^T = K Q^T: M = 32 keys, N = 32 heads; lane holds head c32, keys 8(i/4) + 4g + (i%4).
   // chunk c = 2t + g of key s = kbase + c32: c/8 = t/4, c%8 = 2(t%4) + g, so the slot is
@@ -218,6 +220,12 @@ __device__ __forceinline__ bool attend_half(const uint8_t* buf, int kbase, uint3
     for (int t = 0; t < MT; ++t) {
       if (t + KRING - 1 < MT) ka[(t + KRING - 1) % KRING] = kop(t + KRING - 1);
       s = mfma_bf16_32x32x16(ka[t % KRING], qreg[t], s);
+      // gather load i = t/2 of the next block (key group 2*wave + i/9, chunk group i%9) every
+      // other matrix instruction
+      if ((t & 1) == 0 && gdst)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            gseq, (__attribute__((address_space(3))) void*)(gdst + ((t / 2) / 9) * 1024 + ((t / 2) % 9) * 8192),
+            16, (t / 2) / 9 ? gvoff1 : gvoff0, ((t / 2) % 9) * 128, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -285,12 +293,27 @@ __device__ __forceinline__ bool attend_half(const uint8_t* buf, int kbase, uint3
 // One gathered block of 64 keys, processed as two halves. Returns true if the row must restart.
 __device__ __forceinline__ bool attend_block(const uint8_t* buf, uint64_t vmask,
                                              const bf16x8 (&qreg)[MT], v16f (&acc_o)[MDV / 32],
-                                             SoftmaxState& st, float sl2, int lane) {
+                                             SoftmaxState& st, float sl2, int lane,
+                                             uint8_t* gbuf, __amdgpu_buffer_rsrc_t seq, int ra, int rb,
+                                             bool gon, int wave) {
+  // the next block's gather goes out during this block's first computed half, one load every
+  // other matrix instruction
+  const __amdgpu_buffer_rsrc_t gseq = seq;
+  uint8_t* const gdst = gbuf + (2 * wave) * 1024;
+  const int gvoff0 = ra * (MDQK * 2) + ((lane & 7) ^ kv_swz(lane >> 3)) * 16;
+  const int gvoff1 = rb * (MDQK * 2) + ((lane & 7) ^ kv_swz(8 | (lane >> 3))) * 16;
+  bool pending = true;
 #pragma unroll 1
   for (int h = 0; h < 2; ++h) {
     const uint32_t m32 = (uint32_t)(vmask >> (32 * h));
-    if (m32 && attend_half(buf, 32 * h, m32, qreg, acc_o, st, sl2, lane)) return true;
+    if (m32) {
+      const bool rs = attend_half(buf, 32 * h, m32, qreg, acc_o, st, sl2, lane, gseq,
+                                  pending && gon ? gdst : nullptr, gvoff0, gvoff1);
+      pending = false;
+      if (rs) return true;
+    }
   }
+  if (pending && gon) gather_block(gbuf, seq, ra, rb, wave, lane);   // no half was computed
   return false;
 }
 
@@ -304,7 +327,8 @@ attn_bf16_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restr
   // restart requests: slot (step & 1) holds the id of the last step that asked for one
   __shared__ int s_flag[2];
   const int r = blockIdx.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int g = lane >> 5, c32 = lane & 31;
   const RowLoc L = locate_row(cu_q, cu_k, B, r);
   const int32_t* ir = idx + (int64_t)r * k;
@@ -363,9 +387,10 @@ attn_bf16_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restr
       __syncthreads();
       if (blk > 0 && s_flag[(step - 1) & 1] == step - 1) { restart = true; break; }
       prep(idx_next, ra, rb, vm_next);
-      if (blk + 1 < nblk && vm_next) gather_block(buf1, seq, ra, rb, wave, lane);
+      const bool gon1 = blk + 1 < nblk && vm_next;
       idx_next = load_idx(blk + 2);
-      if (vm_cur && attend_block(buf0, vm_cur, qreg, acc_o, st, sl2, lane)) s_flag[step & 1] = step;
+      // (a block without a valid key skips both halves but still issues the second loads)
+      if (attend_block(buf0, vm_cur, qreg, acc_o, st, sl2, lane, buf1, seq, ra, rb, gon1, wave)) s_flag[step & 1] = step;
       ++step;
       vm_cur = vm_next;
       if (blk + 1 >= nblk) break;
@@ -374,9 +399,10 @@ attn_bf16_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restr
       __syncthreads();
       if (s_flag[(step - 1) & 1] == step - 1) { restart = true; break; }
       prep(idx_next, ra, rb, vm_next);
-      if (blk + 2 < nblk && vm_next) gather_block(buf0, seq, ra, rb, wave, lane);
+      const bool gon0 = blk + 2 < nblk && vm_next;
       idx_next = load_idx(blk + 3);
-      if (vm_cur && attend_block(buf1, vm_cur, qreg, acc_o, st, sl2, lane)) s_flag[step & 1] = step;
+      // (a block without a valid key skips both halves but still issues the second loads)
+      if (attend_block(buf1, vm_cur, qreg, acc_o, st, sl2, lane, buf0, seq, ra, rb, gon0, wave)) s_flag[step & 1] = step;
       ++step;
       vm_cur = vm_next;
     }
