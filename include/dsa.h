@@ -132,6 +132,7 @@ dsa_status_t dsa_topk(const dsa_seqs_t* seqs, const float* scores, int64_t ld_sc
  *   q        [T, H, d_qk] of dtype         queries already in the latent space
  *   kv       [Nk, d_qk] of dtype           latent cache (value = the first d_v dims)
  *   indices  [T, k] int32                  1 <= k <= 16384
+ *   softmax_scale  positive and finite (DSA_ERR_SHAPE otherwise)
  *   out      [T, H, d_v] of dtype (output; bf16 rounded to nearest even)
  *   lse      [T, H] fp32 (output) or NULL
  *   ws       device workspace of at least dsa_sparse_mla_attn_workspace_size(...) bytes

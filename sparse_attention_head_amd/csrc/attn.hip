@@ -170,15 +170,15 @@ __device__ __forceinline__ void gather_block(uint8_t* buf, __amdgpu_buffer_rsrc_
   }
 }
 
+// Weights are taken against a reference fixed for a whole pass over the row instead of a running
+// maximum, so the output accumulators are never rescaled. A lane's weights of one half may sum to
+// at most 2^60 (which keeps P, the sums and the output finite in fp32); beyond that the row is
+// restarted with a larger reference.
 struct SoftmaxState {
-  float m;     // reference max (log2 domain) used in the exponent; fixed during a pass
-  float seen;  // largest block max seen so far in this row (log2 domain)
+  float m;     // reference (log2 domain) used in the exponent; fixed during a pass
+  float seen;  // largest half maximum recorded in this row (log2 domain): reference of a restart
   float l;     // running sum of 2^(z - m) over this lane's keys
 };
-
-// Exponents above the reference max are allowed up to this many powers of two before the row
-// is restarted with a larger reference (2^64 keeps P, the sums and the output finite in fp32).
-constexpr float kHeadroom = 64.f;
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
@@ -190,7 +190,7 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const uint8_t* p) {
 
 // One half block (32 keys starting at kbase inside the LDS block): logits, softmax weights,
 // value accumulation. Returns true (uniform over the wave) when some head's logits exceed its
-// reference max by more than kHeadroom; the caller then restarts the row. LDS operands are
+// reference by too much (see SoftmaxState); the caller then restarts the row. LDS operands are
 // prefetched several MFMAs ahead; scheduling barriers keep the compiler from hoisting further
 // (which would cost registers the resident query block needs).
 __device__ __forceinline__ bool attend_half(const uint8_t* buf, int kbase, uint32_t vmask,
@@ -203,13 +203,15 @@ __device__ __forceinline__ bool attend_half(const uint8_t* buf, int kbase, uint3
   // chunk c = 2t + g of key s = kbase + c32: c/8 = t/4, c%8 = 2(t%4) + g, so the slot is
   // (t/4)*512 + (s/8)*64 + (s%8)*8 + ((2(t%4) + g) ^ kv_swz(s%16)), s%16 = c32%16 (kbase is a
   // multiple of 32)
+  // 4 per-lane base addresses (chunk position within the key row for t % 4); every read is one of
+  // them plus an immediate offset
   const uint8_t* kb_lane = buf + (((kbase + c32) >> 3) * 64 + (c32 & 7) * 8) * 16;
   const int ksw = kv_swz(c32 & 15);
-  int kx[4];
+  const uint8_t* kb[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) kx[q] = ((2 * q + g) ^ ksw) * 16;
+  for (int q = 0; q < 4; ++q) kb[q] = kb_lane + ((2 * q + g) ^ ksw) * 16;
   auto kop = [&](int t) -> bf16x8 {
-    return *reinterpret_cast<const bf16x8*>(kb_lane + kx[t & 3] + (t >> 2) * 8192);
+    return *reinterpret_cast<const bf16x8*>(kb[t & 3] + (t >> 2) * 8192);
   };
   v16f s = {};
   {
@@ -229,28 +231,41 @@ __device__ __forceinline__ bool attend_half(const uint8_t* buf, int kbase, uint3
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  float bmax = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) s[i] *= sl2;
-  if (vmask != 0xFFFFFFFFu) {  // uniform: only partly valid halves pay for the masking
-    const uint32_t mlane = vmask >> (4 * g);  // bit 8(i/4) + (i%4) <-> this lane's key i
+  // Softmax weights against the fixed reference st.m (log2 domain): p = 2^(sl2 * s - m). The
+  // first half with a valid key in a pass sets the reference to its maximum; no maximum is taken
+  // after that. A half whose weights in some lane sum past 2^60 (or overflow) asks for a restart
+  // and records its own maximum, which the restarted pass takes as the reference.
+  const bool partial = vmask != 0xFFFFFFFFu;   // uniform: only partly valid halves pay for masking
+  const uint32_t mlane = vmask >> (4 * g);     // bit 8(i/4) + (i%4) <-> this lane's key i
+  auto key_ok = [&](int i) { return ((mlane >> (8 * (i >> 2) + (i & 3))) & 1u) != 0; };
+  auto half_max = [&]() -> float {   // masked entries are -inf by then or excluded here
+    float bm = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 16; ++i)
-      if (!((mlane >> (8 * (i >> 2) + (i & 3))) & 1u)) s[i] = -INFINITY;
+      if (!partial || key_ok(i)) bm = fmaxf(bm, s[i] * sl2);
+    return fmaxf(bm, __shfl_xor(bm, 32));   // both lanes of a head
+  };
+  if (st.m == -INFINITY) {
+    st.m = half_max();
+    st.seen = fmaxf(st.seen, st.m);
   }
+  if (partial) {   // masked keys: exponent -inf (the scale is positive), weight 0
 #pragma unroll
-  for (int i = 0; i < 16; ++i) bmax = fmaxf(bmax, s[i]);
-  bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
-  if (st.m == -INFINITY) st.m = bmax;  // first non-empty block of the pass
-  st.seen = fmaxf(st.seen, bmax);
-  if (__any(bmax > st.m + kHeadroom)) return true;
+    for (int i = 0; i < 16; ++i)
+      if (!key_ok(i)) s[i] = -INFINITY;
+  }
   bf16x8 pb[2];
   float lsum = 0.f;
+  const float nm = -st.m;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const float p = __builtin_amdgcn_exp2f(s[i] - st.m);
+    const float p = __builtin_amdgcn_exp2f(fmaf(s[i], sl2, nm));
     lsum += p;
     pb[i >> 3][i & 7] = (__bf16)p;
+  }
+  if (__any(!(lsum <= 0x1p60f))) {
+    st.seen = fmaxf(st.seen, half_max());
+    return true;
   }
   st.l += lsum;
   // O^T[v, head] += V^T[v, keys] P^T[keys, head]. K step j covers keys 16j + 8h + 4g + jj
@@ -263,17 +278,18 @@ __device__ __forceinline__ bool attend_half(const uint8_t* buf, int kbase, uint3
   const int grp = (lane >> 4) & 1, li = lane & 15;
   const int jj = li >> 2, q4 = li & 3;
   const uint8_t* vb_lane = buf + ((kbase >> 3) * 64 + (4 * g + jj) * 8) * 16 + (q4 & 1) * 8;
-  int vx[2][2];   // [vt % 2][h]
+  // 4 per-lane base addresses ([vt % 2][h]); every read is one of them plus an immediate offset
+  const uint8_t* vb[2][2];
 #pragma unroll
   for (int p = 0; p < 2; ++p)
 #pragma unroll
     for (int h = 0; h < 2; ++h)
-      vx[p][h] = h * 1024 + ((4 * p + 2 * grp + (q4 >> 1)) ^ kv_swz(8 * h + 4 * g + jj)) * 16;
+      vb[p][h] = vb_lane + h * 1024 + ((4 * p + 2 * grp + (q4 >> 1)) ^ kv_swz(8 * h + 4 * g + jj)) * 16;
   auto vop = [&](int step) -> bf16x8 {
     const int j = step / (MDV / 32), vt = step % (MDV / 32);
-    const uint8_t* p = vb_lane + (vt >> 1) * 8192 + j * 2048;
-    const s16x4 lo = lds_read_tr16(p + vx[vt & 1][0]);
-    const s16x4 hi = lds_read_tr16(p + vx[vt & 1][1]);
+    const int off = (vt >> 1) * 8192 + j * 2048;
+    const s16x4 lo = lds_read_tr16(vb[vt & 1][0] + off);
+    const s16x4 hi = lds_read_tr16(vb[vt & 1][1] + off);
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
   constexpr int NSTEP = 2 * (MDV / 32);
@@ -374,7 +390,7 @@ attn_bf16_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restr
   for (int pass = 0;; ++pass) {
 #pragma unroll
     for (int vt = 0; vt < MDV / 32; ++vt) acc_o[vt] = (v16f){};
-    st.m = st.seen;  // -inf on the first pass, the largest block max seen on a restart
+    st.m = st.seen;  // -inf on the first pass, the largest recorded half maximum on a restart
     st.l = 0.f;
     int ra, rb;
     uint64_t vm_cur, vm_next;

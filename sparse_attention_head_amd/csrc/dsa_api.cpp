@@ -297,6 +297,8 @@ dsa_status_t dsa_sparse_mla_attn(const dsa_seqs_t* seqs, int32_t H, int32_t d_qk
   if (s.B == 0) return ok();
   st = check_attn(s, H, d_qk, d_v, dtype, q, kv, indices, k, out, lse);
   if (st != DSA_OK) return st;
+  if (!(softmax_scale > 0.f) || softmax_scale > 3.0e38f)
+    return fail(DSA_ERR_SHAPE, "softmax_scale must be positive and finite (got %g)", softmax_scale);
   const size_t need = dsa::attn_workspace_bytes(s, H, d_qk, d_v, k, dtype == DSA_BF16);
   if (need > 0 && (!ws || ws_bytes < need))
     return fail(DSA_ERR_WORKSPACE, "attention workspace needs %zu bytes, got %zu", need, ws_bytes);
@@ -326,6 +328,8 @@ dsa_status_t dsa_forward(const dsa_seqs_t* seqs, const dsa_forward_args_t* a, vo
   st = check_attn(s, a->H, a->d_qk, a->d_v, a->dtype, a->q, a->kv, a->indices_out, a->k, a->out,
                   a->lse, a->indices_out == nullptr);
   if (st != DSA_OK) return st;
+  if (!(a->softmax_scale > 0.f) || a->softmax_scale > 3.0e38f)
+    return fail(DSA_ERR_SHAPE, "softmax_scale must be positive and finite (got %g)", a->softmax_scale);
   if (p.total > 0 && (!ws || ws_bytes < p.total))
     return fail(DSA_ERR_WORKSPACE, "forward workspace needs %zu bytes, got %zu", p.total, ws_bytes);
   if (ws && (reinterpret_cast<uintptr_t>(ws) % kAlign) != 0)

@@ -144,6 +144,8 @@ def test_topk_and_attention_validation(dsa):
     assert A(sq.ref, 8, 80, 64, 0, p, None, p, 64, 1.0, p, p, None, 0, None) == dsa.DSA_ERR_NULL
     _, pm = buf(64, misalign=8)
     assert A(sq.ref, 8, 80, 64, 0, p, p, p, 64, 1.0, pm, p, None, 0, None) == dsa.DSA_ERR_ALIGN
+    for bad_scale in (0.0, -0.5, float("inf"), float("nan")):
+        assert A(sq.ref, 8, 80, 64, 0, p, p, p, 64, bad_scale, p, p, None, 0, None) == dsa.DSA_ERR_SHAPE
 
 
 def test_forward_validation_and_workspace(dsa):
