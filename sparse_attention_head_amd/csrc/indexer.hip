@@ -261,31 +261,28 @@ __device__ __forceinline__ float decode_e4m3(uint32_t c) {
 
 constexpr int LIN_BYTES = 4 * kDI;   // pieces of one row: [4][128] codes
 
-// One thread per (row, 8 dims): u = sum_j w_j qI_j, the row's exponent e and the 4 pieces.
+// One wave per row, two dims per lane: u = sum_j w_j qI_j, the row's exponent e and the 4 pieces.
 // pieces [T][4][128] codes; piece_exp [T] = 126 + e, the E8M0 code of 2^(e-1) (the matrix
 // instruction applies 2^(e-1) * 16^-p to piece p through its per-column scale operand).
 __global__ void __launch_bounds__(256)
 indexer_fp8_linear_kernel(int T, const uint8_t* __restrict__ q, const float* __restrict__ w,
                           uint8_t* __restrict__ pieces, int32_t* __restrict__ piece_exp) {
-  const int r = min(blockIdx.x * 16 + (threadIdx.x >> 4), T - 1);
-  const int d0 = (threadIdx.x & 15) * 8;
-  const uint8_t* qr = q + (int64_t)r * (kHI * kDI) + d0;
-  const float* wr = w + (int64_t)r * kHI;
-  float u[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const int r0 = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
+  if (r0 >= T) return;   // whole wave
+  const int lane = threadIdx.x & 63;
+  const uint8_t* qr = q + (int64_t)r0 * (kHI * kDI) + 2 * lane;
+  const float* wr = w + (int64_t)r0 * kHI;
+  float u0 = 0.f, u1 = 0.f;
+#pragma unroll 16
   for (int j = 0; j < kHI; ++j) {
-    const uint2 c = *reinterpret_cast<const uint2*>(qr + j * kDI);
+    const uint32_t c = *reinterpret_cast<const uint16_t*>(qr + j * kDI);
     const float wj = wr[j];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      u[i] = fmaf(wj, decode_e4m3(c.x >> (8 * i)), u[i]);
-      u[4 + i] = fmaf(wj, decode_e4m3(c.y >> (8 * i)), u[4 + i]);
-    }
+    u0 = fmaf(wj, decode_e4m3(c), u0);
+    u1 = fmaf(wj, decode_e4m3(c >> 8), u1);
   }
-  float mx = 0.f;
+  float mx = fmaxf(fabsf(u0), fabsf(u1));
 #pragma unroll
-  for (int i = 0; i < 8; ++i) mx = fmaxf(mx, fabsf(u[i]));
-#pragma unroll
-  for (int o = 8; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 16));
+  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
   int ex = 0;
   if (mx > 0.f) {
     frexpf(mx, &ex);   // mx = f * 2^ex, f in [0.5, 1)
@@ -294,24 +291,16 @@ indexer_fp8_linear_kernel(int T, const uint8_t* __restrict__ q, const float* __r
     // accounted for: the remainder stays below 2^-22 * 2^ex)
     ex = max(ex - 8, -112);
   }
-  uint32_t code[4][2] = {{0u, 0u}, {0u, 0u}, {0u, 0u}, {0u, 0u}};
+  float rem0 = ldexpf(u0, -ex), rem1 = ldexpf(u1, -ex);
+  uint16_t* out = reinterpret_cast<uint16_t*>(pieces + (int64_t)r0 * LIN_BYTES) + lane;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    float rem = ldexpf(u[i], -ex);
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const float v = round_e4m3(rem);
-      code[p][i >> 2] |= encode_e4m3(v) << (8 * (i & 3));
-      rem = (rem - v) * 16.f;
-    }
+  for (int p = 0; p < 4; ++p) {
+    const float v0 = round_e4m3(rem0), v1 = round_e4m3(rem1);
+    out[p * (kDI / 2)] = (uint16_t)(encode_e4m3(v0) | (encode_e4m3(v1) << 8));
+    rem0 = (rem0 - v0) * 16.f;
+    rem1 = (rem1 - v1) * 16.f;
   }
-  if (blockIdx.x * 16 + (threadIdx.x >> 4) < T) {
-#pragma unroll
-    for (int p = 0; p < 4; ++p)
-      *reinterpret_cast<uint2*>(pieces + (int64_t)r * LIN_BYTES + p * kDI + d0) =
-          make_uint2(code[p][0], code[p][1]);
-    if (d0 == 0) piece_exp[r] = 126 + ex;
-  }
+  if (lane == 0) piece_exp[r0] = 126 + ex;
 }
 
 // Scores of 16 keys against the wave's 4 rows. The keys are the A operand (M index = key) and the
@@ -603,7 +592,7 @@ hipError_t launch_indexer_fp8_prefill(const SeqInfo& s, const uint8_t* q, const 
   if (s.T == 0 || s.max_n == 0) return hipSuccess;
   uint8_t* pieces = static_cast<uint8_t*>(ws);
   int32_t* piece_exp = reinterpret_cast<int32_t*>(pieces + (size_t)s.T * LIN_BYTES);
-  hipLaunchKernelGGL(indexer_fp8_linear_kernel, dim3((s.T + 15) / 16), dim3(256), 0, st, s.T, q, w,
+  hipLaunchKernelGGL(indexer_fp8_linear_kernel, dim3((s.T + 3) / 4), dim3(256), 0, st, s.T, q, w,
                      pieces, piece_exp);
   const int tiles = (s.max_m + PF_ROWS - 1) / PF_ROWS;
   const int kc = pick_chunk((int64_t)tiles * s.B, s.max_n, device_cu_count(), PF_SK);

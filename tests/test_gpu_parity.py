@@ -138,6 +138,35 @@ def test_dense_special_case_bf16(gpu):
     check_rows(wl, x, res, range(wl.T), "normal", DELTA_FP8_MFMA)
 
 
+def test_indexer_weight_extremes(gpu):
+    """Rows whose head weights span the fp32 range (huge, tiny, zero, all negative, a single
+    nonzero head): the per-row scaling of the FP8 prefill path's linear term must hold the error
+    bound on every row."""
+    wl = dg.custom(name="wext", seqlens_q=[40], seqlens_k=[300], H_I=64, d_I=128, k=64, H=128,
+                   d_qk=576, d_v=512, idx_dtype="fp8", attn_dtype="bf16", wid=32)
+    x = dg.gen_inputs(wl, "normal", seed=5)
+    w = x["w"].copy()
+    w[0] *= np.float32(2.0 ** 40)
+    w[1] *= np.float32(2.0 ** -60)
+    w[2] = 0.0
+    w[3] = -np.abs(w[3])
+    w[4] = 0.0
+    w[4, 17] = np.float32(1e-3)
+    w[5] *= np.float32(2.0 ** -110)
+    w[6] = np.abs(w[6])
+    x["w"] = w
+    res = run_all(gpu, wl, x)
+    sq = Seqs(wl.cu_seqlens_q, wl.cu_seqlens_k)
+    for r in range(wl.T):
+        _, pos, _, _ = sq.locate(r)
+        ref = oracle.indexer_scores_row(sq, x["qI"], x["kI"], x["w"], r)
+        got = res["scores"][r, :pos + 1].astype(np.float64)
+        eps = score_bound_row(sq, x["qI"], x["kI"], x["w"], r, DELTA_FP8_MFMA)
+        assert np.all(np.abs(got - ref) <= eps), f"row {r}: worst {np.max(np.abs(got - ref) - eps)}"
+        if r == 2:
+            assert np.all(got == 0.0)
+
+
 def test_attention_edge_indices(gpu):
     """-1 and out-of-range indices are skipped, repeats count twice, an empty row gives 0 / -inf."""
     wl = dg.custom(name="edge", seqlens_q=[4], seqlens_k=[50], H=128, d_qk=576, d_v=512,
