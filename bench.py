@@ -30,6 +30,23 @@ PEAK_FP8_TFLOPS = 5000.0
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "indexer_fp8_chunk128k_hbm_traffic.md")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the indexer prefill kernel from the committed counter summary, or
+    None when the kernel source has changed since those counters were taken."""
+    import hashlib
+    try:
+        line = [l for l in open(TRAFFIC_RECORD) if l.startswith("record: ")][-1]
+        rec = json.loads(line[len("record: "):])
+        src = open(os.path.join(ROOT, rec["kernel_source"]), "rb").read()
+        if hashlib.sha256(src).hexdigest()[:16] != rec["source_sha256_16"]:
+            return None
+        return float(rec["bytes_per_launch"])
+    except (OSError, IndexError, KeyError, ValueError):
+        return None
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -182,7 +199,8 @@ def main():
     )
     if prefill:
         roof = dict(kernel="indexer_fp8", bound="mfma", achieved=idx_tflops, peak=PEAK_FP8_TFLOPS,
-                    unit="TFLOP/s", frac=idx_tflops / PEAK_FP8_TFLOPS, traffic=None)
+                    unit="TFLOP/s", frac=idx_tflops / PEAK_FP8_TFLOPS,
+                    traffic=measured_traffic() if wl.name == "chunk128k" else None)
     else:
         gbs = alg["decode_bytes"] / (tm["fused_ms"] / 1e3) / 1e9
         roof = dict(kernel="fused_decode", bound="hbm", achieved=gbs, peak=PEAK_HBM_GBS, unit="GB/s",
