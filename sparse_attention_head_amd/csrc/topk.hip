@@ -27,139 +27,6 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
   return (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
 }
 
-__global__ void __launch_bounds__(TK_THREADS)
-topk_row_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
-                const float* __restrict__ scores, int64_t ld, int k, int32_t* __restrict__ idx) {
-  __shared__ uint32_t hist[2048];
-  __shared__ uint32_t xch[2][TK_WAVES][2];
-  __shared__ uint32_t s_digit, s_above;
-
-  const int r = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const RowLoc L = locate_row(cu_q, cu_k, B, r);
-  const int n = L.pos + 1;
-  int32_t* out = idx + (int64_t)r * k;
-  const float* row = scores + (int64_t)r * ld;
-
-  if (n <= k) {  // every candidate is selected
-    for (int i = tid; i < k; i += TK_THREADS) out[i] = i < n ? i : -1;
-    return;
-  }
-
-  uint32_t prefix = 0, pmask = 0;
-  uint32_t need = (uint32_t)k;  // how many of the keys matching `prefix` still go in
-  const int n4 = n & ~3;
-#pragma unroll 1
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-    const int nb = pass == 2 ? 1024 : 2048;
-    for (int i = tid; i < nb; i += TK_THREADS) hist[i] = 0;
-    __syncthreads();
-    for (int i = tid * 4; i < n4; i += TK_THREADS * 4) {
-      const float4 v = *reinterpret_cast<const float4*>(row + i);
-      const float e[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t u = float_to_ordered(e[j]);
-        if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & (nb - 1)], 1u);
-      }
-    }
-    for (int i = n4 + tid; i < n; i += TK_THREADS) {
-      const uint32_t u = float_to_ordered(row[i]);
-      if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & (nb - 1)], 1u);
-    }
-    __syncthreads();
-    if (wave == 0) {
-      // suffix sums over the bins (from the largest digit down) to find the bin of the
-      // need-th largest key among those matching the prefix
-      const int per = nb / 64;
-      uint32_t sum = 0;
-      for (int j = 0; j < per; ++j) sum += hist[lane * per + j];
-      uint32_t suf = sum;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t t = __shfl_down(suf, off);
-        if (lane + off < 64) suf += t;
-      }
-      const uint32_t above_lane = suf - sum;  // keys in bins of higher lanes
-      if (suf >= need && above_lane < need) {
-        uint32_t above = above_lane;
-        for (int j = per - 1; j >= 0; --j) {
-          const uint32_t h = hist[lane * per + j];
-          if (above + h >= need) {
-            s_digit = (uint32_t)(lane * per + j);
-            s_above = above;
-            break;
-          }
-          above += h;
-        }
-      }
-    }
-    __syncthreads();
-    prefix |= s_digit << shift;
-    pmask |= (uint32_t)(nb - 1) << shift;
-    need -= s_above;
-  }
-  const uint32_t T = prefix;  // the k-th largest key; `need` >= 1 keys equal to T are taken
-
-  // ordered compaction: selected before i = (# keys > T before i) + min(# keys == T before i, need)
-  uint32_t run_gt = 0, run_eq = 0;
-  for (int base = 0, it = 0; base < n; base += TK_THREADS, ++it) {
-    const int i = base + tid;
-    const uint32_t u = i < n ? float_to_ordered(row[i]) : 0u;
-    const bool gt = i < n && u > T;
-    const bool eq = i < n && u == T;
-    const uint64_t bgt = __ballot(gt), beq = __ballot(eq);
-    const int par = it & 1;
-    if (lane == 0) {
-      xch[par][wave][0] = (uint32_t)__popcll(bgt);
-      xch[par][wave][1] = (uint32_t)__popcll(beq);
-    }
-    __syncthreads();
-    uint32_t gt_before = run_gt + lanes_below(bgt), eq_before = run_eq + lanes_below(beq);
-    uint32_t tot_gt = 0, tot_eq = 0;
-    for (int v = 0; v < TK_WAVES; ++v) {
-      const uint32_t a = xch[par][v][0], b2 = xch[par][v][1];
-      if (v < wave) { gt_before += a; eq_before += b2; }
-      tot_gt += a;
-      tot_eq += b2;
-    }
-    const uint32_t at = gt_before + min(eq_before, need);
-    if ((gt || (eq && eq_before < need)) && at < (uint32_t)k) out[at] = i;
-    run_gt += tot_gt;
-    run_eq += tot_eq;
-    if (run_gt + min(run_eq, need) >= (uint32_t)k) break;  // uniform: all k written
-  }
-}
-
-// ------------------------------------------------------------------------------------------
-// Register-resident variant for rows of up to 4096 * NT candidates. The row is read once, as
-// float4: in tile j (positions 4096j .. 4096j + 4095) thread t holds positions 4096j + 4t + c,
-// c = 0..3, and keeps only the upper 16 bits of their keys, two per register. Digits 1 and 2 of
-// the threshold (key bits 31..21 and 20..16) come from registers; digits 3 and 4 (bits 15..8 and
-// 7..0) only concern keys whose upper half equals the threshold's, and those few are re-read from
-// memory. The ordered compaction counts, per lane, the keys above / equal to the threshold, scans
-// the counts across the wave, stores one total per (tile, wave), turns those totals into offsets
-// with one block-wide exclusive scan in (tile, wave) order -- which is position order -- and
-// writes every selected position at its offset.
-
-__device__ __forceinline__ uint32_t block_excl_scan2(uint32_t a, uint32_t b, uint32_t* sw,
-                                                     uint32_t& excl_b) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t xa = a, xb = b;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t ta = __shfl_up(xa, off), tb = __shfl_up(xb, off);
-    if (lane >= off) { xa += ta; xb += tb; }
-  }
-  if (lane == 63) { sw[2 * wave] = xa; sw[2 * wave + 1] = xb; }
-  __syncthreads();
-  uint32_t ba = 0, bb = 0;
-  for (int w = 0; w < wave; ++w) { ba += sw[2 * w]; bb += sw[2 * w + 1]; }
-  excl_b = bb + xb - b;
-  return ba + xa - a;
-}
-
 // Finds the bin holding the need-th largest key among the counted ones (suffix sums from the
 // top bin down). Called by all threads; wave 0 does the work.
 __device__ __forceinline__ void select_bin(const uint32_t* hist, int nb, uint32_t need,
@@ -194,6 +61,124 @@ __device__ __forceinline__ void select_bin(const uint32_t* hist, int nb, uint32_
     }
   }
   __syncthreads();
+}
+
+// Exact selection for one row straight from global memory with NTH threads: three histogram
+// passes (key bits 31..21, 20..10, 9..0) find the k-th largest key T and how many keys equal to T
+// are taken (`need`); then an ordered compaction in position order keeps every key > T and the
+// first `need` keys == T. n > k. hist: 2048 words, xch: [2][NTH/64][2].
+template <int NTH>
+__device__ void topk_row_exact(const float* __restrict__ row, int n, int k, int32_t* __restrict__ out,
+                               uint32_t* hist, uint32_t (*xch)[NTH / 64][2], uint32_t* s_digit,
+                               uint32_t* s_above) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t prefix = 0, pmask = 0;
+  uint32_t need = (uint32_t)k;  // how many of the keys matching `prefix` still go in
+  const int n4 = n & ~3;
+#pragma unroll 1
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+    const int nb = pass == 2 ? 1024 : 2048;
+    for (int i = tid; i < nb; i += NTH) hist[i] = 0;
+    __syncthreads();
+    for (int i = tid * 4; i < n4; i += NTH * 4) {
+      const float4 v = *reinterpret_cast<const float4*>(row + i);
+      const float e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t u = float_to_ordered(e[j]);
+        if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & (nb - 1)], 1u);
+      }
+    }
+    for (int i = n4 + tid; i < n; i += NTH) {
+      const uint32_t u = float_to_ordered(row[i]);
+      if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & (nb - 1)], 1u);
+    }
+    __syncthreads();
+    select_bin(hist, nb, need, s_digit, s_above);
+    prefix |= *s_digit << shift;
+    pmask |= (uint32_t)(nb - 1) << shift;
+    need -= *s_above;
+  }
+  const uint32_t T = prefix;  // the k-th largest key; `need` >= 1 keys equal to T are taken
+
+  // ordered compaction: selected before i = (# keys > T before i) + min(# keys == T before i, need)
+  uint32_t run_gt = 0, run_eq = 0;
+  for (int base = 0, it = 0; base < n; base += NTH, ++it) {
+    const int i = base + tid;
+    const uint32_t u = i < n ? float_to_ordered(row[i]) : 0u;
+    const bool gt = i < n && u > T;
+    const bool eq = i < n && u == T;
+    const uint64_t bgt = __ballot(gt), beq = __ballot(eq);
+    const int par = it & 1;
+    if (lane == 0) {
+      xch[par][wave][0] = (uint32_t)__popcll(bgt);
+      xch[par][wave][1] = (uint32_t)__popcll(beq);
+    }
+    __syncthreads();
+    uint32_t gt_before = run_gt + lanes_below(bgt), eq_before = run_eq + lanes_below(beq);
+    uint32_t tot_gt = 0, tot_eq = 0;
+    for (int v = 0; v < NTH / 64; ++v) {
+      const uint32_t a = xch[par][v][0], b2 = xch[par][v][1];
+      if (v < wave) { gt_before += a; eq_before += b2; }
+      tot_gt += a;
+      tot_eq += b2;
+    }
+    const uint32_t at = gt_before + min(eq_before, need);
+    if ((gt || (eq && eq_before < need)) && at < (uint32_t)k) out[at] = i;
+    run_gt += tot_gt;
+    run_eq += tot_eq;
+    if (run_gt + min(run_eq, need) >= (uint32_t)k) break;  // uniform: all k written
+  }
+}
+
+__global__ void __launch_bounds__(TK_THREADS)
+topk_row_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
+                const float* __restrict__ scores, int64_t ld, int k, int32_t* __restrict__ idx) {
+  __shared__ uint32_t hist[2048];
+  __shared__ uint32_t xch[2][TK_WAVES][2];
+  __shared__ uint32_t s_digit, s_above;
+
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x;
+  const RowLoc L = locate_row(cu_q, cu_k, B, r);
+  const int n = L.pos + 1;
+  int32_t* out = idx + (int64_t)r * k;
+  const float* row = scores + (int64_t)r * ld;
+
+  if (n <= k) {  // every candidate is selected
+    for (int i = tid; i < k; i += TK_THREADS) out[i] = i < n ? i : -1;
+    return;
+  }
+  topk_row_exact<TK_THREADS>(row, n, k, out, hist, xch, &s_digit, &s_above);
+}
+
+// ------------------------------------------------------------------------------------------
+// Register-resident variant for rows of up to 4096 * NT candidates. The row is read once, as
+// float4: in tile j (positions 4096j .. 4096j + 4095) thread t holds positions 4096j + 4t + c,
+// c = 0..3, and keeps only the upper 16 bits of their keys, two per register. Digits 1 and 2 of
+// the threshold (key bits 31..21 and 20..16) come from registers; digits 3 and 4 (bits 15..8 and
+// 7..0) only concern keys whose upper half equals the threshold's, and those few are re-read from
+// memory. The ordered compaction counts, per lane, the keys above / equal to the threshold, scans
+// the counts across the wave, stores one total per (tile, wave), turns those totals into offsets
+// with one block-wide exclusive scan in (tile, wave) order -- which is position order -- and
+// writes every selected position at its offset.
+
+__device__ __forceinline__ uint32_t block_excl_scan2(uint32_t a, uint32_t b, uint32_t* sw,
+                                                     uint32_t& excl_b) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t xa = a, xb = b;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t ta = __shfl_up(xa, off), tb = __shfl_up(xb, off);
+    if (lane >= off) { xa += ta; xb += tb; }
+  }
+  if (lane == 63) { sw[2 * wave] = xa; sw[2 * wave + 1] = xb; }
+  __syncthreads();
+  uint32_t ba = 0, bb = 0;
+  for (int w = 0; w < wave; ++w) { ba += sw[2 * w]; bb += sw[2 * w + 1]; }
+  excl_b = bb + xb - b;
+  return ba + xa - a;
 }
 
 constexpr int TK_TILE = 4 * TK_THREADS;      // positions per tile (one float4 per thread)
@@ -520,6 +505,222 @@ topk_reg_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restri
 #undef HI
 }
 
+// ------------------------------------------------------------------------------------------
+// Streaming variant for k <= 2048 and rows of up to 131072 candidates: one pass over the row with
+// almost no work per score, so that the pass runs at memory speed, and a small workgroup (four
+// waves, 72 KB of LDS) so that two rows share a compute unit and one row's selection work
+// overlaps the other's streaming.
+//  1. A sample of the row (all of it up to 8192 positions, else 8 evenly spaced runs of 1024) is
+//     kept in LDS; radix select gives its `want`-th largest key F. With the whole row as sample
+//     want = k, so at least k keys reach F; otherwise want = 1.5 k S / n aims at about 1.5 k keys.
+//  2. The stream appends every key >= F with its position to an LDS list (ballot, one atomic per
+//     wave, lanes-below offsets).
+//  3. If the list holds fewer than k or more than its 4096 slots, the row is redone exactly from
+//     global memory (rare: a sample far from the row's distribution, or massive ties).
+//  4. Radix select over the list finds the k-th largest key T and how many keys equal to T are
+//     taken (`need`, the lowest positions first).
+//  5. The list marks two position bitmaps (keys > T, keys == T); each thread owns a run of words,
+//     counts its bits, one block-wide exclusive scan gives its output offsets, and it writes its
+//     positions in ascending order, keeping only the first `need` equal keys of the row.
+constexpr int TS_THREADS = 256;
+constexpr int TS_WAVES = TS_THREADS / 64;
+constexpr int TS_MAXN = 131072;            // positions covered by the bitmaps
+constexpr int TS_MAXK = 2048;
+constexpr int TS_CAP = 4096;               // candidate slots
+constexpr int TS_SEG = 1024;               // positions per sample run
+constexpr int TS_SEGS = 8;
+constexpr int TS_SAMPLE = TS_SEG * TS_SEGS;   // 8192 = 2 * TS_CAP: the sample reuses the list
+constexpr int TS_UNROLL = 8;               // float4 loads in flight per thread
+
+// Radix select over `count` keys in LDS (digits of 11, 11 and 10 bits): the want-th largest key
+// T (returned) and how many of the keys equal to T rank within the first `want` (*need_out).
+__device__ __forceinline__ uint32_t lds_select(const uint32_t* keys, uint32_t count, uint32_t want,
+                                               uint32_t* hist, uint32_t* s_digit, uint32_t* s_above,
+                                               uint32_t* need_out) {
+  const int tid = threadIdx.x;
+  uint32_t prefix = 0, pmask = 0, need = want;
+#pragma unroll 1
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+    const int nb = pass == 2 ? 1024 : 2048;
+    for (int i = tid; i < nb; i += TS_THREADS) hist[i] = 0;
+    __syncthreads();
+    for (uint32_t c = tid; c < count; c += TS_THREADS) {
+      const uint32_t u = keys[c];
+      if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & (nb - 1)], 1u);
+    }
+    __syncthreads();
+    select_bin(hist, nb, need, s_digit, s_above);
+    prefix |= *s_digit << shift;
+    pmask |= (uint32_t)(nb - 1) << shift;
+    need -= *s_above;
+  }
+  *need_out = need;
+  return prefix;
+}
+
+__global__ void __launch_bounds__(TS_THREADS)
+topk_stream_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
+                   const float* __restrict__ scores, int64_t ld, int k, int32_t* __restrict__ idx) {
+  __shared__ uint32_t hist[2048];
+  __shared__ uint32_t cbuf[2 * TS_CAP];    // sample keys, then candidate keys | positions
+  __shared__ uint32_t gtm[TS_MAXN / 32];
+  __shared__ uint32_t eqm[TS_MAXN / 32];
+  __shared__ uint32_t xch[2][TS_WAVES][2];
+  __shared__ uint32_t s_digit, s_above, s_count;
+  uint32_t* const ckey = cbuf;
+  uint32_t* const cpos = cbuf + TS_CAP;
+
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const RowLoc L = locate_row(cu_q, cu_k, B, r);
+  const int n = L.pos + 1;
+  int32_t* out = idx + (int64_t)r * k;
+  const float* row = scores + (int64_t)r * ld;
+
+  if (n <= k) {
+    for (int i = tid; i < k; i += TS_THREADS) out[i] = i < n ? i : -1;
+    return;
+  }
+  const int nw = (n + 31) >> 5;
+  for (int i = tid; i < nw; i += TS_THREADS) {
+    gtm[i] = 0;
+    eqm[i] = 0;
+  }
+
+  // 1. sample and floor
+  const bool whole = n <= TS_SAMPLE;
+  const int S = whole ? n : TS_SAMPLE;
+  if (whole) {
+    for (int i = tid; i < n; i += TS_THREADS) cbuf[i] = float_to_ordered(row[i]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < TS_SEGS; ++j) {
+      const int start = (int)((int64_t)j * (n - TS_SEG) / (TS_SEGS - 1));
+#pragma unroll
+      for (int c = 0; c < TS_SEG / TS_THREADS; ++c)
+        cbuf[j * TS_SEG + c * TS_THREADS + tid] = float_to_ordered(row[start + c * TS_THREADS + tid]);
+    }
+  }
+  if (tid == 0) s_count = 0;
+  __syncthreads();
+  const uint32_t want = whole ? (uint32_t)k
+                              : (uint32_t)max<int64_t>(1, min<int64_t>(S, (3 * (int64_t)k * S + 2 * (int64_t)n - 1) / (2 * (int64_t)n)));
+  uint32_t unused;
+  const uint32_t F = lds_select(cbuf, (uint32_t)S, want, hist, &s_digit, &s_above, &unused);
+  __syncthreads();   // every thread has F before the list overwrites the sample
+
+  // 2. stream: list every key >= F. Keys are compared as floats (the order-preserving map is
+  // monotone and folds -0 onto +0, which the float comparison treats as equal too); per batch of
+  // 32 scores per lane the wave counts its hits, reserves its slots with one atomic, and its
+  // lanes then store key and position of each hit.
+  const float Ff = __uint_as_float((F & 0x80000000u) ? (F & 0x7FFFFFFFu) : ~F);
+  const int n4 = n & ~3;
+  for (int base = 0; base < n4; base += TS_THREADS * 4 * TS_UNROLL) {
+    float4 v[TS_UNROLL];
+#pragma unroll
+    for (int u = 0; u < TS_UNROLL; ++u) {
+      const int i = base + (u * TS_THREADS + tid) * 4;
+      v[u] = i < n4 ? *reinterpret_cast<const float4*>(row + i) : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+    }
+    uint32_t hits = 0;   // wave-uniform
+#pragma unroll
+    for (int u = 0; u < TS_UNROLL; ++u) {
+      const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) hits += (uint32_t)__popcll(__ballot(e[c] >= Ff));
+    }
+    if (hits) {   // uniform
+      uint32_t wbase = 0;
+      if (lane == 0) wbase = atomicAdd(&s_count, hits);
+      uint32_t run = __builtin_amdgcn_readfirstlane(wbase);
+#pragma unroll
+      for (int u = 0; u < TS_UNROLL; ++u) {
+        const int i = base + (u * TS_THREADS + tid) * 4;
+        const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const bool sel = e[c] >= Ff;
+          const uint64_t m = __ballot(sel);
+          if (m) {   // uniform
+            if (sel) {
+              const uint32_t slot = run + lanes_below_count(m);
+              if (slot < TS_CAP) {
+                ckey[slot] = float_to_ordered(e[c]);
+                cpos[slot] = (uint32_t)(i + c);
+              }
+            }
+            run += (uint32_t)__popcll(m);
+          }
+        }
+      }
+    }
+  }
+  {
+    const int i = n4 + tid;   // tail: fewer than 4 positions
+    const float e = i < n ? row[i] : -INFINITY;
+    const bool sel = i < n && e >= Ff;
+    const uint64_t m = __ballot(sel);
+    if (m) {
+      uint32_t wbase = 0;
+      if (lane == 0) wbase = atomicAdd(&s_count, (uint32_t)__popcll(m));
+      wbase = __builtin_amdgcn_readfirstlane(wbase);
+      if (sel) {
+        const uint32_t slot = wbase + lanes_below_count(m);
+        if (slot < TS_CAP) {
+          ckey[slot] = float_to_ordered(e);
+          cpos[slot] = (uint32_t)i;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  const uint32_t total = s_count;
+  if (total < (uint32_t)k || total > (uint32_t)TS_CAP) {
+    topk_row_exact<TS_THREADS>(row, n, k, out, hist, xch, &s_digit, &s_above);
+    return;
+  }
+
+  // 4. radix select over the list
+  uint32_t need;
+  const uint32_t T = lds_select(ckey, total, (uint32_t)k, hist, &s_digit, &s_above, &need);
+
+  // 5. bitmaps, one scan, ascending output
+  for (uint32_t c = tid; c < total; c += TS_THREADS) {
+    const uint32_t u = ckey[c], p = cpos[c];
+    if (u > T) atomicOr(&gtm[p >> 5], 1u << (p & 31));
+    else if (u == T) atomicOr(&eqm[p >> 5], 1u << (p & 31));
+  }
+  __syncthreads();
+  const int per = (nw + TS_THREADS - 1) / TS_THREADS;
+  const int w0 = min(tid * per, nw), w1 = min(w0 + per, nw);
+  uint32_t cg = 0, ce = 0;
+  for (int w = w0; w < w1; ++w) {
+    cg += (uint32_t)__popc(gtm[w]);
+    ce += (uint32_t)__popc(eqm[w]);
+  }
+  uint32_t e_before;
+  const uint32_t g_before = block_excl_scan2(cg, ce, &xch[0][0][0], e_before);
+  uint32_t slot = g_before + min(e_before, need);
+  uint32_t e_seen = e_before;
+  for (int w = w0; w < w1; ++w) {
+    const uint32_t g = gtm[w], e = eqm[w];
+    uint32_t keep = e;
+    const uint32_t pe = (uint32_t)__popc(e);
+    if (e_seen >= need) {
+      keep = 0u;
+    } else if (e_seen + pe > need) {
+      for (uint32_t drop = e_seen + pe - need; drop > 0; --drop) keep &= ~(1u << (31 - __clz(keep)));
+    }
+    e_seen += pe;
+    uint32_t sel = g | keep;
+    while (sel) {
+      out[slot++] = w * 32 + (__ffs(sel) - 1);
+      sel &= sel - 1;
+    }
+  }
+}
+
 size_t topk_workspace_bytes(const SeqInfo&, int) { return 0; }
 
 hipError_t launch_topk(const SeqInfo& s, const float* scores, int64_t ld, int k, int32_t* idx,
@@ -527,7 +728,12 @@ hipError_t launch_topk(const SeqInfo& s, const float* scores, int64_t ld, int k,
   if (s.T == 0) return hipSuccess;
   const int tiles = (s.max_n + TK_TILE - 1) / TK_TILE;
   const dim3 grid(s.T), block(TK_THREADS);
-  if (tiles <= 2)
+  // the streaming kernel needs enough rows to keep two per compute unit busy; small batches
+  // (decode) use the register-resident kernel, whose 16 waves per row finish one row faster
+  if (k <= TS_MAXK && s.max_n <= TS_MAXN && s.T >= 2 * device_cu_count())
+    hipLaunchKernelGGL(topk_stream_kernel, grid, dim3(TS_THREADS), 0, st, s.B, s.cu_q, s.cu_k, scores, ld,
+                       k, idx);
+  else if (tiles <= 2)
     hipLaunchKernelGGL(topk_reg_kernel<2>, grid, block, 0, st, s.B, s.cu_q, s.cu_k, scores, ld, k, idx);
   else if (tiles <= 8)
     hipLaunchKernelGGL(topk_reg_kernel<8>, grid, block, 0, st, s.B, s.cu_q, s.cu_k, scores, ld, k, idx);

@@ -211,23 +211,32 @@ def test_topk_ties_and_zeros(gpu):
         assert idx[r].tolist() == oracle.topk_row(sc[r, :pos + 1].astype(np.float64), k).tolist()
 
 
+@pytest.mark.parametrize("rows", [5, 600])
 @pytest.mark.parametrize("n", [5000, 30000, 131072, 140000])
-def test_topk_row_lengths_and_degenerate_rows(gpu, n):
-    """Every top-k code path (register-resident rows of 1, 2..8, 9..32 tiles of 4096 and the
-    multi-pass fallback beyond 131072), with degenerate rows: all equal, all +-0, one distinct
-    value, integer ties, and random floats."""
+def test_topk_row_lengths_and_degenerate_rows(gpu, n, rows):
+    """Every top-k code path: register-resident rows of 1, 2..8, 9..32 tiles of 4096 (small
+    batches), the streaming kernel with its exact fallback (batches of at least two rows per
+    compute unit), the multi-pass kernel beyond 131072 -- each with degenerate rows: all equal,
+    all +-0, one distinct value, integer ties, random floats, and a row whose largest values all
+    sit outside the sampled runs."""
     k = 2048
-    rng = np.random.default_rng(n)
-    rows = [np.full(n, 1.5, np.float32),
+    rng = np.random.default_rng(n + rows)
+    late = rng.standard_normal(n).astype(np.float32)
+    late[n - 3000:] += 50.0   # the top scores cluster in one stretch of the row
+    pats = [np.full(n, 1.5, np.float32),
             np.where(rng.random(n) < 0.5, 0.0, -0.0).astype(np.float32),
             np.concatenate([np.full(n - 1, -2.0, np.float32), [3.0]]).astype(np.float32),
             rng.integers(-4, 5, size=n).astype(np.float32),
-            rng.standard_normal(n).astype(np.float32)]
-    sc = np.stack(rows)
-    T = sc.shape[0]
+            rng.standard_normal(n).astype(np.float32),
+            late]
+    T = max(rows, len(pats))
+    sc = np.empty((T, n), np.float32)
+    for r in range(T):
+        sc[r] = pats[r] if r < len(pats) else rng.standard_normal(n).astype(np.float32)
     seqs = gpu.Seqs([0, T], [0, n])
     idx = gpu.topk(seqs, torch.from_numpy(sc).cuda(), k).cpu().numpy()
-    for r in range(T):
+    check = list(range(len(pats))) + list(range(len(pats), T, max(1, T // 8)))[:8] + [T - 1]
+    for r in check:
         pos = n - T + r
         assert idx[r].tolist() == oracle.topk_row(sc[r, :pos + 1].astype(np.float64), k).tolist(), f"row {r}"
 
