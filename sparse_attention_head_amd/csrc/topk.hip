@@ -28,7 +28,9 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
 }
 
 // Finds the bin holding the need-th largest key among the counted ones (suffix sums from the
-// top bin down). Called by all threads; wave 0 does the work.
+// top bin down). Called by all threads; wave 0 does the work: lane l sums bins l*per ..
+// l*per + per - 1 (per <= 64), a suffix scan across lanes finds the lane whose run holds the
+// need-th largest key, and a second scan over that run's bins (one bin per lane) finds the bin.
 __device__ __forceinline__ void select_bin(const uint32_t* hist, int nb, uint32_t need,
                                            uint32_t* s_digit, uint32_t* s_above) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -39,25 +41,31 @@ __device__ __forceinline__ void select_bin(const uint32_t* hist, int nb, uint32_
       const int bin = lane * per + j;
       sum += bin < nb ? hist[bin] : 0u;
     }
-    uint32_t suf = sum;
+    uint32_t suf = sum;   // bins of this lane and above
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const uint32_t t = __shfl_down(suf, off);
       if (lane + off < 64) suf += t;
     }
     const uint32_t above_lane = suf - sum;
-    if (suf >= need && above_lane < need) {
-      uint32_t above = above_lane;
-      for (int j = per - 1; j >= 0; --j) {
-        const int bin = lane * per + j;
-        const uint32_t h = bin < nb ? hist[bin] : 0u;
-        if (above + h >= need) {
-          *s_digit = (uint32_t)bin;
-          *s_above = above;
-          break;
-        }
-        above += h;
-      }
+    // the crossing lane: its run holds the need-th largest key
+    const uint64_t hit = __ballot(suf >= need && above_lane < need);
+    const int cl = __builtin_amdgcn_readfirstlane(hit ? (int)(__ffsll((unsigned long long)hit) - 1) : 0);
+    const uint32_t above = __builtin_amdgcn_readfirstlane(__shfl(above_lane, cl));
+    // bins of that run, one per lane (lane j: bin cl*per + j), suffix sums within the run
+    const int bin = cl * per + lane;
+    const uint32_t h = (lane < per && bin < nb) ? hist[bin] : 0u;
+    uint32_t rs = h;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t t = __shfl_down(rs, off);
+      if (lane + off < 64) rs += t;
+    }
+    // the bin: above + (bins of the run above it) < need <= above + rs
+    const uint64_t hb = __ballot(lane < per && above + rs >= need && above + rs - h < need);
+    if (hb && lane == (int)(__ffsll((unsigned long long)hb) - 1)) {
+      *s_digit = (uint32_t)bin;
+      *s_above = above + rs - h;
     }
   }
   __syncthreads();
@@ -508,39 +516,46 @@ topk_reg_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restri
 // ------------------------------------------------------------------------------------------
 // Streaming variant for k <= 2048 and rows of up to 131072 candidates: one pass over the row with
 // almost no work per score, so that the pass runs at memory speed, and a small workgroup (four
-// waves, 72 KB of LDS) so that two rows share a compute unit and one row's selection work
-// overlaps the other's streaming.
+// waves, 52 KB of LDS) so that three rows share a compute unit and the selection work of some
+// overlaps the streaming of others.
 //  1. A sample of the row (all of it up to 8192 positions, else 8 evenly spaced runs of 1024) is
-//     kept in LDS; radix select gives its `want`-th largest key F. With the whole row as sample
-//     want = k, so at least k keys reach F; otherwise want = 1.5 k S / n aims at about 1.5 k keys.
-//  2. The stream appends every key >= F with its position to an LDS list (ballot, one atomic per
-//     wave, lanes-below offsets).
-//  3. If the list holds fewer than k or more than its 4096 slots, the row is redone exactly from
-//     global memory (rare: a sample far from the row's distribution, or massive ties).
-//  4. Radix select over the list finds the k-th largest key T and how many keys equal to T are
-//     taken (`need`, the lowest positions first).
-//  5. The list marks two position bitmaps (keys > T, keys == T); each thread owns a run of words,
-//     counts its bits, one block-wide exclusive scan gives its output offsets, and it writes its
-//     positions in ascending order, keeping only the first `need` equal keys of the row.
+//     kept in LDS; two radix digits (22 key bits) locate its `want`-th largest key and the floor F
+//     is that 22-bit bin's lower edge. With the whole row as sample want = k, so at least k keys
+//     reach F; otherwise want = 1.3 k S / n aims at about 1.3 k keys (3 sigma above k and 4.5
+//     sigma below the list's capacity for independent scores).
+//  2. The stream appends every score >= F with its position to an LDS list (float comparison,
+//     per batch of 32 scores per lane one atomic per wave reserves the slots).
+//  3. If the list holds fewer than k or more than its 3584 slots, or more than 2048 keys tie at
+//     the threshold, the row is redone exactly from global memory.
+//  4. Radix select over the list: the k-th largest key T and how many keys equal to T are taken
+//     (`need`, the lowest positions first; when fewer than all, a radix select over the tied
+//     positions finds the last one taken).
+//  5. The selected positions are marked in a bitmap; each thread owns a run of its words, one
+//     block-wide exclusive scan of their popcounts gives the output offsets, and every thread
+//     writes its positions in ascending order.
 constexpr int TS_THREADS = 256;
 constexpr int TS_WAVES = TS_THREADS / 64;
-constexpr int TS_MAXN = 131072;            // positions covered by the bitmaps
+constexpr int TS_MAXN = 131072;            // positions covered by the bitmap
 constexpr int TS_MAXK = 2048;
-constexpr int TS_CAP = 4096;               // candidate slots
+constexpr int TS_CAP = 3584;               // list slots
 constexpr int TS_SEG = 1024;               // positions per sample run
 constexpr int TS_SEGS = 8;
-constexpr int TS_SAMPLE = TS_SEG * TS_SEGS;   // 8192 = 2 * TS_CAP: the sample reuses the list
+constexpr int TS_SAMPLE = TS_SEG * TS_SEGS;   // 8192
+constexpr int TS_MAXEQ = 2048;             // tied keys handled in LDS
+constexpr int TS_REGION = 2 * TS_CAP + TS_MAXN / 32;   // 11264 words: sample | list keys, list positions, bitmap
+static_assert(TS_SAMPLE <= TS_REGION, "the sample reuses the list and bitmap space");
 constexpr int TS_UNROLL = 8;               // float4 loads in flight per thread
 
-// Radix select over `count` keys in LDS (digits of 11, 11 and 10 bits): the want-th largest key
-// T (returned) and how many of the keys equal to T rank within the first `want` (*need_out).
+// Radix select over `count` keys in LDS, `passes` digits (11, 11, 10 bits) from the top: the
+// key prefix of the want-th largest key (the key itself after 3 passes) and how many of the keys
+// with that prefix rank within the first `want` (*need_out). hist: 2048 words.
 __device__ __forceinline__ uint32_t lds_select(const uint32_t* keys, uint32_t count, uint32_t want,
-                                               uint32_t* hist, uint32_t* s_digit, uint32_t* s_above,
-                                               uint32_t* need_out) {
+                                               int passes, uint32_t* hist, uint32_t* s_digit,
+                                               uint32_t* s_above, uint32_t* need_out) {
   const int tid = threadIdx.x;
   uint32_t prefix = 0, pmask = 0, need = want;
 #pragma unroll 1
-  for (int pass = 0; pass < 3; ++pass) {
+  for (int pass = 0; pass < passes; ++pass) {
     const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
     const int nb = pass == 2 ? 1024 : 2048;
     for (int i = tid; i < nb; i += TS_THREADS) hist[i] = 0;
@@ -562,14 +577,13 @@ __device__ __forceinline__ uint32_t lds_select(const uint32_t* keys, uint32_t co
 __global__ void __launch_bounds__(TS_THREADS)
 topk_stream_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
                    const float* __restrict__ scores, int64_t ld, int k, int32_t* __restrict__ idx) {
-  __shared__ uint32_t hist[2048];
-  __shared__ uint32_t cbuf[2 * TS_CAP];    // sample keys, then candidate keys | positions
-  __shared__ uint32_t gtm[TS_MAXN / 32];
-  __shared__ uint32_t eqm[TS_MAXN / 32];
+  __shared__ uint32_t hist[2048];          // histograms; tied positions at the end
+  __shared__ uint32_t region[TS_REGION];
   __shared__ uint32_t xch[2][TS_WAVES][2];
-  __shared__ uint32_t s_digit, s_above, s_count;
-  uint32_t* const ckey = cbuf;
-  uint32_t* const cpos = cbuf + TS_CAP;
+  __shared__ uint32_t s_digit, s_above, s_count, s_eq;
+  uint32_t* const ckey = region;
+  uint32_t* const cpos = region + TS_CAP;
+  uint32_t* const bmap = region + 2 * TS_CAP;
 
   const int r = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -583,46 +597,55 @@ topk_stream_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __res
     return;
   }
   const int nw = (n + 31) >> 5;
-  for (int i = tid; i < nw; i += TS_THREADS) {
-    gtm[i] = 0;
-    eqm[i] = 0;
-  }
 
   // 1. sample and floor
   const bool whole = n <= TS_SAMPLE;
   const int S = whole ? n : TS_SAMPLE;
   if (whole) {
-    for (int i = tid; i < n; i += TS_THREADS) cbuf[i] = float_to_ordered(row[i]);
+    for (int i = tid; i < n; i += TS_THREADS) region[i] = float_to_ordered(row[i]);
   } else {
 #pragma unroll
     for (int j = 0; j < TS_SEGS; ++j) {
       const int start = (int)((int64_t)j * (n - TS_SEG) / (TS_SEGS - 1));
 #pragma unroll
       for (int c = 0; c < TS_SEG / TS_THREADS; ++c)
-        cbuf[j * TS_SEG + c * TS_THREADS + tid] = float_to_ordered(row[start + c * TS_THREADS + tid]);
+        region[j * TS_SEG + c * TS_THREADS + tid] = float_to_ordered(row[start + c * TS_THREADS + tid]);
     }
   }
-  if (tid == 0) s_count = 0;
+  if (tid == 0) {
+    s_count = 0;
+    s_eq = 0;
+  }
   __syncthreads();
   const uint32_t want = whole ? (uint32_t)k
-                              : (uint32_t)max<int64_t>(1, min<int64_t>(S, (3 * (int64_t)k * S + 2 * (int64_t)n - 1) / (2 * (int64_t)n)));
+                              : (uint32_t)max<int64_t>(1, min<int64_t>(S, (13 * (int64_t)k * S + 10 * (int64_t)n - 1) / (10 * (int64_t)n)));
   uint32_t unused;
-  const uint32_t F = lds_select(cbuf, (uint32_t)S, want, hist, &s_digit, &s_above, &unused);
-  __syncthreads();   // every thread has F before the list overwrites the sample
+  const uint32_t F = lds_select(region, (uint32_t)S, want, 2, hist, &s_digit, &s_above, &unused);
+  __syncthreads();   // every thread has F before the list and bitmap overwrite the sample
+  for (int i = tid; i < nw; i += TS_THREADS) bmap[i] = 0;
 
-  // 2. stream: list every key >= F. Keys are compared as floats (the order-preserving map is
+  // 2. stream: list every score >= F. Scores are compared as floats (the order-preserving map is
   // monotone and folds -0 onto +0, which the float comparison treats as equal too); per batch of
   // 32 scores per lane the wave counts its hits, reserves its slots with one atomic, and its
   // lanes then store key and position of each hit.
   const float Ff = __uint_as_float((F & 0x80000000u) ? (F & 0x7FFFFFFFu) : ~F);
   const int n4 = n & ~3;
-  for (int base = 0; base < n4; base += TS_THREADS * 4 * TS_UNROLL) {
-    float4 v[TS_UNROLL];
+  // batches of TS_UNROLL float4 per lane, double-buffered: the next batch is in flight while the
+  // current one is scanned
+  auto load_batch = [&](int base, float4 (&v)[TS_UNROLL]) {
 #pragma unroll
     for (int u = 0; u < TS_UNROLL; ++u) {
       const int i = base + (u * TS_THREADS + tid) * 4;
       v[u] = i < n4 ? *reinterpret_cast<const float4*>(row + i) : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
     }
+  };
+  float4 vn[TS_UNROLL];
+  load_batch(0, vn);
+  for (int base = 0; base < n4; base += TS_THREADS * 4 * TS_UNROLL) {
+    float4 v[TS_UNROLL];
+#pragma unroll
+    for (int u = 0; u < TS_UNROLL; ++u) v[u] = vn[u];
+    if (base + TS_THREADS * 4 * TS_UNROLL < n4) load_batch(base + TS_THREADS * 4 * TS_UNROLL, vn);
     uint32_t hits = 0;   // wave-uniform
 #pragma unroll
     for (int u = 0; u < TS_UNROLL; ++u) {
@@ -681,39 +704,49 @@ topk_stream_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __res
     return;
   }
 
-  // 4. radix select over the list
+  // 4. radix select over the list; keys above T go to the bitmap, tied positions to a list
   uint32_t need;
-  const uint32_t T = lds_select(ckey, total, (uint32_t)k, hist, &s_digit, &s_above, &need);
-
-  // 5. bitmaps, one scan, ascending output
+  const uint32_t T = lds_select(ckey, total, (uint32_t)k, 3, hist, &s_digit, &s_above, &need);
+  __syncthreads();   // the histogram space is reused for the tied positions
   for (uint32_t c = tid; c < total; c += TS_THREADS) {
     const uint32_t u = ckey[c], p = cpos[c];
-    if (u > T) atomicOr(&gtm[p >> 5], 1u << (p & 31));
-    else if (u == T) atomicOr(&eqm[p >> 5], 1u << (p & 31));
+    if (u > T) {
+      atomicOr(&bmap[p >> 5], 1u << (p & 31));
+    } else if (u == T) {
+      const uint32_t e = atomicAdd(&s_eq, 1u);
+      if (e < (uint32_t)TS_MAXEQ) hist[e] = ~p;   // inverted: the largest are the lowest positions
+    }
   }
   __syncthreads();
+  const uint32_t eqc = s_eq;
+  if (eqc > (uint32_t)TS_MAXEQ) {
+    topk_row_exact<TS_THREADS>(row, n, k, out, hist, xch, &s_digit, &s_above);
+    return;
+  }
+  // the tied keys taken are the `need` lowest positions: ~pos >= the need-th largest ~pos
+  uint32_t cut = 0u;
+  if (eqc > need) {
+    uint32_t unused2;
+    cut = lds_select(hist, eqc, need, 3, ckey, &s_digit, &s_above, &unused2);   // ckey is free now
+  }
+  for (uint32_t e = tid; e < eqc; e += TS_THREADS) {
+    const uint32_t ip = hist[e];
+    if (ip >= cut) {
+      const uint32_t p = ~ip;
+      atomicOr(&bmap[p >> 5], 1u << (p & 31));
+    }
+  }
+  __syncthreads();
+
+  // 5. one scan over the bitmap, ascending output
   const int per = (nw + TS_THREADS - 1) / TS_THREADS;
   const int w0 = min(tid * per, nw), w1 = min(w0 + per, nw);
-  uint32_t cg = 0, ce = 0;
+  uint32_t cnt = 0;
+  for (int w = w0; w < w1; ++w) cnt += (uint32_t)__popc(bmap[w]);
+  uint32_t unused3;
+  uint32_t slot = block_excl_scan2(cnt, 0u, &xch[0][0][0], unused3);
   for (int w = w0; w < w1; ++w) {
-    cg += (uint32_t)__popc(gtm[w]);
-    ce += (uint32_t)__popc(eqm[w]);
-  }
-  uint32_t e_before;
-  const uint32_t g_before = block_excl_scan2(cg, ce, &xch[0][0][0], e_before);
-  uint32_t slot = g_before + min(e_before, need);
-  uint32_t e_seen = e_before;
-  for (int w = w0; w < w1; ++w) {
-    const uint32_t g = gtm[w], e = eqm[w];
-    uint32_t keep = e;
-    const uint32_t pe = (uint32_t)__popc(e);
-    if (e_seen >= need) {
-      keep = 0u;
-    } else if (e_seen + pe > need) {
-      for (uint32_t drop = e_seen + pe - need; drop > 0; --drop) keep &= ~(1u << (31 - __clz(keep)));
-    }
-    e_seen += pe;
-    uint32_t sel = g | keep;
+    uint32_t sel = bmap[w];
     while (sel) {
       out[slot++] = w * 32 + (__ffs(sel) - 1);
       sel &= sel - 1;
