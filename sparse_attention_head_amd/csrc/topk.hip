@@ -515,36 +515,53 @@ topk_reg_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restri
 
 // ------------------------------------------------------------------------------------------
 // Streaming variant for k <= 2048 and rows of up to 131072 candidates: one pass over the row with
-// almost no work per score, so that the pass runs at memory speed, and a small workgroup (four
-// waves, 52 KB of LDS) so that three rows share a compute unit and the selection work of some
-// overlaps the streaming of others.
+// about two vector instructions per score, so that the pass runs at memory speed, and workgroups
+// of eight waves with 76 KB of LDS, two per compute unit, so that the selection work of one row
+// overlaps the streaming of another.
 //  1. A sample of the row (all of it up to 8192 positions, else 8 evenly spaced runs of 1024) is
 //     kept in LDS; two radix digits (22 key bits) locate its `want`-th largest key and the floor F
 //     is that 22-bit bin's lower edge. With the whole row as sample want = k, so at least k keys
-//     reach F; otherwise want = 1.3 k S / n aims at about 1.3 k keys (3 sigma above k and 4.5
-//     sigma below the list's capacity for independent scores).
-//  2. The stream appends every score >= F with its position to an LDS list (float comparison,
-//     per batch of 32 scores per lane one atomic per wave reserves the slots).
-//  3. If the list holds fewer than k or more than its 3584 slots, or more than 2048 keys tie at
-//     the threshold, the row is redone exactly from global memory.
-//  4. Radix select over the list: the k-th largest key T and how many keys equal to T are taken
+//     reach F; otherwise want = 1.3 k S / n aims at about 1.3 k keys (3 sigma above k and about
+//     4 sigma below the list's capacity for independent scores).
+//  2. The stream works on groups of 4 consecutive scores (one float4 per lane): a group whose
+//     maximum reaches F is appended whole, with its position, to a list in LDS (structure of
+//     arrays). Per batch of 8 groups per lane one atomic per wave reserves the slots; each lane
+//     then stores every group unconditionally, to its slot or, without a hit, to a spare slot of
+//     its own, so the loop has no per-group branch.
+//  3. The groups are compacted into a list of single keys >= F with their positions.
+//  4. If there are more groups than slots, fewer than k or more than 4096 keys, or more than 2048
+//     keys tie at the threshold, the row is redone exactly from global memory.
+//  5. Radix select over the list: the k-th largest key T and how many keys equal to T are taken
 //     (`need`, the lowest positions first; when fewer than all, a radix select over the tied
 //     positions finds the last one taken).
-//  5. The selected positions are marked in a bitmap; each thread owns a run of its words, one
+//  6. The selected positions are marked in a bitmap; each thread owns a run of its words, one
 //     block-wide exclusive scan of their popcounts gives the output offsets, and every thread
 //     writes its positions in ascending order.
-constexpr int TS_THREADS = 256;
+constexpr int TS_THREADS = 512;
 constexpr int TS_WAVES = TS_THREADS / 64;
 constexpr int TS_MAXN = 131072;            // positions covered by the bitmap
 constexpr int TS_MAXK = 2048;
-constexpr int TS_CAP = 3584;               // list slots
+constexpr int TS_GCAP = 3392;              // group slots
+constexpr int TS_GSTRIDE = TS_GCAP + 64;   // words per group array: the slots, then one spare per lane
+static_assert(TS_GSTRIDE % 64 == 0, "group arrays are 256-byte aligned (paired-store offsets)");
+constexpr int TS_HCAP = 4096;              // keys in the compacted list
 constexpr int TS_SEG = 1024;               // positions per sample run
 constexpr int TS_SEGS = 8;
 constexpr int TS_SAMPLE = TS_SEG * TS_SEGS;   // 8192
 constexpr int TS_MAXEQ = 2048;             // tied keys handled in LDS
-constexpr int TS_REGION = 2 * TS_CAP + TS_MAXN / 32;   // 11264 words: sample | list keys, list positions, bitmap
-static_assert(TS_SAMPLE <= TS_REGION, "the sample reuses the list and bitmap space");
+constexpr int TS_REGION = 5 * TS_GSTRIDE;  // sample | group arrays x, y, z, w, position | keys, positions, bitmap
+static_assert(TS_SAMPLE <= TS_REGION, "the sample shares the region");
+static_assert(2 * TS_HCAP + TS_MAXN / 32 <= TS_REGION, "compacted list and bitmap share the region");
 constexpr int TS_UNROLL = 8;               // float4 loads in flight per thread
+constexpr int TS_GPT = (TS_GCAP + TS_THREADS - 1) / TS_THREADS;   // groups per thread in the compaction
+
+// Largest of the four values (finite inputs: no NaN handling, which fmaxf would add per operand).
+__device__ __forceinline__ float max4(float4 v) {
+  float t, r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(t) : "v"(v.x), "v"(v.y), "v"(v.z));
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(t), "v"(v.w));
+  return r;
+}
 
 // Radix select over `count` keys in LDS, `passes` digits (11, 11, 10 bits) from the top: the
 // key prefix of the want-th largest key (the key itself after 3 passes) and how many of the keys
@@ -578,12 +595,12 @@ __global__ void __launch_bounds__(TS_THREADS)
 topk_stream_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
                    const float* __restrict__ scores, int64_t ld, int k, int32_t* __restrict__ idx) {
   __shared__ uint32_t hist[2048];          // histograms; tied positions at the end
-  __shared__ uint32_t region[TS_REGION];
+  __shared__ __attribute__((aligned(16))) uint32_t region[TS_REGION];
   __shared__ uint32_t xch[2][TS_WAVES][2];
   __shared__ uint32_t s_digit, s_above, s_count, s_eq;
   uint32_t* const ckey = region;
-  uint32_t* const cpos = region + TS_CAP;
-  uint32_t* const bmap = region + 2 * TS_CAP;
+  uint32_t* const cpos = region + TS_HCAP;
+  uint32_t* const bmap = region + 2 * TS_HCAP;
 
   const int r = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -621,90 +638,136 @@ topk_stream_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __res
                               : (uint32_t)max<int64_t>(1, min<int64_t>(S, (13 * (int64_t)k * S + 10 * (int64_t)n - 1) / (10 * (int64_t)n)));
   uint32_t unused;
   const uint32_t F = lds_select(region, (uint32_t)S, want, 2, hist, &s_digit, &s_above, &unused);
-  __syncthreads();   // every thread has F before the list and bitmap overwrite the sample
-  for (int i = tid; i < nw; i += TS_THREADS) bmap[i] = 0;
+  __syncthreads();   // every thread has F before the group arrays overwrite the sample
 
-  // 2. stream: list every score >= F. Scores are compared as floats (the order-preserving map is
-  // monotone and folds -0 onto +0, which the float comparison treats as equal too); per batch of
-  // 32 scores per lane the wave counts its hits, reserves its slots with one atomic, and its
-  // lanes then store key and position of each hit.
+  // 2. stream. Scores are compared as floats: the order-preserving key map is monotone and folds
+  // -0 onto +0, which the float comparison treats as equal too.
   const float Ff = __uint_as_float((F & 0x80000000u) ? (F & 0x7FFFFFFFu) : ~F);
   const int n4 = n & ~3;
-  // batches of TS_UNROLL float4 per lane, double-buffered: the next batch is in flight while the
-  // current one is scanned
+  // group arrays; a lane's slot address is its word index * 4, the arrays follow at multiples of
+  // TS_GSTRIDE words
+  const uint32_t spare4 = 4u * (uint32_t)(TS_GCAP + lane);
+  auto store_group = [&](uint32_t slot4, float4 v, uint32_t p) {   // slot4 = 4 * slot
+    uint32_t* a = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(region) + slot4);
+    a[0] = __float_as_uint(v.x);
+    a[TS_GSTRIDE] = __float_as_uint(v.y);
+    a[2 * TS_GSTRIDE] = __float_as_uint(v.z);
+    a[3 * TS_GSTRIDE] = __float_as_uint(v.w);
+    a[4 * TS_GSTRIDE] = p;
+  };
+  // batches of TS_UNROLL float4 per lane, double-buffered (two register sets used in turn): the
+  // next batch is in flight while the current one is scanned. Buffer loads: one resource per
+  // batch (starting at the batch, covering the whole groups left in the row) and fixed lane
+  // offsets, so no per-load address arithmetic; groups past the end read as zero (scan_batch then
+  // sets them to -inf), so every batch issues the same eight loads.
+  constexpr int BATCH = TS_THREADS * 4 * TS_UNROLL;
   auto load_batch = [&](int base, float4 (&v)[TS_UNROLL]) {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(row) + base, (short)0, max(n4 - base, 0) * 4, 0x00020000);
 #pragma unroll
     for (int u = 0; u < TS_UNROLL; ++u) {
-      const int i = base + (u * TS_THREADS + tid) * 4;
-      v[u] = i < n4 ? *reinterpret_cast<const float4*>(row + i) : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+      const auto t = __builtin_amdgcn_raw_buffer_load_b128(rs, (u * TS_THREADS + tid) * 16, 0, 0);
+      v[u] = make_float4(__uint_as_float(t[0]), __uint_as_float(t[1]), __uint_as_float(t[2]), __uint_as_float(t[3]));
     }
   };
-  float4 vn[TS_UNROLL];
-  load_batch(0, vn);
-  for (int base = 0; base < n4; base += TS_THREADS * 4 * TS_UNROLL) {
-    float4 v[TS_UNROLL];
+  auto scan_batch = [&](int base, float4 (&v)[TS_UNROLL]) {
+    if (base + BATCH > n4) {   // uniform: the partial batch
 #pragma unroll
-    for (int u = 0; u < TS_UNROLL; ++u) v[u] = vn[u];
-    if (base + TS_THREADS * 4 * TS_UNROLL < n4) load_batch(base + TS_THREADS * 4 * TS_UNROLL, vn);
-    uint32_t hits = 0;   // wave-uniform
+      for (int u = 0; u < TS_UNROLL; ++u)
+        if (base + (u * TS_THREADS + tid) * 4 >= n4) v[u] = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+    }
+    bool sel[TS_UNROLL];      // group u reaches F
+    uint64_t m[TS_UNROLL];    // wave-uniform: the lanes where it does
+    uint32_t hits = 0;
 #pragma unroll
     for (int u = 0; u < TS_UNROLL; ++u) {
-      const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-#pragma unroll
-      for (int c = 0; c < 4; ++c) hits += (uint32_t)__popcll(__ballot(e[c] >= Ff));
+      sel[u] = max4(v[u]) >= Ff;
+      m[u] = __ballot(sel[u]);
+      hits += (uint32_t)__popcll(m[u]);
     }
     if (hits) {   // uniform
       uint32_t wbase = 0;
       if (lane == 0) wbase = atomicAdd(&s_count, hits);
       uint32_t run = __builtin_amdgcn_readfirstlane(wbase);
+      if (run + hits <= (uint32_t)TS_GCAP) {   // uniform; on overflow the row is redone exactly
+        const uint32_t p0 = (uint32_t)(base + tid * 4);
 #pragma unroll
-      for (int u = 0; u < TS_UNROLL; ++u) {
-        const int i = base + (u * TS_THREADS + tid) * 4;
-        const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const bool sel = e[c] >= Ff;
-          const uint64_t m = __ballot(sel);
-          if (m) {   // uniform
-            if (sel) {
-              const uint32_t slot = run + lanes_below_count(m);
-              if (slot < TS_CAP) {
-                ckey[slot] = float_to_ordered(e[c]);
-                cpos[slot] = (uint32_t)(i + c);
-              }
-            }
-            run += (uint32_t)__popcll(m);
-          }
+        for (int u = 0; u < TS_UNROLL; ++u) {
+          const uint32_t at4 = 4u * lanes_below_count(m[u]) + 4u * run;
+          store_group(sel[u] ? at4 : spare4, v[u], p0 + (uint32_t)(u * TS_THREADS * 4));
+          run += (uint32_t)__popcll(m[u]);
         }
       }
     }
+  };
+  const int nb = (n4 + BATCH - 1) / BATCH;
+  if (nb > 0) {   // n4 >= 4
+    float4 va[TS_UNROLL], vb[TS_UNROLL];
+    load_batch(0, va);
+    for (int j = 0;;) {
+      load_batch((j + 1) * BATCH, vb);
+      scan_batch(j * BATCH, va);
+      if (++j >= nb) break;
+      load_batch((j + 1) * BATCH, va);
+      scan_batch(j * BATCH, vb);
+      if (++j >= nb) break;
+    }
   }
-  {
-    const int i = n4 + tid;   // tail: fewer than 4 positions
-    const float e = i < n ? row[i] : -INFINITY;
-    const bool sel = i < n && e >= Ff;
-    const uint64_t m = __ballot(sel);
-    if (m) {
-      uint32_t wbase = 0;
-      if (lane == 0) wbase = atomicAdd(&s_count, (uint32_t)__popcll(m));
-      wbase = __builtin_amdgcn_readfirstlane(wbase);
-      if (sel) {
-        const uint32_t slot = wbase + lanes_below_count(m);
-        if (slot < TS_CAP) {
-          ckey[slot] = float_to_ordered(e);
-          cpos[slot] = (uint32_t)i;
-        }
-      }
+  if (tid == 0 && n4 < n) {   // the last, partial group
+    const float4 t = *reinterpret_cast<const float4*>(row + n4);   // inside the row: ld >= round_up(n, 4)
+    const float4 v = make_float4(t.x, n4 + 1 < n ? t.y : -INFINITY, n4 + 2 < n ? t.z : -INFINITY, -INFINITY);
+    if (max4(v) >= Ff) {
+      const uint32_t at = atomicAdd(&s_count, 1u);
+      if (at < (uint32_t)TS_GCAP) store_group(4u * at, v, (uint32_t)n4);
     }
   }
   __syncthreads();
-  const uint32_t total = s_count;
-  if (total < (uint32_t)k || total > (uint32_t)TS_CAP) {
+
+  // 3. compaction of the groups into single keys >= F (order does not matter)
+  const uint32_t groups = s_count;
+  if (groups > (uint32_t)TS_GCAP) {
     topk_row_exact<TS_THREADS>(row, n, k, out, hist, xch, &s_digit, &s_above);
     return;
   }
+  float4 gv[TS_GPT];
+  uint32_t gp[TS_GPT], mine = 0;
+#pragma unroll
+  for (int j = 0; j < TS_GPT; ++j) {
+    const uint32_t g = (uint32_t)(tid + j * TS_THREADS);
+    if (g < groups) {
+      gv[j] = make_float4(__uint_as_float(region[g]), __uint_as_float(region[TS_GSTRIDE + g]),
+                          __uint_as_float(region[2 * TS_GSTRIDE + g]), __uint_as_float(region[3 * TS_GSTRIDE + g]));
+      gp[j] = region[4 * TS_GSTRIDE + g];
+    } else {
+      gv[j] = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+      gp[j] = 0;
+    }
+    mine += (gv[j].x >= Ff) + (gv[j].y >= Ff) + (gv[j].z >= Ff) + (gv[j].w >= Ff);
+  }
+  uint32_t unused_b;
+  uint32_t at = block_excl_scan2(mine, 0u, &xch[0][0][0], unused_b);   // barrier: all groups read
+  uint32_t total = 0;
+  for (int w = 0; w < TS_WAVES; ++w) total += xch[0][w][0];
+  if (total < (uint32_t)k || total > (uint32_t)TS_HCAP) {
+    __syncthreads();   // the fallback reuses xch
+    topk_row_exact<TS_THREADS>(row, n, k, out, hist, xch, &s_digit, &s_above);
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < TS_GPT; ++j) {
+    const float e[4] = {gv[j].x, gv[j].y, gv[j].z, gv[j].w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      if (e[c] >= Ff) {
+        ckey[at] = float_to_ordered(e[c]);
+        cpos[at] = gp[j] + (uint32_t)c;
+        ++at;
+      }
+  }
+  for (int i = tid; i < nw; i += TS_THREADS) bmap[i] = 0;
+  __syncthreads();
 
-  // 4. radix select over the list; keys above T go to the bitmap, tied positions to a list
+  // 5. radix select over the list; keys above T go to the bitmap, tied positions to a list
   uint32_t need;
   const uint32_t T = lds_select(ckey, total, (uint32_t)k, 3, hist, &s_digit, &s_above, &need);
   __syncthreads();   // the histogram space is reused for the tied positions
@@ -738,13 +801,13 @@ topk_stream_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __res
   }
   __syncthreads();
 
-  // 5. one scan over the bitmap, ascending output
+  // 6. one scan over the bitmap, ascending output
   const int per = (nw + TS_THREADS - 1) / TS_THREADS;
   const int w0 = min(tid * per, nw), w1 = min(w0 + per, nw);
   uint32_t cnt = 0;
   for (int w = w0; w < w1; ++w) cnt += (uint32_t)__popc(bmap[w]);
   uint32_t unused3;
-  uint32_t slot = block_excl_scan2(cnt, 0u, &xch[0][0][0], unused3);
+  uint32_t slot = block_excl_scan2(cnt, 0u, &xch[1][0][0], unused3);
   for (int w = w0; w < w1; ++w) {
     uint32_t sel = bmap[w];
     while (sel) {
