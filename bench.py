@@ -125,8 +125,10 @@ def measure(torch, dsa, wl, T, seqs, steps, warmup):
     t_idx = time_loop(torch, lambda: dsa.indexer_scores(seqs, T["qI"], T["kI"], T["w"], scores=scores, ws=iws),
                       steps, warmup)
     t_topk = time_loop(torch, lambda: dsa.topk(seqs, scores, wl.k, indices=idx), steps, warmup)
+    aws_n = dsa.attn_workspace_size(seqs, wl.H, wl.d_qk, wl.d_v, wl.k, dsa._dtype_code(T["q"]))
+    aws = torch.empty(max(aws_n, 1), dtype=torch.uint8, device="cuda")
     t_attn = time_loop(torch, lambda: dsa.sparse_mla_attn(seqs, T["q"], T["kv"], idx, wl.scale, wl.d_v,
-                                                          out=out, lse=lse), steps, warmup)
+                                                          out=out, lse=lse, ws=aws), steps, warmup)
     t_fwd = time_loop(torch, fwd, steps, warmup)
     return dict(fused_ms=t_fwd, indexer_ms=t_idx, topk_ms=t_topk, attn_ms=t_attn)
 

@@ -214,9 +214,15 @@ def topk(seqs: Seqs, scores, k: int, indices=None, stream=None):
     return indices
 
 
+def attn_workspace_size(seqs: Seqs, H: int, d_qk: int, d_v: int, k: int, dtype: int) -> int:
+    cs = seqs.c()
+    return int(_c_attn_ws(ctypes.byref(cs), H, d_qk, d_v, k, dtype))
+
+
 def sparse_mla_attn(seqs: Seqs, q, kv, indices, scale: float, d_v: int = None, out=None, lse=None,
-                    with_lse=True, stream=None):
-    """Attention of every head over the selected latent rows; returns (out, lse)."""
+                    with_lse=True, ws=None, stream=None):
+    """Attention of every head over the selected latent rows; returns (out, lse).
+    `ws` (uint8 device tensor of attn_workspace_size bytes) is allocated when not given."""
     torch = _torch()
     T, H, d_qk = (int(x) for x in q.shape)
     if d_v is None:
@@ -229,7 +235,10 @@ def sparse_mla_attn(seqs: Seqs, q, kv, indices, scale: float, d_v: int = None, o
     cs = seqs.c()
     dt = _dtype_code(q)
     wsz = int(_c_attn_ws(ctypes.byref(cs), H, d_qk, d_v, k, dt))
-    ws = torch.empty(max(wsz, 1), dtype=torch.uint8, device=q.device) if wsz else None
+    if ws is None:
+        ws = torch.empty(max(wsz, 1), dtype=torch.uint8, device=q.device) if wsz else None
+    elif wsz:
+        wsz = int(ws.numel())
     _check(_c_attn(ctypes.byref(cs), H, d_qk, d_v, dt, _ptr(q), _ptr(kv), _ptr(indices), k, float(scale),
                    _ptr(out), _ptr(lse), _ptr(ws), wsz, _stream(stream)), "dsa_sparse_mla_attn")
     return out, lse

@@ -333,11 +333,17 @@ __device__ __forceinline__ bool attend_block(const uint8_t* buf, uint64_t vmask,
   return false;
 }
 
+// One workgroup per (query row, split of its index list): the row's entries are split into
+// gridDim.y runs of whole blocks. With one split the workgroup writes the normalised output and
+// lse; with several it writes, per head, its normalised partial output (fp32) and its partial
+// log2-sum-exp to part_o [splits][T][H][d_v] and part_lse [splits][T][H], which
+// attn_combine_kernel merges.
 __global__ void __launch_bounds__(256, 1)
 attn_bf16_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
                  const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv,
                  const int32_t* __restrict__ idx, int k, float scale, uint16_t* __restrict__ out,
-                 float* __restrict__ lse) {
+                 float* __restrict__ lse, int T, float* __restrict__ part_o,
+                 float* __restrict__ part_lse) {
   __shared__ __attribute__((aligned(1024))) uint8_t buf0[MBUF];
   __shared__ __attribute__((aligned(1024))) uint8_t buf1[MBUF];
   // restart requests: slot (step & 1) holds the id of the last step that asked for one
@@ -347,8 +353,12 @@ attn_bf16_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restr
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int g = lane >> 5, c32 = lane & 31;
   const RowLoc L = locate_row(cu_q, cu_k, B, r);
-  const int32_t* ir = idx + (int64_t)r * k;
-  const int nblk = (k + MBLK - 1) / MBLK;
+  const int split = blockIdx.y, nsplit = gridDim.y;
+  const int nblk_row = (k + MBLK - 1) / MBLK;
+  const int b0 = split * nblk_row / nsplit, b1 = (split + 1) * nblk_row / nsplit;
+  const int32_t* ir = idx + (int64_t)r * k + b0 * MBLK;   // this split's entries
+  const int kk = min(k - b0 * MBLK, (b1 - b0) * MBLK);
+  const int nblk = b1 - b0;
 
   // query block of this wave as B operand: head 32w + c32, dims 16t + 8g .. +8
   bf16x8 qreg[MT];
@@ -365,7 +375,7 @@ attn_bf16_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restr
   // lane l's key of block blk is entry blk*64 + l of the index row
   auto load_idx = [&](int blk) -> int {
     const int j = blk * MBLK + lane;
-    return (blk < nblk && j < k) ? ir[j] : -1;
+    return (blk < nblk && j < kk) ? ir[j] : -1;
   };
   // the sequence's latent rows as a buffer (byte offsets fit 32 bits: n * 1152 < 2^31 is checked
   // on the host); out-of-range offsets would read as zero
@@ -433,6 +443,21 @@ attn_bf16_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restr
   const float ltot = st.l + __shfl_xor(st.l, 32);
   const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
   const int head = 32 * wave + c32;
+  if (nsplit > 1) {
+    const int64_t rh = ((int64_t)split * T + r) * MH + head;
+    float* po = part_o + rh * MDV;
+#pragma unroll
+    for (int vt = 0; vt < MDV / 32; ++vt) {
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4)
+        *reinterpret_cast<float4*>(po + 32 * vt + 8 * i4 + 4 * g) =
+            make_float4(acc_o[vt][4 * i4] * inv, acc_o[vt][4 * i4 + 1] * inv, acc_o[vt][4 * i4 + 2] * inv,
+                        acc_o[vt][4 * i4 + 3] * inv);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (g == 0) part_lse[rh] = ltot > 0.f ? st.m + __log2f(ltot) : -INFINITY;
+    return;
+  }
   uint16_t* orow = out + ((int64_t)r * MH + head) * MDV;
 #pragma unroll
   for (int vt = 0; vt < MDV / 32; ++vt) {
@@ -452,14 +477,72 @@ attn_bf16_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restr
     lse[(int64_t)r * MH + head] = ltot > 0.f ? (st.m + __log2f(ltot)) * 0.6931471805599453f : -INFINITY;
 }
 
-size_t attn_workspace_bytes(const SeqInfo&, int, int, int, int, bool) { return 0; }
+// Merges the splits of one (row, head) per wave: with M the largest partial log2-sum-exp, split
+// s weighs 2^(lse_s - M); out = sum of weighted partial outputs / sum of weights, lse = M +
+// log2(sum of weights) (natural log on output). Splits without a valid entry have weight 0; a
+// row without any gives out = 0, lse = -inf.
+__global__ void __launch_bounds__(256)
+attn_combine_kernel(int T, int nsplit, const float* __restrict__ part_o,
+                    const float* __restrict__ part_lse, uint16_t* __restrict__ out,
+                    float* __restrict__ lse) {
+  const int lane = threadIdx.x & 63;
+  const int64_t rh = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // row * H + head
+  if (rh >= (int64_t)T * MH) return;
+  const int64_t stride = (int64_t)T * MH;
+  float M = -INFINITY;
+  for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, part_lse[sp * stride + rh]);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.f;
+  if (M != -INFINITY) {
+    for (int sp = 0; sp < nsplit; ++sp) {
+      const float ls = part_lse[sp * stride + rh];
+      if (ls == -INFINITY) continue;
+      const float w = __builtin_amdgcn_exp2f(ls - M);
+      wsum += w;
+      const float4* po = reinterpret_cast<const float4*>(part_o + (sp * stride + rh) * MDV + 8 * lane);
+      const float4 a = po[0], b = po[1];
+      acc[0] += w * a.x; acc[1] += w * a.y; acc[2] += w * a.z; acc[3] += w * a.w;
+      acc[4] += w * b.x; acc[5] += w * b.y; acc[6] += w * b.z; acc[7] += w * b.w;
+    }
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  uint4 pk;
+  pk.x = (uint32_t)f32_to_bf16_rne(acc[0] * inv) | ((uint32_t)f32_to_bf16_rne(acc[1] * inv) << 16);
+  pk.y = (uint32_t)f32_to_bf16_rne(acc[2] * inv) | ((uint32_t)f32_to_bf16_rne(acc[3] * inv) << 16);
+  pk.z = (uint32_t)f32_to_bf16_rne(acc[4] * inv) | ((uint32_t)f32_to_bf16_rne(acc[5] * inv) << 16);
+  pk.w = (uint32_t)f32_to_bf16_rne(acc[6] * inv) | ((uint32_t)f32_to_bf16_rne(acc[7] * inv) << 16);
+  *reinterpret_cast<uint4*>(out + rh * MDV + 8 * lane) = pk;
+  if (lse && lane == 0) lse[rh] = wsum > 0.f ? (M + __log2f(wsum)) * 0.6931471805599453f : -INFINITY;
+}
+
+// Splits of each row's index list: batches with fewer rows than compute units (decode) split
+// every row into up to 32 runs of whole blocks so that each compute unit gets a workgroup.
+int attn_splits(const SeqInfo& s, int k) {
+  const int nblk = (k + MBLK - 1) / MBLK;
+  const int cus = device_cu_count();
+  if (s.T <= 0 || s.T >= cus) return 1;
+  return max(1, min(min(nblk, 32), cus / s.T));
+}
+
+size_t attn_workspace_bytes(const SeqInfo& s, int, int, int, int k, bool bf16) {
+  if (!bf16) return 0;
+  const int ns = attn_splits(s, k);
+  return ns > 1 ? (size_t)ns * s.T * MH * (MDV + 1) * sizeof(float) : 0;
+}
 
 hipError_t launch_attn_bf16(const SeqInfo& s, const uint16_t* q, const uint16_t* kv,
                             const int32_t* idx, int k, float scale, uint16_t* out, float* lse,
-                            void*, size_t, hipStream_t st) {
+                            void* ws, size_t, hipStream_t st) {
   if (s.T == 0) return hipSuccess;
-  hipLaunchKernelGGL(attn_bf16_kernel, dim3(s.T), dim3(256), 0, st, s.B, s.cu_q, s.cu_k, q,
-                     reinterpret_cast<const uint8_t*>(kv), idx, k, scale, out, lse);
+  const int ns = attn_splits(s, k);
+  float* part_o = ns > 1 ? static_cast<float*>(ws) : nullptr;
+  float* part_lse = ns > 1 ? part_o + (size_t)ns * s.T * MH * MDV : nullptr;
+  hipLaunchKernelGGL(attn_bf16_kernel, dim3(s.T, ns), dim3(256), 0, st, s.B, s.cu_q, s.cu_k, q,
+                     reinterpret_cast<const uint8_t*>(kv), idx, k, scale, out, lse, s.T, part_o,
+                     part_lse);
+  if (ns > 1)
+    hipLaunchKernelGGL(attn_combine_kernel, dim3((s.T * MH + 3) / 4), dim3(256), 0, st, s.T, ns,
+                       part_o, part_lse, out, lse);
   return hipGetLastError();
 }
 
