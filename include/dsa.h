@@ -138,9 +138,9 @@ dsa_status_t dsa_topk(const dsa_seqs_t* seqs, const float* scores, int64_t ld_sc
  *   ws       device workspace of at least dsa_sparse_mla_attn_workspace_size(...) bytes, 16-byte
  *            aligned (may be NULL when that size is 0); contents on entry do not matter. The bf16
  *            path splits each row's index list over several workgroups when the batch has fewer
- *            rows than the device has compute units, and keeps the per-split partial outputs and
- *            log-sum-exps there (splits * T * H * (d_v + 1) * 4 bytes); the size depends on the
- *            current device's compute unit count.
+ *            rows than the device has compute units, and keeps the per-split partial outputs
+ *            (bf16) and log-sum-exps (fp32) there (splits * T * H * (2 d_v + 4) bytes); the size
+ *            depends on the current device's compute unit count.
  */
 size_t dsa_sparse_mla_attn_workspace_size(const dsa_seqs_t* seqs, int32_t H, int32_t d_qk,
                                           int32_t d_v, int32_t k, dsa_dtype_t dtype);

@@ -335,14 +335,14 @@ __device__ __forceinline__ bool attend_block(const uint8_t* buf, uint64_t vmask,
 
 // One workgroup per (query row, split of its index list): the row's entries are split into
 // gridDim.y runs of whole blocks. With one split the workgroup writes the normalised output and
-// lse; with several it writes, per head, its normalised partial output (fp32) and its partial
-// log2-sum-exp to part_o [splits][T][H][d_v] and part_lse [splits][T][H], which
+// lse; with several it writes, per head, its normalised partial output (bf16) and its partial
+// log2-sum-exp to part_o [splits][T][H][d_v] (bf16) and part_lse [splits][T][H] (fp32), which
 // attn_combine_kernel merges.
 __global__ void __launch_bounds__(256, 1)
 attn_bf16_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
                  const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv,
                  const int32_t* __restrict__ idx, int k, float scale, uint16_t* __restrict__ out,
-                 float* __restrict__ lse, int T, float* __restrict__ part_o,
+                 float* __restrict__ lse, int T, uint16_t* __restrict__ part_o,
                  float* __restrict__ part_lse) {
   __shared__ __attribute__((aligned(1024))) uint8_t buf0[MBUF];
   __shared__ __attribute__((aligned(1024))) uint8_t buf1[MBUF];
@@ -445,14 +445,18 @@ attn_bf16_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restr
   const int head = 32 * wave + c32;
   if (nsplit > 1) {
     const int64_t rh = ((int64_t)split * T + r) * MH + head;
-    float* po = part_o + rh * MDV;
+    uint16_t* po = part_o + rh * MDV;
 #pragma unroll
     for (int vt = 0; vt < MDV / 32; ++vt) {
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4)
-        *reinterpret_cast<float4*>(po + 32 * vt + 8 * i4 + 4 * g) =
-            make_float4(acc_o[vt][4 * i4] * inv, acc_o[vt][4 * i4 + 1] * inv, acc_o[vt][4 * i4 + 2] * inv,
-                        acc_o[vt][4 * i4 + 3] * inv);
+      for (int i4 = 0; i4 < 4; ++i4) {
+        uint2 pk;
+        pk.x = (uint32_t)f32_to_bf16_rne(acc_o[vt][4 * i4 + 0] * inv) |
+               ((uint32_t)f32_to_bf16_rne(acc_o[vt][4 * i4 + 1] * inv) << 16);
+        pk.y = (uint32_t)f32_to_bf16_rne(acc_o[vt][4 * i4 + 2] * inv) |
+               ((uint32_t)f32_to_bf16_rne(acc_o[vt][4 * i4 + 3] * inv) << 16);
+        *reinterpret_cast<uint2*>(po + 32 * vt + 8 * i4 + 4 * g) = pk;
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
     if (g == 0) part_lse[rh] = ltot > 0.f ? st.m + __log2f(ltot) : -INFINITY;
@@ -482,7 +486,7 @@ attn_bf16_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restr
 // log2(sum of weights) (natural log on output). Splits without a valid entry have weight 0; a
 // row without any gives out = 0, lse = -inf.
 __global__ void __launch_bounds__(256)
-attn_combine_kernel(int T, int nsplit, const float* __restrict__ part_o,
+attn_combine_kernel(int T, int nsplit, const uint16_t* __restrict__ part_o,
                     const float* __restrict__ part_lse, uint16_t* __restrict__ out,
                     float* __restrict__ lse) {
   const int lane = threadIdx.x & 63;
@@ -499,10 +503,13 @@ attn_combine_kernel(int T, int nsplit, const float* __restrict__ part_o,
       if (ls == -INFINITY) continue;
       const float w = __builtin_amdgcn_exp2f(ls - M);
       wsum += w;
-      const float4* po = reinterpret_cast<const float4*>(part_o + (sp * stride + rh) * MDV + 8 * lane);
-      const float4 a = po[0], b = po[1];
-      acc[0] += w * a.x; acc[1] += w * a.y; acc[2] += w * a.z; acc[3] += w * a.w;
-      acc[4] += w * b.x; acc[5] += w * b.y; acc[6] += w * b.z; acc[7] += w * b.w;
+      const uint4 pk = *reinterpret_cast<const uint4*>(part_o + (sp * stride + rh) * MDV + 8 * lane);
+      const uint32_t wd[4] = {pk.x, pk.y, pk.z, pk.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[2 * j] += w * __uint_as_float(wd[j] << 16);
+        acc[2 * j + 1] += w * __uint_as_float(wd[j] & 0xFFFF0000u);
+      }
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
@@ -527,7 +534,7 @@ int attn_splits(const SeqInfo& s, int k) {
 size_t attn_workspace_bytes(const SeqInfo& s, int, int, int, int k, bool bf16) {
   if (!bf16) return 0;
   const int ns = attn_splits(s, k);
-  return ns > 1 ? (size_t)ns * s.T * MH * (MDV + 1) * sizeof(float) : 0;
+  return ns > 1 ? (size_t)ns * s.T * MH * (MDV * sizeof(uint16_t) + sizeof(float)) : 0;
 }
 
 hipError_t launch_attn_bf16(const SeqInfo& s, const uint16_t* q, const uint16_t* kv,
@@ -535,8 +542,8 @@ hipError_t launch_attn_bf16(const SeqInfo& s, const uint16_t* q, const uint16_t*
                             void* ws, size_t, hipStream_t st) {
   if (s.T == 0) return hipSuccess;
   const int ns = attn_splits(s, k);
-  float* part_o = ns > 1 ? static_cast<float*>(ws) : nullptr;
-  float* part_lse = ns > 1 ? part_o + (size_t)ns * s.T * MH * MDV : nullptr;
+  uint16_t* part_o = ns > 1 ? static_cast<uint16_t*>(ws) : nullptr;
+  float* part_lse = ns > 1 ? reinterpret_cast<float*>(part_o + (size_t)ns * s.T * MH * MDV) : nullptr;
   hipLaunchKernelGGL(attn_bf16_kernel, dim3(s.T, ns), dim3(256), 0, st, s.B, s.cu_q, s.cu_k, q,
                      reinterpret_cast<const uint8_t*>(kv), idx, k, scale, out, lse, s.T, part_o,
                      part_lse);
