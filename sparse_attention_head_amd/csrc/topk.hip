@@ -27,40 +27,45 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
   return (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
 }
 
-// Finds the bin holding the need-th largest key among the counted ones (suffix sums from the
-// top bin down). Called by all threads; wave 0 does the work: lane l sums bins l*per ..
-// l*per + per - 1 (per <= 64), a suffix scan across lanes finds the lane whose run holds the
-// need-th largest key, and a second scan over that run's bins (one bin per lane) finds the bin.
+// Inclusive prefix sum over the 64 lanes of a wave: four shifts within each row of 16 lanes,
+// then each row's total broadcast into the rows above it (GCN data-parallel primitives).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xF, 0xF, false);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xF, 0xF, false);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xF, 0xF, false);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xF, 0xF, false);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x142, 0xA, 0xF, false);   // row_bcast:15 -> rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0u, x, 0x143, 0xC, 0xF, false);   // row_bcast:31 -> rows 2, 3
+  return x;
+}
+
+// Finds the bin holding the need-th largest key among the counted ones (nb bins, a power of two
+// <= 2048; suffix sums from the top bin down). Called by all threads; wave 0 does the work: lane l
+// sums bins l*per .. l*per + per - 1 (read in a lane-rotated order, which spreads the lanes over
+// the banks), suffix sums across lanes (total minus a prefix scan) find the lane whose run holds
+// the need-th largest key, and a second scan over that run's bins (one bin per lane) finds the
+// bin.
 __device__ __forceinline__ void select_bin(const uint32_t* hist, int nb, uint32_t need,
                                            uint32_t* s_digit, uint32_t* s_above) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (wave == 0) {
-    const int per = (nb + 63) / 64;
+    const int per = nb >= 64 ? nb >> 6 : 1;
     uint32_t sum = 0;
-    for (int j = 0; j < per; ++j) {
-      const int bin = lane * per + j;
-      sum += bin < nb ? hist[bin] : 0u;
-    }
-    uint32_t suf = sum;   // bins of this lane and above
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint32_t t = __shfl_down(suf, off);
-      if (lane + off < 64) suf += t;
-    }
+    if (lane * per < nb)
+      for (int j = 0; j < per; ++j) sum += hist[lane * per + ((j + lane) & (per - 1))];
+    const uint32_t pre = wave_incl_scan(sum);
+    const uint32_t total = __builtin_amdgcn_readlane(pre, 63);
+    const uint32_t suf = total - pre + sum;   // bins of this lane and above
     const uint32_t above_lane = suf - sum;
     // the crossing lane: its run holds the need-th largest key
     const uint64_t hit = __ballot(suf >= need && above_lane < need);
     const int cl = __builtin_amdgcn_readfirstlane(hit ? (int)(__ffsll((unsigned long long)hit) - 1) : 0);
-    const uint32_t above = __builtin_amdgcn_readfirstlane(__shfl(above_lane, cl));
+    const uint32_t above = __builtin_amdgcn_readlane(above_lane, cl);
     // bins of that run, one per lane (lane j: bin cl*per + j), suffix sums within the run
     const int bin = cl * per + lane;
     const uint32_t h = (lane < per && bin < nb) ? hist[bin] : 0u;
-    uint32_t rs = h;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint32_t t = __shfl_down(rs, off);
-      if (lane + off < 64) rs += t;
-    }
+    const uint32_t pre2 = wave_incl_scan(h);
+    const uint32_t rs = __builtin_amdgcn_readlane(pre2, 63) - pre2 + h;
     // the bin: above + (bins of the run above it) < need <= above + rs
     const uint64_t hb = __ballot(lane < per && above + rs >= need && above + rs - h < need);
     if (hb && lane == (int)(__ffsll((unsigned long long)hb) - 1)) {
@@ -563,18 +568,21 @@ __device__ __forceinline__ float max4(float4 v) {
   return r;
 }
 
-// Radix select over `count` keys in LDS, `passes` digits (11, 11, 10 bits) from the top: the
-// key prefix of the want-th largest key (the key itself after 3 passes) and how many of the keys
+// Radix select over `count` keys in LDS that all share `prefix` on the bits of `pmask`: digits of
+// at most 11 bits resolve key bits hi..lo, most significant first. Returns the key prefix of the
+// want-th largest key (bits below lo zero; the key itself when lo = 0) and how many of the keys
 // with that prefix rank within the first `want` (*need_out). hist: 2048 words.
 __device__ __forceinline__ uint32_t lds_select(const uint32_t* keys, uint32_t count, uint32_t want,
-                                               int passes, uint32_t* hist, uint32_t* s_digit,
+                                               int hi, int lo, uint32_t prefix, uint32_t pmask,
+                                               uint32_t* hist, uint32_t* s_digit,
                                                uint32_t* s_above, uint32_t* need_out) {
   const int tid = threadIdx.x;
-  uint32_t prefix = 0, pmask = 0, need = want;
+  uint32_t need = want;
 #pragma unroll 1
-  for (int pass = 0; pass < passes; ++pass) {
-    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-    const int nb = pass == 2 ? 1024 : 2048;
+  for (int top = hi; top >= lo;) {
+    const int width = min(11, top - lo + 1);
+    const int shift = top + 1 - width;
+    const int nb = 1 << width;
     for (int i = tid; i < nb; i += TS_THREADS) hist[i] = 0;
     __syncthreads();
     for (uint32_t c = tid; c < count; c += TS_THREADS) {
@@ -586,9 +594,22 @@ __device__ __forceinline__ uint32_t lds_select(const uint32_t* keys, uint32_t co
     prefix |= *s_digit << shift;
     pmask |= (uint32_t)(nb - 1) << shift;
     need -= *s_above;
+    top = shift - 1;
   }
   *need_out = need;
   return prefix;
+}
+
+// Largest value over the wave (prefix maximum with the same data-parallel steps as
+// wave_incl_scan, read from the last lane).
+__device__ __forceinline__ uint32_t wave_max(uint32_t x) {
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0u, x, 0x111, 0xF, 0xF, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0u, x, 0x112, 0xF, 0xF, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0u, x, 0x114, 0xF, 0xF, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0u, x, 0x118, 0xF, 0xF, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0u, x, 0x142, 0xA, 0xF, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0u, x, 0x143, 0xC, 0xF, false));
+  return __builtin_amdgcn_readlane(x, 63);
 }
 
 __global__ void __launch_bounds__(TS_THREADS)
@@ -597,7 +618,7 @@ topk_stream_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __res
   __shared__ uint32_t hist[2048];          // histograms; tied positions at the end
   __shared__ __attribute__((aligned(16))) uint32_t region[TS_REGION];
   __shared__ uint32_t xch[2][TS_WAVES][2];
-  __shared__ uint32_t s_digit, s_above, s_count, s_eq;
+  __shared__ uint32_t s_digit, s_above, s_count, s_eq, s_max;
   uint32_t* const ckey = region;
   uint32_t* const cpos = region + TS_HCAP;
   uint32_t* const bmap = region + 2 * TS_HCAP;
@@ -632,12 +653,13 @@ topk_stream_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __res
   if (tid == 0) {
     s_count = 0;
     s_eq = 0;
+    s_max = 0;
   }
   __syncthreads();
   const uint32_t want = whole ? (uint32_t)k
                               : (uint32_t)max<int64_t>(1, min<int64_t>(S, (13 * (int64_t)k * S + 10 * (int64_t)n - 1) / (10 * (int64_t)n)));
   uint32_t unused;
-  const uint32_t F = lds_select(region, (uint32_t)S, want, 2, hist, &s_digit, &s_above, &unused);
+  const uint32_t F = lds_select(region, (uint32_t)S, want, 31, 10, 0u, 0u, hist, &s_digit, &s_above, &unused);
   __syncthreads();   // every thread has F before the group arrays overwrite the sample
 
   // 2. stream. Scores are compared as floats: the order-preserving key map is monotone and folds
@@ -753,23 +775,34 @@ topk_stream_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __res
     topk_row_exact<TS_THREADS>(row, n, k, out, hist, xch, &s_digit, &s_above);
     return;
   }
+  uint32_t kmax = 0u;   // largest key of the thread's hits (ordered keys are >= 0)
 #pragma unroll
   for (int j = 0; j < TS_GPT; ++j) {
     const float e[4] = {gv[j].x, gv[j].y, gv[j].z, gv[j].w};
 #pragma unroll
     for (int c = 0; c < 4; ++c)
       if (e[c] >= Ff) {
-        ckey[at] = float_to_ordered(e[c]);
+        const uint32_t u = float_to_ordered(e[c]);
+        ckey[at] = u;
         cpos[at] = gp[j] + (uint32_t)c;
+        kmax = max(kmax, u);
         ++at;
       }
   }
+  kmax = wave_max(kmax);
+  if (lane == 0) atomicMax(&s_max, kmax);
   for (int i = tid; i < nw; i += TS_THREADS) bmap[i] = 0;
   __syncthreads();
 
   // 5. radix select over the list; keys above T go to the bitmap, tied positions to a list
   uint32_t need;
-  const uint32_t T = lds_select(ckey, total, (uint32_t)k, 3, hist, &s_digit, &s_above, &need);
+  // every key lies in [F, M]: the bits above the highest one where F and M differ are common, and
+  // the digits start below them
+  const uint32_t M = s_max;
+  const int h = (M == F) ? -1 : 31 - __clz(M ^ F);
+  const uint32_t common = h < 0 ? 0xFFFFFFFFu : ~((2u << h) - 1u);   // h = 31: no common bits
+  const uint32_t T = lds_select(ckey, total, (uint32_t)k, h, 0, F & common, common, hist, &s_digit,
+                                &s_above, &need);
   __syncthreads();   // the histogram space is reused for the tied positions
   for (uint32_t c = tid; c < total; c += TS_THREADS) {
     const uint32_t u = ckey[c], p = cpos[c];
@@ -790,7 +823,7 @@ topk_stream_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __res
   uint32_t cut = 0u;
   if (eqc > need) {
     uint32_t unused2;
-    cut = lds_select(hist, eqc, need, 3, ckey, &s_digit, &s_above, &unused2);   // ckey is free now
+    cut = lds_select(hist, eqc, need, 31, 0, 0u, 0u, ckey, &s_digit, &s_above, &unused2);   // ckey is free now
   }
   for (uint32_t e = tid; e < eqc; e += TS_THREADS) {
     const uint32_t ip = hist[e];
