@@ -12,6 +12,7 @@ shared latent row of d_qk dims whose first d_v dims are the value):
   decode32k 64 sequences, one query each at position 32767 over 32768 cached entries.
   chunk128k 4096 query rows at positions 126976..131071 of one sequence of 131072 keys.
   ragged    128 single-query sequences with context lengths ~ U[4096, 131072] (seeded).
+  short2k   one causal sequence L=2048 with k=2048 (every row selects all its candidates).
 
 Value recipe: q^I, k^I, q and the latent rows are N(0,1); w is N(0,1)/sqrt(H_I). FP8 and bf16
 tensors are produced by rounding the fp32 draws to nearest-even (torch's host cast). The
@@ -113,10 +114,12 @@ def workload(name: str, seed: int = 0) -> Workload:
         return Workload(name, 3, [4096], [131072], **big)
     if name == "ragged":
         return Workload(name, 4, [1] * 128, _ragged_lengths(seed, 4, 128, 4096, 131072), **big)
+    if name == "short2k":
+        return Workload(name, 5, [2048], [2048], **big)
     raise KeyError(name)
 
 
-WORKLOADS = ("tiny", "prefill8k", "decode32k", "chunk128k", "ragged")
+WORKLOADS = ("tiny", "prefill8k", "decode32k", "chunk128k", "ragged", "short2k")
 
 
 def custom(name="custom", seqlens_q=(64,), seqlens_k=(64,), H_I=4, d_I=32, k=16, H=8, d_qk=80,

@@ -334,10 +334,11 @@ __device__ __forceinline__ bool attend_block(const uint8_t* buf, uint64_t vmask,
 }
 
 // One workgroup per (query row, split of its index list): the row's entries are split into
-// gridDim.y runs of whole blocks. With one split the workgroup writes the normalised output and
-// lse; with several it writes, per head, its normalised partial output (bf16) and its partial
-// log2-sum-exp to part_o [splits][T][H][d_v] (bf16) and part_lse [splits][T][H] (fp32), which
-// attn_combine_kernel merges.
+// gridDim.y runs of whole blocks. A null idx stands for the list 0, 1, ..., pos, -1, ... (every
+// causal candidate: the selection when a sequence has at most k keys). With one split the
+// workgroup writes the normalised output and lse; with several it writes, per head, its
+// normalised partial output and its partial log2-sum-exp to part_o [splits][T][H][d_v] (bf16)
+// and part_lse [splits][T][H] (fp32), which attn_combine_kernel merges.
 __global__ void __launch_bounds__(256, 1)
 attn_bf16_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
                  const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv,
@@ -356,7 +357,8 @@ attn_bf16_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restr
   const int split = blockIdx.y, nsplit = gridDim.y;
   const int nblk_row = (k + MBLK - 1) / MBLK;
   const int b0 = split * nblk_row / nsplit, b1 = (split + 1) * nblk_row / nsplit;
-  const int32_t* ir = idx + (int64_t)r * k + b0 * MBLK;   // this split's entries
+  // this split's entries; without an index list, entry e of the row is candidate e (e <= pos)
+  const int32_t* ir = idx ? idx + (int64_t)r * k + b0 * MBLK : nullptr;
   const int kk = min(k - b0 * MBLK, (b1 - b0) * MBLK);
   const int nblk = b1 - b0;
 
@@ -375,7 +377,10 @@ attn_bf16_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restr
   // lane l's key of block blk is entry blk*64 + l of the index row
   auto load_idx = [&](int blk) -> int {
     const int j = blk * MBLK + lane;
-    return (blk < nblk && j < kk) ? ir[j] : -1;
+    if (blk >= nblk || j >= kk) return -1;
+    if (ir) return ir[j];
+    const int e = b0 * MBLK + j;
+    return e <= L.pos ? e : -1;
   };
   // the sequence's latent rows as a buffer (byte offsets fit 32 bits: n * 1152 < 2^31 is checked
   // on the host); out-of-range offsets would read as zero

@@ -175,6 +175,7 @@ dsa_status_t run_attn(const dsa::SeqInfo& s, int32_t H, int32_t d_qk, int32_t d_
 
 struct ForwardPlan {
   int64_t ld;
+  bool dense, run_indexer, implicit_idx, run_topk;
   size_t index_off, index_bytes;
   size_t scores_off, scores_bytes;
   size_t idx_off, idx_bytes;
@@ -187,17 +188,24 @@ ForwardPlan plan_forward(const dsa::SeqInfo& s, const dsa_forward_args_t* a) {
   ForwardPlan p{};
   p.ld = ((int64_t)s.max_n + 3) / 4 * 4;
   if (p.ld == 0) p.ld = 4;
+  // Short contexts: with at most k keys per sequence every row selects all its candidates, so
+  // the scores are only computed when the caller asks for them, and the bf16 attention walks the
+  // candidates without an index list (top-k only runs to fill indices_out, or for the fp32 path).
+  p.dense = s.max_n <= a->k;
+  p.run_indexer = !p.dense || a->scores_out != nullptr;
+  p.implicit_idx = p.dense && a->dtype == DSA_BF16;
+  p.run_topk = !p.implicit_idx || a->indices_out != nullptr;
   size_t off = 0;
-  p.index_bytes = align_up(indexer_ws_bytes(s, a->qk_dtype));
+  p.index_bytes = p.run_indexer ? align_up(indexer_ws_bytes(s, a->qk_dtype)) : 0;
   p.index_off = off;
   off += p.index_bytes;
-  p.scores_bytes = a->scores_out ? 0 : align_up((size_t)s.T * p.ld * sizeof(float));
+  p.scores_bytes = (a->scores_out || p.dense) ? 0 : align_up((size_t)s.T * p.ld * sizeof(float));
   p.scores_off = off;
   off += p.scores_bytes;
-  p.idx_bytes = a->indices_out ? 0 : align_up((size_t)s.T * a->k * sizeof(int32_t));
+  p.idx_bytes = (a->indices_out || !p.run_topk) ? 0 : align_up((size_t)s.T * a->k * sizeof(int32_t));
   p.idx_off = off;
   off += p.idx_bytes;
-  p.topk_bytes = align_up(dsa::topk_workspace_bytes(s, a->k));
+  p.topk_bytes = p.run_topk ? align_up(dsa::topk_workspace_bytes(s, a->k)) : 0;
   p.topk_off = off;
   off += p.topk_bytes;
   p.attn_bytes = align_up(dsa::attn_workspace_bytes(s, a->H, a->d_qk, a->d_v, a->k, a->dtype == DSA_BF16));
@@ -336,18 +344,26 @@ dsa_status_t dsa_forward(const dsa_seqs_t* seqs, const dsa_forward_args_t* a, vo
     return fail(DSA_ERR_ALIGN, "forward workspace must be %zu-byte aligned", kAlign);
   if (s.T == 0) return ok();
   char* base = static_cast<char*>(ws);
-  float* scores = a->scores_out ? a->scores_out : reinterpret_cast<float*>(base + p.scores_off);
-  int32_t* idx = a->indices_out ? a->indices_out : reinterpret_cast<int32_t*>(base + p.idx_off);
+  // (without the indexer, the top-k kernels never read the scores: every row has n <= k)
+  float* scores = a->scores_out ? a->scores_out
+                                : (p.scores_bytes ? reinterpret_cast<float*>(base + p.scores_off) : nullptr);
+  int32_t* idx = a->indices_out ? a->indices_out
+                                : (p.idx_bytes ? reinterpret_cast<int32_t*>(base + p.idx_off) : nullptr);
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  st = run_indexer(s, a->H_I, a->d_I, a->qk_dtype, a->q_idx, a->k_idx, a->w, scores, ld,
-                   base ? base + p.index_off : nullptr, hs);
-  if (st != DSA_OK) return st;
-  st = hip_status(dsa::launch_topk(s, scores, ld, a->k, idx, base ? base + p.topk_off : nullptr,
-                                   p.topk_bytes, hs),
-                  "top-k launch");
-  if (st != DSA_OK) return st;
-  return run_attn(s, a->H, a->d_qk, a->d_v, a->dtype, a->q, a->kv, idx, a->k, a->softmax_scale,
-                  a->out, a->lse, base ? base + p.attn_off : nullptr, p.attn_bytes, hs);
+  if (p.run_indexer) {
+    st = run_indexer(s, a->H_I, a->d_I, a->qk_dtype, a->q_idx, a->k_idx, a->w, scores, ld,
+                     p.index_bytes ? base + p.index_off : nullptr, hs);
+    if (st != DSA_OK) return st;
+  }
+  if (p.run_topk) {
+    st = hip_status(dsa::launch_topk(s, scores, ld, a->k, idx, p.topk_bytes ? base + p.topk_off : nullptr,
+                                     p.topk_bytes, hs),
+                    "top-k launch");
+    if (st != DSA_OK) return st;
+  }
+  return run_attn(s, a->H, a->d_qk, a->d_v, a->dtype, a->q, a->kv, p.implicit_idx ? nullptr : idx,
+                  a->k, a->softmax_scale, a->out, a->lse, p.attn_bytes ? base + p.attn_off : nullptr,
+                  p.attn_bytes, hs);
 }
 
 const char* dsa_status_string(dsa_status_t status) {

@@ -174,6 +174,31 @@ def test_forward_validation_and_workspace(dsa):
     assert dsa._c_fwd(sq.ref, ctypes.byref(a), p, need, None) == dsa.DSA_ERR_SHAPE
 
 
+def test_forward_short_context_workspace(dsa):
+    """With at most k keys per sequence the fused call needs neither scores nor indices: its
+    workspace is the attention's alone, and grows by the indexer's when scores are requested."""
+    sq = FakeSeqs(dsa, [0, 100], [0, 100])
+    keep, p = buf(64)
+    a = dsa._FwdArgs()
+    a.H_I, a.d_I, a.qk_dtype = 64, 128, dsa.DSA_FP8_E4M3
+    a.q_idx = a.k_idx = a.w = p
+    a.k = 128
+    a.H, a.d_qk, a.d_v, a.dtype = 128, 576, 512, dsa.DSA_BF16
+    a.q = a.kv = a.out = a.lse = p
+    a.softmax_scale = 0.04
+    attn = dsa._c_attn_ws(sq.ref, 128, 576, 512, 128, dsa.DSA_BF16)
+    assert dsa._c_fwd_ws(sq.ref, ctypes.byref(a)) == attn
+    a.indices_out = p
+    assert dsa._c_fwd_ws(sq.ref, ctypes.byref(a)) == attn
+    a.scores_out, a.ld_scores_out = p, 100
+    idx_ws = dsa._c_indexer_ws(sq.ref, 64, 128, dsa.DSA_FP8_E4M3)
+    assert idx_ws > 0
+    assert dsa._c_fwd_ws(sq.ref, ctypes.byref(a)) >= attn + idx_ws
+    # one key more than k: the full path with its scores and indices
+    a.k, a.scores_out, a.indices_out = 99, None, None
+    assert dsa._c_fwd_ws(sq.ref, ctypes.byref(a)) >= 100 * 100 * 4 + 100 * 99 * 4
+
+
 def test_last_error_is_descriptive(dsa):
     sq = FakeSeqs(dsa, [0, 10], [0, 5])
     indexer(dsa, sq)

@@ -138,6 +138,37 @@ def test_dense_special_case_bf16(gpu):
     check_rows(wl, x, res, range(wl.T), "normal", DELTA_FP8_MFMA)
 
 
+@pytest.mark.parametrize("shape", [([5, 40, 1], [40, 100, 7], 128), ([1, 1, 1, 1], [100, 2000, 2048, 64], 2048)])
+def test_short_context_forward(gpu, shape):
+    """Every sequence has at most k keys: the fused call skips the indexer and the top-k and walks
+    all causal candidates. Its output must equal, bit for bit, the attention call on the explicit
+    list 0..pos (same kernel arithmetic), and the oracle within the attention bar. The second shape
+    is a decode batch (the rows are split over several workgroups)."""
+    sq_q, sq_k, k = shape
+    wl = dg.custom(name="short", seqlens_q=sq_q, seqlens_k=sq_k, H_I=64, d_I=128, k=k, H=128,
+                   d_qk=576, d_v=512, idx_dtype="fp8", attn_dtype="bf16", wid=33)
+    x = dg.gen_inputs(wl, "normal", seed=7)
+    seqs = gpu.Seqs(wl.cu_seqlens_q, wl.cu_seqlens_k)
+    T = {kk: dev(v) for kk, v in x.items() if kk not in ("cu_seqlens_q", "cu_seqlens_k")}
+    fwd = gpu.Forward(seqs, T["qI"], T["kI"], T["w"], T["q"], T["kv"], wl.k, wl.scale, wl.d_v)
+    fout, flse = fwd()
+    sq = Seqs(wl.cu_seqlens_q, wl.cu_seqlens_k)
+    full = np.full((wl.T, k), -1, np.int32)
+    for r in range(wl.T):
+        _, pos, _, _ = sq.locate(r)
+        full[r, :pos + 1] = np.arange(pos + 1)
+    out, lse = gpu.sparse_mla_attn(seqs, T["q"], T["kv"], dev(full), wl.scale, wl.d_v)
+    torch.cuda.synchronize()
+    fo, o = to_np_bf16(fout), to_np_bf16(out)
+    assert np.array_equal(fo, o), "implicit candidate list differs from the explicit one"
+    assert np.array_equal(flse.cpu().numpy(), lse.cpu().numpy())
+    for r in range(wl.T):
+        ref, refl = oracle.attn_row(sq, x["q"], x["kv"], full[r], wl.scale, wl.d_v, r)
+        err = np.abs(oracle.decode(fo[r]) - ref)
+        assert err.max() <= 2e-2 and err.mean() <= 2e-3, f"row {r}: max {err.max()} mean {err.mean()}"
+        assert np.all(np.abs(flse[r].cpu().numpy() - refl) <= 1e-3)
+
+
 def test_indexer_weight_extremes(gpu):
     """Rows whose head weights span the fp32 range (huge, tiny, zero, all negative, a single
     nonzero head): the per-row scaling of the FP8 prefill path's linear term must hold the error
