@@ -153,6 +153,10 @@ dsa_status_t dsa_sparse_mla_attn(const dsa_seqs_t* seqs, int32_t H, int32_t d_qk
  * Runs the three steps above on one stream for prefill and decode batches alike. Scores and
  * indices live in the workspace unless the caller asks for them through scores_out /
  * indices_out (then they are written there and also kept as the intermediate).
+ * Short contexts (max_seqlen_k <= k): every row selects all its causal candidates, so the
+ * indexer runs only when scores_out is given, the top-k only when indices_out is given (or for
+ * the fp32 attention), and the bf16 attention walks the candidates 0..pos directly (the pages'
+ * dense short-context case). The indexer arguments are still validated.
  */
 typedef struct {
   /* indexer */
