@@ -349,7 +349,9 @@ attn_bf16_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restr
   __shared__ __attribute__((aligned(1024))) uint8_t buf1[MBUF];
   // restart requests: slot (step & 1) holds the id of the last step that asked for one
   __shared__ int s_flag[2];
-  const int r = blockIdx.x;
+  // rows from the last: in a causal batch the later rows of a sequence have more candidates, so
+  // the heaviest start first and the short ones fill the tail
+  const int r = (int)gridDim.x - 1 - (int)blockIdx.x;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int g = lane >> 5, c32 = lane & 31;
