@@ -35,7 +35,7 @@ import numpy as np
 CHUNK = 4096
 
 # tensor ids for the counter-based streams
-T_QI, T_KI, T_W, T_Q, T_KV, T_LEN = 0, 1, 2, 3, 4, 5
+T_QI, T_KI, T_W, T_Q, T_KV, T_LEN, T_QS, T_KS = 0, 1, 2, 3, 4, 5, 6, 7
 VARIANTS = {"normal": 0, "int": 1}
 
 
@@ -154,6 +154,10 @@ def _draw(seed, wid, variant, tid, rows, inner, kind, row_lo=0, row_hi=None):
             blk = rng.integers(-3, 3, endpoint=True, size=(hi - lo, inner), dtype=np.int8).astype(np.float32)
         elif kind == "eighths":
             blk = rng.integers(-8, 8, endpoint=True, size=(hi - lo, inner), dtype=np.int8).astype(np.float32) / 8
+        elif kind == "pow2":
+            blk = np.exp2(rng.integers(-1, 1, endpoint=True, size=(hi - lo, inner))).astype(np.float32)
+        elif kind == "logu":
+            blk = np.exp2(rng.uniform(-2.0, 2.0, size=(hi - lo, inner))).astype(np.float32)
         else:
             raise ValueError(kind)
         a, b = max(lo, row_lo), min(hi, row_hi)
@@ -210,3 +214,17 @@ def gen_inputs(wl: Workload, variant: str = "normal", seed: int = 0, parts=("idx
             q, kv = to_bf16_bits(q), to_bf16_bits(kv)
         out.update(q=q, kv=kv)
     return out
+
+
+def gen_scales(wl: Workload, variant: str = "normal", seed: int = 0) -> dict:
+    """Positive scales of the indexer inputs: q_scale [T, H_I] and k_scale [Nk] float32.
+
+    "int" variant: powers of two 1/2, 1, 2 (with the integer inputs every partial sum of a scaled
+    score is a multiple of 1/16 below 2^18, exact in fp32);
+    "normal": 2^U(-2, 2).
+    """
+    v = VARIANTS[variant]
+    kind = "pow2" if variant == "int" else "logu"
+    qs = _draw(seed, wl.wid, v, T_QS, wl.T, wl.H_I, kind)
+    ks = _draw(seed, wl.wid, v, T_KS, wl.Nk, 1, kind).reshape(wl.Nk)
+    return dict(q_scale=np.ascontiguousarray(qs), k_scale=np.ascontiguousarray(ks))

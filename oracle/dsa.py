@@ -62,23 +62,30 @@ class Seqs:
 
 # ------------------------------------------------------------------ step 1: lightning indexer
 
-def indexer_scores_row(seqs: Seqs, qI, kI, w, r: int) -> np.ndarray:
+def indexer_scores_row(seqs: Seqs, qI, kI, w, r: int, q_scale=None, k_scale=None) -> np.ndarray:
     """I[r, s] for s = 0..pos(r) ([digest] Key claims, Eq. 1; [36kr] section 02).
 
     I[r, s] = sum_j w[r, j] * max(0, sum_d qI[r, j, d] * kI[s, d]).
     qI: [T, H_I, d_I], kI: [Nk, d_I] (stored codes or floats), w: [T, H_I] float.
+    Scaled FP8 inputs (a reading: the pages say "FP8" without a scaling scheme): the stored
+    query vector of (r, j) stands for q_scale[r, j] times itself and key s for k_scale[s] times
+    itself; the scores are those of the scaled vectors (q_scale [T, H_I], k_scale [Nk]).
     """
     _, pos, k0, _ = seqs.locate(r)
     q = decode(qI[r])                              # [H_I, d_I]
     keys = decode(kI[k0:k0 + pos + 1])             # [pos+1, d_I]
+    if q_scale is not None:
+        q = q * np.asarray(q_scale[r], np.float64)[:, None]
+    if k_scale is not None:
+        keys = keys * np.asarray(k_scale[k0:k0 + pos + 1], np.float64)[:, None]
     dots = q @ keys.T                              # [H_I, pos+1]
     return decode(w[r]) @ np.maximum(dots, 0.0)    # [pos+1]
 
 
-def indexer_scores(seqs: Seqs, qI, kI, w, rows=None) -> list:
+def indexer_scores(seqs: Seqs, qI, kI, w, rows=None, q_scale=None, k_scale=None) -> list:
     """List of score rows (one float64 array of length pos+1 per requested row)."""
     rows = range(seqs.T) if rows is None else rows
-    return [indexer_scores_row(seqs, qI, kI, w, int(r)) for r in rows]
+    return [indexer_scores_row(seqs, qI, kI, w, int(r), q_scale, k_scale) for r in rows]
 
 
 def indexer_error_bound_row(seqs: Seqs, qI, kI, w, r: int) -> np.ndarray:
@@ -161,13 +168,14 @@ def sparse_mla_attn(seqs: Seqs, q, kv, indices, scale: float, d_v: int, rows=Non
 
 # ------------------------------------------------------------------ composition
 
-def forward_rows(seqs: Seqs, qI, kI, w, q, kv, k: int, scale: float, d_v: int, rows=None):
+def forward_rows(seqs: Seqs, qI, kI, w, q, kv, k: int, scale: float, d_v: int, rows=None,
+                 q_scale=None, k_scale=None):
     """Indexer -> top-k -> attention for the requested rows.
 
     Returns dict(scores=list of rows, indices [R, k], out [R, H, d_v], lse [R, H]).
     """
     rows = list(range(seqs.T)) if rows is None else [int(r) for r in rows]
-    sc = indexer_scores(seqs, qI, kI, w, rows)
+    sc = indexer_scores(seqs, qI, kI, w, rows, q_scale, k_scale)
     idx = topk(sc, k)
     out, lse = sparse_mla_attn(seqs, q, kv, idx, scale, d_v, rows)
     return dict(scores=sc, indices=idx, out=out, lse=lse)

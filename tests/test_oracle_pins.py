@@ -80,7 +80,9 @@ def test_handworked_indexer_and_topk(case):
     qI = np.asarray(case["qI"], np.float64)
     kI = np.asarray(case["kI"], np.float64)
     w = np.asarray(case["w"], np.float64)
-    rows = oracle.indexer_scores(sq, qI, kI, w)
+    qs = np.asarray(case["q_scale"], np.float64) if "q_scale" in case else None
+    ks = np.asarray(case["k_scale"], np.float64) if "k_scale" in case else None
+    rows = oracle.indexer_scores(sq, qI, kI, w, q_scale=qs, k_scale=ks)
     assert len(rows) == len(case["scores"])
     for got, want in zip(rows, case["scores"]):
         assert got.shape[0] == len(want)        # exactly pos+1 candidates
@@ -133,6 +135,37 @@ def test_brute_force_matches_vectorised(variant, seed):
         vo, vl = oracle.attn_row(sq, x["q"], x["kv"], sel, wl.scale, wl.d_v, r)
         assert np.allclose(vo, bo, rtol=1e-12, atol=1e-12)
         assert np.allclose(vl, bl, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_scaled_indexer_brute_force_and_identities(seed):
+    """Scaled inputs: the vectorised oracle equals pure-Python loops over the scaled vectors; unit
+    scales give the unscaled scores exactly; a key scale of 2^m multiplies that key's scores by
+    2^m exactly, and a query scale a_j > 0 equals weights w_j a_j (positive homogeneity of ReLU)."""
+    wl, x = _tiny(seed, "normal")
+    sq = Seqs(wl.cu_seqlens_q, wl.cu_seqlens_k)
+    rng = np.random.default_rng(100 + seed)
+    qs = np.exp2(rng.uniform(-2, 2, size=(wl.T, wl.H_I)))
+    ks = np.exp2(rng.uniform(-2, 2, size=wl.Nk))
+    seq_of, pos_of = wl.row_positions()
+    dq, dk, dw = oracle.decode(x["qI"]), oracle.decode(x["kI"]), oracle.decode(x["w"])
+    for r in range(wl.T):
+        b, pos = int(seq_of[r]), int(pos_of[r])
+        k0 = int(wl.cu_seqlens_k[b])
+        q_sc = (dq[r] * qs[r][:, None]).tolist()
+        k_sc = (dk[k0:k0 + pos + 1] * ks[k0:k0 + pos + 1][:, None]).tolist()
+        bs = brute.indexer_row(q_sc, k_sc, dw[r].tolist())
+        vs = oracle.indexer_scores_row(sq, x["qI"], x["kI"], x["w"], r, qs, ks)
+        assert np.allclose(vs, bs, rtol=1e-12, atol=1e-12)
+        base = oracle.indexer_scores_row(sq, x["qI"], x["kI"], x["w"], r)
+        ones = oracle.indexer_scores_row(sq, x["qI"], x["kI"], x["w"], r, np.ones_like(qs), np.ones_like(ks))
+        assert np.array_equal(ones, base)
+        p2 = np.exp2(rng.integers(-3, 4, size=wl.Nk)).astype(np.float64)
+        scaled = oracle.indexer_scores_row(sq, x["qI"], x["kI"], x["w"], r, None, p2)
+        assert np.array_equal(scaled, base * p2[k0:k0 + pos + 1])
+        folded = oracle.indexer_scores_row(sq, x["qI"], x["kI"], dw * qs, r)
+        viaq = oracle.indexer_scores_row(sq, x["qI"], x["kI"], x["w"], r, qs, None)
+        assert np.allclose(folded, viaq, rtol=1e-12, atol=1e-12)
 
 
 def test_brute_topk_integer_ties():
