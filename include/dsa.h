@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 2
+#define DSA_ABI_VERSION 3
 
 typedef enum {
   DSA_OK = 0,
@@ -99,6 +99,27 @@ dsa_status_t dsa_indexer_scores(const dsa_seqs_t* seqs, int32_t H_I, int32_t d_I
                                 dsa_dtype_t qk_dtype, const void* q_idx, const void* k_idx,
                                 const float* w, float* scores, int64_t ld_scores, void* ws,
                                 size_t ws_bytes, void* stream);
+
+/* Scaled FP8 inputs. The pages give the indexer's inputs as FP8 without saying how they are
+ * scaled; this call takes the common form: q_idx[r, j, :] stands for q_scale[r, j] * q_idx and
+ * k_idx[s, :] for k_scale[s] * k_idx, i.e.
+ *   I[r,s] = sum_j w[r,j] * ReLU((q_scale[r,j] qI[r,j]) . (k_scale[kofs_b + s] kI[kofs_b + s]))
+ *          = k_scale[kofs_b + s] * sum_j (w[r,j] q_scale[r,j]) * ReLU(qI[r,j] . kI[kofs_b + s])
+ * (positive homogeneity of ReLU; the kernels compute the second form).
+ *   q_scale  [T, H_I] fp32 or NULL (all 1); every value positive and finite
+ *   k_scale  [Nk] fp32 or NULL (all 1); every value positive and finite
+ *            (other values give unspecified results; they are device data and not checked)
+ *   ws       at least dsa_indexer_scaled_workspace_size(...) bytes (the unscaled call's
+ *            workspace, then the scaled head weights [T, H_I] fp32), 16-byte aligned.
+ * Other arguments as in dsa_indexer_scores.
+ */
+size_t dsa_indexer_scaled_workspace_size(const dsa_seqs_t* seqs, int32_t H_I, int32_t d_I,
+                                         dsa_dtype_t qk_dtype);
+dsa_status_t dsa_indexer_scores_scaled(const dsa_seqs_t* seqs, int32_t H_I, int32_t d_I,
+                                       dsa_dtype_t qk_dtype, const void* q_idx, const float* q_scale,
+                                       const void* k_idx, const float* k_scale, const float* w,
+                                       float* scores, int64_t ld_scores, void* ws, size_t ws_bytes,
+                                       void* stream);
 
 /* ---------------------------------------------------------------- step 2: top-k selection
  * For each row r: the min(k, pos+1) positions s <= pos with the largest scores[r, s]
@@ -179,6 +200,9 @@ typedef struct {
   float* scores_out;            /* [T, ld_scores_out] or NULL */
   int64_t ld_scores_out;
   int32_t* indices_out;         /* [T, k] or NULL */
+  /* optional scales of the indexer inputs (see dsa_indexer_scores_scaled) */
+  const float* q_idx_scale;     /* [T, H_I] or NULL */
+  const float* k_idx_scale;     /* [Nk] or NULL */
 } dsa_forward_args_t;
 
 size_t dsa_forward_workspace_size(const dsa_seqs_t* seqs, const dsa_forward_args_t* args);

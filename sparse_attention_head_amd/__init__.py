@@ -53,7 +53,8 @@ class _FwdArgs(ctypes.Structure):
                 ("H", ctypes.c_int32), ("d_qk", ctypes.c_int32), ("d_v", ctypes.c_int32),
                 ("dtype", ctypes.c_int), ("q", _vp), ("kv", _vp), ("softmax_scale", ctypes.c_float),
                 ("out", _vp), ("lse", _vp),
-                ("scores_out", _vp), ("ld_scores_out", ctypes.c_int64), ("indices_out", _vp)]
+                ("scores_out", _vp), ("ld_scores_out", ctypes.c_int64), ("indices_out", _vp),
+                ("q_idx_scale", _vp), ("k_idx_scale", _vp)]
 
 
 def _proto(name, res, args):
@@ -68,6 +69,11 @@ _c_indexer_ws = _proto("dsa_indexer_workspace_size", ctypes.c_size_t,
 _c_indexer = _proto("dsa_indexer_scores", ctypes.c_int,
                     [ctypes.POINTER(_Seqs), ctypes.c_int32, ctypes.c_int32, ctypes.c_int, _vp, _vp, _vp,
                      _vp, ctypes.c_int64, _vp, ctypes.c_size_t, _vp])
+_c_indexer_sws = _proto("dsa_indexer_scaled_workspace_size", ctypes.c_size_t,
+                        [ctypes.POINTER(_Seqs), ctypes.c_int32, ctypes.c_int32, ctypes.c_int])
+_c_indexer_s = _proto("dsa_indexer_scores_scaled", ctypes.c_int,
+                      [ctypes.POINTER(_Seqs), ctypes.c_int32, ctypes.c_int32, ctypes.c_int, _vp, _vp, _vp, _vp,
+                       _vp, _vp, ctypes.c_int64, _vp, ctypes.c_size_t, _vp])
 _c_topk_ws = _proto("dsa_topk_workspace_size", ctypes.c_size_t, [ctypes.POINTER(_Seqs), ctypes.c_int32])
 _c_topk = _proto("dsa_topk", ctypes.c_int,
                  [ctypes.POINTER(_Seqs), _vp, ctypes.c_int64, ctypes.c_int32, _vp, _vp, ctypes.c_size_t, _vp])
@@ -84,7 +90,8 @@ _c_status = _proto("dsa_status_string", ctypes.c_char_p, [ctypes.c_int])
 _c_last = _proto("dsa_last_error", ctypes.c_char_p, [])
 _c_abi = _proto("dsa_abi_version", ctypes.c_int32, [])
 
-EXPORTS = ("dsa_indexer_workspace_size", "dsa_indexer_scores", "dsa_topk_workspace_size", "dsa_topk", "dsa_sparse_mla_attn_workspace_size",
+EXPORTS = ("dsa_indexer_workspace_size", "dsa_indexer_scores", "dsa_indexer_scaled_workspace_size",
+           "dsa_indexer_scores_scaled", "dsa_topk_workspace_size", "dsa_topk", "dsa_sparse_mla_attn_workspace_size",
            "dsa_sparse_mla_attn", "dsa_forward_workspace_size", "dsa_forward", "dsa_status_string",
            "dsa_last_error", "dsa_abi_version")
 
@@ -201,6 +208,32 @@ def indexer_scores(seqs: Seqs, q_idx, k_idx, w, scores=None, ws=None, stream=Non
     return scores
 
 
+def indexer_scaled_workspace_size(seqs: Seqs, H_I: int, d_I: int, qk_dtype: int) -> int:
+    cs = seqs.c()
+    return int(_c_indexer_sws(ctypes.byref(cs), H_I, d_I, qk_dtype))
+
+
+def indexer_scores_scaled(seqs: Seqs, q_idx, q_scale, k_idx, k_scale, w, scores=None, ws=None,
+                          stream=None):
+    """Scores of scaled inputs: q_scale [T, H_I] and k_scale [Nk] fp32 (positive) or None."""
+    torch = _torch()
+    H_I, d_I = int(q_idx.shape[1]), int(q_idx.shape[2])
+    if scores is None:
+        scores = torch.empty((seqs.T, scores_ld(seqs.max_n)), dtype=torch.float32, device=q_idx.device)
+    cs = seqs.c()
+    dt = _dtype_code(q_idx)
+    wsz = int(_c_indexer_sws(ctypes.byref(cs), H_I, d_I, dt))
+    if ws is None:
+        ws = torch.empty(max(wsz, 1), dtype=torch.uint8, device=q_idx.device)
+    else:
+        wsz = ws.numel()
+    _check(_c_indexer_s(ctypes.byref(cs), H_I, d_I, dt, _ptr(q_idx), _ptr(q_scale), _ptr(k_idx),
+                        _ptr(k_scale), _ptr(w), _ptr(scores), int(scores.stride(0)), _ptr(ws), wsz,
+                        _stream(stream)),
+           "dsa_indexer_scores_scaled")
+    return scores
+
+
 def topk(seqs: Seqs, scores, k: int, indices=None, stream=None):
     """Top-k positions per row: ascending, ties to the lower position, -1 padded."""
     torch = _torch()
@@ -248,7 +281,7 @@ class Forward:
     """Fused indexer -> top-k -> attention with a reusable workspace (one allocation per shape)."""
 
     def __init__(self, seqs: Seqs, q_idx, k_idx, w, q, kv, k: int, scale: float, d_v: int = None,
-                 keep_scores=False, keep_indices=False, with_lse=True):
+                 keep_scores=False, keep_indices=False, with_lse=True, q_idx_scale=None, k_idx_scale=None):
         torch = _torch()
         self.seqs = seqs
         T, H, d_qk = (int(x) for x in q.shape)
@@ -272,8 +305,10 @@ class Forward:
         a.scores_out = _ptr(self.scores)
         a.ld_scores_out = int(self.scores.stride(0)) if self.scores is not None else 0
         a.indices_out = _ptr(self.indices)
+        a.q_idx_scale, a.k_idx_scale = _ptr(q_idx_scale), _ptr(k_idx_scale)
         self._args = a
-        self._keep = (q_idx, k_idx, w, q, kv)  # keep the inputs alive while the object lives
+        # keep the inputs alive while the object lives
+        self._keep = (q_idx, k_idx, w, q, kv, q_idx_scale, k_idx_scale)
         self._cs = seqs.c()
         wsz = int(_c_fwd_ws(ctypes.byref(self._cs), ctypes.byref(a)))
         self.ws_bytes = wsz

@@ -136,25 +136,37 @@ dsa_status_t check_attn(const dsa::SeqInfo& s, int32_t H, int32_t d_qk, int32_t 
   return ok();
 }
 
-// Bytes of indexer workspace: the FP8 prefill path keeps per-row data of the query side there.
+// Bytes of indexer workspace: the FP8 prefill path keeps per-row data of the query side there;
+// with query scales, the scaled head weights [T, H_I] follow.
 size_t indexer_ws_bytes(const dsa::SeqInfo& s, dsa_dtype_t dt) {
   return (dt == DSA_FP8_E4M3 && s.max_m > 1) ? dsa::indexer_workspace_bytes(s, true) : 0;
 }
+size_t indexer_scaled_ws_bytes(const dsa::SeqInfo& s, int32_t H_I, dsa_dtype_t dt) {
+  return align_up(indexer_ws_bytes(s, dt)) + align_up((size_t)s.T * H_I * sizeof(float));
+}
 
+// qscale [T, H_I] / kscale [Nk]: optional positive scales of the indexer queries and keys.
 dsa_status_t run_indexer(const dsa::SeqInfo& s, int32_t H_I, int32_t d_I, dsa_dtype_t dt,
-                         const void* q, const void* k, const float* w, float* scores, int64_t ld,
-                         void* ws, hipStream_t st) {
+                         const void* q, const float* qscale, const void* k, const float* kscale,
+                         const float* w, float* scores, int64_t ld, void* ws, hipStream_t st) {
   if (s.T == 0) return ok();
   hipError_t e;
+  if (qscale) {   // fold the query scales into the head weights
+    float* weff = reinterpret_cast<float*>(static_cast<char*>(ws) + align_up(indexer_ws_bytes(s, dt)));
+    e = dsa::launch_indexer_scale_weights(s, H_I, w, qscale, weff, st);
+    if (e != hipSuccess) return hip_status(e, "indexer scale launch");
+    w = weff;
+  }
   if (dt == DSA_F32)
     e = dsa::launch_indexer_f32(s, H_I, d_I, static_cast<const float*>(q),
-                                static_cast<const float*>(k), w, scores, ld, st);
+                                static_cast<const float*>(k), w, kscale, scores, ld, st);
   else if (s.max_m == 1)
     e = dsa::launch_indexer_fp8_decode(s, static_cast<const uint8_t*>(q),
-                                       static_cast<const uint8_t*>(k), w, scores, ld, st);
+                                       static_cast<const uint8_t*>(k), w, kscale, scores, ld, st);
   else
     e = dsa::launch_indexer_fp8_prefill(s, static_cast<const uint8_t*>(q),
-                                        static_cast<const uint8_t*>(k), w, scores, ld, ws, st);
+                                        static_cast<const uint8_t*>(k), w, kscale, scores, ld, ws,
+                                        st);
   return hip_status(e, "indexer launch");
 }
 
@@ -196,7 +208,9 @@ ForwardPlan plan_forward(const dsa::SeqInfo& s, const dsa_forward_args_t* a) {
   p.implicit_idx = p.dense && a->dtype == DSA_BF16;
   p.run_topk = !p.implicit_idx || a->indices_out != nullptr;
   size_t off = 0;
-  p.index_bytes = p.run_indexer ? align_up(indexer_ws_bytes(s, a->qk_dtype)) : 0;
+  p.index_bytes = !p.run_indexer ? 0
+                  : (a->q_idx_scale ? indexer_scaled_ws_bytes(s, a->H_I, a->qk_dtype)
+                                    : align_up(indexer_ws_bytes(s, a->qk_dtype)));
   p.index_off = off;
   off += p.index_bytes;
   p.scores_bytes = (a->scores_out || p.dense) ? 0 : align_up((size_t)s.T * p.ld * sizeof(float));
@@ -260,8 +274,36 @@ dsa_status_t dsa_indexer_scores(const dsa_seqs_t* seqs, int32_t H_I, int32_t d_I
   if (need > 0 && (!ws || ws_bytes < need))
     return fail(DSA_ERR_WORKSPACE, "indexer workspace needs %zu bytes, got %zu", need, ws_bytes);
   if (ws && !aligned16(ws)) return fail(DSA_ERR_ALIGN, "workspace must be 16-byte aligned");
-  return run_indexer(s, H_I, d_I, qk_dtype, q_idx, k_idx, w, scores, ld_scores, ws,
+  return run_indexer(s, H_I, d_I, qk_dtype, q_idx, nullptr, k_idx, nullptr, w, scores, ld_scores, ws,
                      static_cast<hipStream_t>(stream));
+}
+
+size_t dsa_indexer_scaled_workspace_size(const dsa_seqs_t* seqs, int32_t H_I, int32_t d_I,
+                                         dsa_dtype_t qk_dtype) {
+  dsa::SeqInfo s;
+  if (check_seqs(seqs, s) != DSA_OK || s.B == 0 || H_I <= 0 || d_I <= 0) return 0;
+  return indexer_scaled_ws_bytes(s, H_I, qk_dtype);
+}
+
+dsa_status_t dsa_indexer_scores_scaled(const dsa_seqs_t* seqs, int32_t H_I, int32_t d_I,
+                                       dsa_dtype_t qk_dtype, const void* q_idx, const float* q_scale,
+                                       const void* k_idx, const float* k_scale, const float* w,
+                                       float* scores, int64_t ld_scores, void* ws, size_t ws_bytes,
+                                       void* stream) {
+  dsa::SeqInfo s;
+  dsa_status_t st = check_seqs(seqs, s);
+  if (st != DSA_OK) return st;
+  if (s.B == 0) return ok();
+  st = check_indexer(s, H_I, d_I, qk_dtype, q_idx, k_idx, w, scores, ld_scores);
+  if (st != DSA_OK) return st;
+  if ((q_scale && !aligned16(q_scale)) || (k_scale && !aligned16(k_scale)))
+    return fail(DSA_ERR_ALIGN, "scale arrays must be 16-byte aligned");
+  const size_t need = indexer_scaled_ws_bytes(s, H_I, qk_dtype);
+  if (s.T > 0 && (!ws || ws_bytes < need))
+    return fail(DSA_ERR_WORKSPACE, "scaled indexer workspace needs %zu bytes, got %zu", need, ws_bytes);
+  if (ws && !aligned16(ws)) return fail(DSA_ERR_ALIGN, "workspace must be 16-byte aligned");
+  return run_indexer(s, H_I, d_I, qk_dtype, q_idx, q_scale, k_idx, k_scale, w, scores, ld_scores,
+                     ws, static_cast<hipStream_t>(stream));
 }
 
 size_t dsa_topk_workspace_size(const dsa_seqs_t* seqs, int32_t k) {
@@ -338,6 +380,8 @@ dsa_status_t dsa_forward(const dsa_seqs_t* seqs, const dsa_forward_args_t* a, vo
   if (st != DSA_OK) return st;
   if (!(a->softmax_scale > 0.f) || a->softmax_scale > 3.0e38f)
     return fail(DSA_ERR_SHAPE, "softmax_scale must be positive and finite (got %g)", a->softmax_scale);
+  if ((a->q_idx_scale && !aligned16(a->q_idx_scale)) || (a->k_idx_scale && !aligned16(a->k_idx_scale)))
+    return fail(DSA_ERR_ALIGN, "scale arrays must be 16-byte aligned");
   if (p.total > 0 && (!ws || ws_bytes < p.total))
     return fail(DSA_ERR_WORKSPACE, "forward workspace needs %zu bytes, got %zu", p.total, ws_bytes);
   if (ws && (reinterpret_cast<uintptr_t>(ws) % kAlign) != 0)
@@ -351,8 +395,8 @@ dsa_status_t dsa_forward(const dsa_seqs_t* seqs, const dsa_forward_args_t* a, vo
                                 : (p.idx_bytes ? reinterpret_cast<int32_t*>(base + p.idx_off) : nullptr);
   hipStream_t hs = static_cast<hipStream_t>(stream);
   if (p.run_indexer) {
-    st = run_indexer(s, a->H_I, a->d_I, a->qk_dtype, a->q_idx, a->k_idx, a->w, scores, ld,
-                     p.index_bytes ? base + p.index_off : nullptr, hs);
+    st = run_indexer(s, a->H_I, a->d_I, a->qk_dtype, a->q_idx, a->q_idx_scale, a->k_idx,
+                     a->k_idx_scale, a->w, scores, ld, p.index_bytes ? base + p.index_off : nullptr, hs);
     if (st != DSA_OK) return st;
   }
   if (p.run_topk) {

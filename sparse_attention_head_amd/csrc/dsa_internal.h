@@ -22,14 +22,20 @@ struct SeqInfo {
 };
 
 // ---------------------------------------------------------------- indexer
+// kscale: per-key scale [Nk] multiplying every score of that key, or NULL.
 hipError_t launch_indexer_f32(const SeqInfo& s, int H_I, int d_I, const float* q, const float* k,
-                              const float* w, float* scores, int64_t ld, hipStream_t st);
+                              const float* w, const float* kscale, float* scores, int64_t ld,
+                              hipStream_t st);
 size_t indexer_workspace_bytes(const SeqInfo& s, bool fp8);
 hipError_t launch_indexer_fp8_prefill(const SeqInfo& s, const uint8_t* q, const uint8_t* k,
-                                      const float* w, float* scores, int64_t ld, void* ws,
-                                      hipStream_t st);
+                                      const float* w, const float* kscale, float* scores,
+                                      int64_t ld, void* ws, hipStream_t st);
 hipError_t launch_indexer_fp8_decode(const SeqInfo& s, const uint8_t* q, const uint8_t* k,
-                                     const float* w, float* scores, int64_t ld, hipStream_t st);
+                                     const float* w, const float* kscale, float* scores,
+                                     int64_t ld, hipStream_t st);
+// weff = w * qscale elementwise ([T, H_I]).
+hipError_t launch_indexer_scale_weights(const SeqInfo& s, int H_I, const float* w, const float* qscale,
+                                        float* weff, hipStream_t st);
 
 // ---------------------------------------------------------------- top-k
 size_t topk_workspace_bytes(const SeqInfo& s, int k);

@@ -37,7 +37,8 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 __global__ void __launch_bounds__(256)
 indexer_f32_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
                    int H_I, int d_I, const float* __restrict__ q, const float* __restrict__ k,
-                   const float* __restrict__ w, float* __restrict__ scores, int64_t ld) {
+                   const float* __restrict__ w, const float* __restrict__ kscale,
+                   float* __restrict__ scores, int64_t ld) {
   extern __shared__ float sm[];  // q row [H_I * d_I], then w row [H_I]
   const int r = blockIdx.x;
   const RowLoc L = locate_row(cu_q, cu_k, B, r);
@@ -57,16 +58,37 @@ indexer_f32_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __res
     for (int d = 0; d < d_I; ++d) dot = fmaf(qs[j * d_I + d], kr[d], dot);
     acc = fmaf(ws[j], fmaxf(dot, 0.f), acc);
   }
+  if (kscale) acc *= kscale[L.kofs + s];   // per-key scale of the keys (positive)
   scores[(int64_t)r * ld + s] = acc;
 }
 
 hipError_t launch_indexer_f32(const SeqInfo& s, int H_I, int d_I, const float* q, const float* k,
-                              const float* w, float* scores, int64_t ld, hipStream_t st) {
+                              const float* w, const float* kscale, float* scores, int64_t ld,
+                              hipStream_t st) {
   if (s.T == 0 || s.max_n == 0) return hipSuccess;
   dim3 grid(s.T, (s.max_n + 255) / 256);
   size_t lds = (size_t)(H_I * d_I + H_I) * sizeof(float);
   hipLaunchKernelGGL(indexer_f32_kernel, grid, dim3(256), lds, st, s.B, s.cu_q, s.cu_k, H_I, d_I,
-                     q, k, w, scores, ld);
+                     q, k, w, kscale, scores, ld);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------- scale factors
+// Per-(row, head) query scales a_rj > 0 fold into the head weights: ReLU(a x) = a ReLU(x), so
+// sum_j w_j ReLU(a_j q_j . k) = sum_j (w_j a_j) ReLU(q_j . k). The kernels then run on w * a.
+__global__ void __launch_bounds__(256)
+indexer_scale_weights_kernel(int64_t count, const float* __restrict__ w, const float* __restrict__ qs,
+                             float* __restrict__ weff) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < count) weff[i] = w[i] * qs[i];
+}
+
+hipError_t launch_indexer_scale_weights(const SeqInfo& s, int H_I, const float* w, const float* qscale,
+                                        float* weff, hipStream_t st) {
+  const int64_t count = (int64_t)s.T * H_I;
+  if (count == 0) return hipSuccess;
+  hipLaunchKernelGGL(indexer_scale_weights_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0,
+                     st, count, w, qscale, weff);
   return hipGetLastError();
 }
 
@@ -131,11 +153,13 @@ __device__ __forceinline__ v8i load_slice(const uint8_t* __restrict__ base, int6
 // Prefill: one workgroup = W waves x RW rows of one sequence against a chunk of KC keys; all waves
 // walk the same keys. Decode (m_b == 1 everywhere): one workgroup = one row and a chunk of keys that
 // the W waves split in interleaved 16-key blocks.
-template <int RW, int W, bool DECODE, int PF>
+// KS: every score is multiplied by the per-key scale kscale[key row] (positive).
+template <int RW, int W, bool DECODE, int PF, bool KS>
 __global__ void __launch_bounds__(W * 64, 2)
 indexer_fp8_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
                    const uint8_t* __restrict__ q, const uint8_t* __restrict__ k,
-                   const float* __restrict__ w, float* __restrict__ scores, int64_t ld, int KC) {
+                   const float* __restrict__ w, const float* __restrict__ kscale,
+                   float* __restrict__ scores, int64_t ld, int KC) {
   constexpr int HPM = 16 / RW;      // heads of one row inside a 16x16 tile
   constexpr int NMF = 4 * RW;       // tiles (MFMAs) per 16-key block
   const int lane = threadIdx.x & 63;
@@ -196,9 +220,12 @@ indexer_fp8_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __res
   const int step = DECODE ? 16 * W : 16;
   const int first = DECODE ? kbeg + 16 * wave : kbeg;
   v8i ring[PF];
+  float kring[PF];   // the lane's key scale, loaded with the key (KS only)
 #pragma unroll
-  for (int p = 0; p < PF; ++p)
+  for (int p = 0; p < PF; ++p) {
     ring[p] = load_slice(k, k0 + min(first + p * step + c, n - 1), g);
+    if (KS) kring[p] = kscale[k0 + min(first + p * step + c, n - 1)];
+  }
 
   for (int kb0 = first; kb0 < kend; kb0 += PF * step) {
 #pragma unroll
@@ -206,6 +233,11 @@ indexer_fp8_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __res
       const int kb = kb0 + p * step;
       const v8i cur = ring[p];
       ring[p] = load_slice(k, k0 + min(kb + PF * step + c, n - 1), g);
+      float kcur = 1.f;
+      if (KS) {
+        kcur = kring[p];
+        kring[p] = kscale[k0 + min(kb + PF * step + c, n - 1)];
+      }
       if (kb < kend) {
         float acc = score_block<RW>(a, cur, wv);
         // keep the epilogue in this block (it would otherwise sink into the store's branch and
@@ -213,6 +245,7 @@ indexer_fp8_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __res
         asm volatile("" ::"v"(acc));
         if (RW <= 2) acc += __shfl_xor(acc, 16);
         if (RW == 1) acc += __shfl_xor(acc, 32);
+        if (KS) acc *= kcur;
         const int s = kb + c;
         const bool owner = (RW == 4) || (RW == 2 ? (g & 1) == 0 : g == 0);
         if (owner && row_ok && s <= my_pos && s < kend) srow[s] = acc;
@@ -353,12 +386,13 @@ struct PipeState {
   int lsc;              // E8M0 column scale of the linear tile
   bool hi2, hi1;
   float* sp;            // this lane's first score of the stage
+  const float* ks;      // this lane's first key scale of the stage (LDS; scaled kernel only)
   v8i key[2];
   v4f d[4];
   float acc[4], red[4], n0, n1, kk, ss;
 };
 
-template <int NB, int T>
+template <int NB, int T, bool KS>
 __device__ __forceinline__ void pipe_step(PipeState& P) {
   constexpr int NM = 17, LAG = 3, TOT = NB * NM;
   if constexpr (T < TOT) {
@@ -404,18 +438,21 @@ __device__ __forceinline__ void pipe_step(PipeState& P) {
   }
   if constexpr (f >= 3 && (f - 3) % NM == 0 && (f - 3) / NM < NB) {
     constexpr int blk = (f - 3) / NM;
-    P.sp[blk * 16] = P.kk + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(P.ss), 0xB1, 0xF, 0xF, true));
+    float v = P.kk + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(P.ss), 0xB1, 0xF, 0xF, true));
+    if constexpr (KS) v *= P.ks[blk * 16];
+    P.sp[blk * 16] = v;
   }
   __builtin_amdgcn_sched_barrier(0);
-  if constexpr (T + 1 < TOT + LAG + 3) pipe_step<NB, T + 1>(P);
+  if constexpr (T + 1 < TOT + LAG + 3) pipe_step<NB, T + 1, KS>(P);
 }
 
-template <int NB>
+template <int NB, bool KS>
 __device__ __forceinline__ void stage_pipeline(const uint8_t* __restrict__ buf, int kb0, int kb1,
                                                const v8i (&qa)[16], const v8i& ql,
                                                const float (&wt)[16], int lsc, bool hi2, bool hi1,
-                                               float* __restrict__ sp) {
+                                               float* __restrict__ sp, const float* ks) {
   PipeState P;
+  P.ks = ks;
   P.buf = buf;
   P.kb0 = kb0;
   P.kb1 = kb1;
@@ -431,7 +468,7 @@ __device__ __forceinline__ void stage_pipeline(const uint8_t* __restrict__ buf, 
     const v4i hi = *reinterpret_cast<const v4i*>(buf + kb1);
     P.key[0] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   }
-  pipe_step<NB, 0>(P);
+  pipe_step<NB, 0, KS>(P);
 }
 
 // Workgroup = 8 waves x 4 rows = 32 query rows of one sequence against a chunk of keys. The keys
@@ -447,14 +484,19 @@ constexpr int PF_RW = 4;                // rows per wave
 constexpr int PF_ROWS = PF_W * PF_RW;   // 32
 constexpr int PF_SK = 256;              // keys per stage
 constexpr int PF_NR = 3;                // stages in the ring
+constexpr int PF_KC_MAX = 8192;         // keys per workgroup (chunk) at most
 
+// KS: every score is multiplied by the per-key scale kscale[key row] (positive); the chunk's
+// scales sit in LDS (32 KB more).
+template <bool KS>
 __global__ void __launch_bounds__(PF_W * 64, 1)
 indexer_fp8_prefill_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
                            const uint8_t* __restrict__ q, const uint8_t* __restrict__ k,
                            const float* __restrict__ w, const uint8_t* __restrict__ lin,
-                           const int32_t* __restrict__ piece_exp, float* __restrict__ scores,
-                           int64_t ld, int KC) {
+                           const int32_t* __restrict__ piece_exp, const float* __restrict__ kscale,
+                           float* __restrict__ scores, int64_t ld, int KC) {
   __shared__ __attribute__((aligned(1024))) uint8_t kst[PF_NR][PF_SK * kDI];
+  __shared__ float ksc[KS ? PF_KC_MAX : 1];
   constexpr int HPM = 4, NMF = 16;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
@@ -478,6 +520,10 @@ indexer_fp8_prefill_kernel(int B, const int32_t* __restrict__ cu_q, const int32_
   // DMA of stage st: 32 instructions of 1 KB (8 keys each), 4 per wave; lane l of instruction i
   // covers key (i*8 + l/8) of the stage, whose 16 mod 16 is 8*(i%2) + l/8, and writes physical
   // chunk l%8, i.e. logical chunk (l%8) ^ key_swz(key % 16).
+  if (KS) {   // the chunk's key scales, before any DMA (the first stage wait is vmcnt(0))
+    for (int i = threadIdx.x; i < kend - kbeg; i += PF_W * 64) ksc[i] = kscale[k0 + kbeg + i];
+    __syncthreads();
+  }
   const int dch0 = ((lane & 7) ^ key_swz(lane >> 3)) * 16;
   const int dch1 = ((lane & 7) ^ key_swz(8 | (lane >> 3))) * 16;
   auto issue = [&](int st) {
@@ -559,14 +605,15 @@ indexer_fp8_prefill_kernel(int B, const int32_t* __restrict__ cu_q, const int32_
     if (fast) {
       // whole stage for 4 valid rows: every score lands below wkend <= n <= ld (keys past a row's
       // own position fall in the part of the row the interface leaves unspecified)
-      stage_pipeline<PF_SK / 16>(buf + c * kDI, bx0, bx1, a, al, wt, lsc, hi2, hi1,
-                                 srow + sbase + kofs);
+      stage_pipeline<PF_SK / 16, KS>(buf + c * kDI, bx0, bx1, a, al, wt, lsc, hi2, hi1,
+                                     srow + sbase + kofs, ksc + (sbase - kbeg) + kofs);
     } else {
       const int nblk = min(PF_SK, wkend - sbase) > 0 ? (min(PF_SK, wkend - sbase) + 15) / 16 : 0;
       for (int blk = 0; blk < nblk; ++blk) {
-        const float acc = score_block_t(a, al, load_b(buf, blk * 16), wt, lsc, hi2, hi1);
+        float acc = score_block_t(a, al, load_b(buf, blk * 16), wt, lsc, hi2, hi1);
         asm volatile("" ::"v"(acc));
         const int s = sbase + blk * 16 + kofs;
+        if (KS) acc *= ksc[min(s - kbeg, KC - 1)];
         if (row_ok && s <= my_pos && s < wkend) srow[s] = acc;
       }
     }
@@ -587,8 +634,8 @@ static int pick_chunk(int64_t tiles, int max_n, int cus, int align) {
 }
 
 hipError_t launch_indexer_fp8_prefill(const SeqInfo& s, const uint8_t* q, const uint8_t* k,
-                                      const float* w, float* scores, int64_t ld, void* ws,
-                                      hipStream_t st) {
+                                      const float* w, const float* kscale, float* scores,
+                                      int64_t ld, void* ws, hipStream_t st) {
   if (s.T == 0 || s.max_n == 0) return hipSuccess;
   uint8_t* pieces = static_cast<uint8_t*>(ws);
   int32_t* piece_exp = reinterpret_cast<int32_t*>(pieces + (size_t)s.T * LIN_BYTES);
@@ -597,19 +644,29 @@ hipError_t launch_indexer_fp8_prefill(const SeqInfo& s, const uint8_t* q, const 
   const int tiles = (s.max_m + PF_ROWS - 1) / PF_ROWS;
   const int kc = pick_chunk((int64_t)tiles * s.B, s.max_n, device_cu_count(), PF_SK);
   dim3 grid(tiles, (s.max_n + kc - 1) / kc, s.B);
-  hipLaunchKernelGGL(indexer_fp8_prefill_kernel, grid, dim3(PF_W * 64), 0, st, s.B, s.cu_q, s.cu_k,
-                     q, k, w, pieces, piece_exp, scores, ld, kc);
+  static_assert(PF_KC_MAX >= 8192, "pick_chunk returns at most 8192 keys");
+  if (kscale)
+    hipLaunchKernelGGL(indexer_fp8_prefill_kernel<true>, grid, dim3(PF_W * 64), 0, st, s.B, s.cu_q,
+                       s.cu_k, q, k, w, pieces, piece_exp, kscale, scores, ld, kc);
+  else
+    hipLaunchKernelGGL(indexer_fp8_prefill_kernel<false>, grid, dim3(PF_W * 64), 0, st, s.B, s.cu_q,
+                       s.cu_k, q, k, w, pieces, piece_exp, kscale, scores, ld, kc);
   return hipGetLastError();
 }
 
 hipError_t launch_indexer_fp8_decode(const SeqInfo& s, const uint8_t* q, const uint8_t* k,
-                                     const float* w, float* scores, int64_t ld, hipStream_t st) {
+                                     const float* w, const float* kscale, float* scores,
+                                     int64_t ld, hipStream_t st) {
   if (s.T == 0 || s.max_n == 0) return hipSuccess;
   constexpr int W = 4;
   const int kc = 2048;
   dim3 grid((s.max_n + kc - 1) / kc, s.B);
-  hipLaunchKernelGGL((indexer_fp8_kernel<1, W, true, 4>), grid, dim3(W * 64), 0, st, s.B, s.cu_q,
-                     s.cu_k, q, k, w, scores, ld, kc);
+  if (kscale)
+    hipLaunchKernelGGL((indexer_fp8_kernel<1, W, true, 4, true>), grid, dim3(W * 64), 0, st, s.B,
+                       s.cu_q, s.cu_k, q, k, w, kscale, scores, ld, kc);
+  else
+    hipLaunchKernelGGL((indexer_fp8_kernel<1, W, true, 4, false>), grid, dim3(W * 64), 0, st, s.B,
+                       s.cu_q, s.cu_k, q, k, w, kscale, scores, ld, kc);
   return hipGetLastError();
 }
 

@@ -36,15 +36,23 @@ def gamma(n):
 DELTA_FP8_MFMA = 2.0 ** -11
 
 
-def score_bound_row(sq: Seqs, qI, kI, w, r, delta):
+def score_bound_row(sq: Seqs, qI, kI, w, r, delta, q_scale=None, k_scale=None):
+    """Bound for one row. With scales, the kernels run on w' = fl(w * q_scale) (one more rounding
+    per weight: at most u * S') and multiply each score by k_scale (one more rounding: u |I|)."""
     _, pos, k0, _ = sq.locate(r)
     q = np.abs(oracle.decode(qI[r]))
     keys = np.abs(oracle.decode(kI[k0:k0 + pos + 1]))
     H_I = q.shape[0]
     wr = oracle.decode(w[r])
+    if q_scale is not None:
+        wr = wr * np.asarray(q_scale[r], np.float64)
     S = np.abs(wr) @ (q @ keys.T)
     u = wr @ oracle.decode(qI[r])
-    return 2.0 * (delta + gamma(H_I + 1)) * S + 2.0 ** -29 * np.max(np.abs(u)) * keys.sum(axis=1)
+    eps = 2.0 * (delta + gamma(H_I + 1)) * S + 2.0 ** -29 * np.max(np.abs(u)) * keys.sum(axis=1)
+    if q_scale is None and k_scale is None:
+        return eps
+    ks = np.ones(pos + 1) if k_scale is None else np.asarray(k_scale[k0:k0 + pos + 1], np.float64)
+    return ks * (eps + 2.0 * U * S) * (1 + 2.0 * U) + 2.0 * U * ks * S
 
 
 def check_topk_row(got, exact_scores, eps, k, pos):

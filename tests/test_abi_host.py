@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(dsa):
 
 
 def test_abi_version_and_status_strings(dsa):
-    assert dsa.abi_version() == 2
+    assert dsa.abi_version() == 3
     for st in range(8):
         s = dsa._c_status(st)
         assert s and len(s) >= 2

@@ -169,6 +169,55 @@ def test_short_context_forward(gpu, shape):
         assert np.all(np.abs(flse[r].cpu().numpy() - refl) <= 1e-3)
 
 
+SCALED = {
+    # name: (seqlens_q, seqlens_k, H_I, d_I, idx dtype, k)
+    "prefill_fp8": ([300, 37], [300, 700], 64, 128, "fp8", 64),
+    "decode_fp8": ([1, 1, 1], [40, 2100, 5000], 64, 128, "fp8", 256),
+    "tiny_f32": ([50], [80], 4, 32, "f32", 16),
+}
+
+
+@pytest.mark.parametrize("sides", ["both", "q", "k"])
+@pytest.mark.parametrize("variant", ["int", "normal"])
+@pytest.mark.parametrize("case", list(SCALED))
+def test_scaled_indexer(gpu, case, variant, sides):
+    """Scaled indexer inputs (per query row and head, per key) against the oracle on the scaled
+    vectors: bit-exact for integer inputs with power-of-two scales, else within the bound; the
+    fused call with the same scales gives the same scores, and (integer case) the oracle's
+    top-k."""
+    sq_q, sq_k, H_I, d_I, idt, k = SCALED[case]
+    wl = dg.custom(name="scaled", seqlens_q=sq_q, seqlens_k=sq_k, H_I=H_I, d_I=d_I, k=k, H=128,
+                   d_qk=576, d_v=512, idx_dtype=idt, attn_dtype="bf16", wid=34)
+    x = dg.gen_inputs(wl, variant, seed=3)
+    sc = dg.gen_scales(wl, variant, seed=3)
+    qs = sc["q_scale"] if sides in ("both", "q") else None
+    ks = sc["k_scale"] if sides in ("both", "k") else None
+    seqs = gpu.Seqs(wl.cu_seqlens_q, wl.cu_seqlens_k)
+    T = {kk: dev(v) for kk, v in x.items() if kk not in ("cu_seqlens_q", "cu_seqlens_k")}
+    dqs = dev(qs) if qs is not None else None
+    dks = dev(ks) if ks is not None else None
+    scores = gpu.indexer_scores_scaled(seqs, T["qI"], dqs, T["kI"], dks, T["w"])
+    fwd = gpu.Forward(seqs, T["qI"], T["kI"], T["w"], T["q"], T["kv"], wl.k, wl.scale, wl.d_v,
+                      keep_scores=True, keep_indices=True, q_idx_scale=dqs, k_idx_scale=dks)
+    fwd()
+    torch.cuda.synchronize()
+    got_all, fs, fi = scores.cpu().numpy(), fwd.scores.cpu().numpy(), fwd.indices.cpu().numpy()
+    sq = Seqs(wl.cu_seqlens_q, wl.cu_seqlens_k)
+    delta = DELTA_FP8_MFMA if idt == "fp8" else gamma(d_I)
+    for r in range(wl.T):
+        _, pos, _, _ = sq.locate(r)
+        ref = oracle.indexer_scores_row(sq, x["qI"], x["kI"], x["w"], r, qs, ks)
+        got = got_all[r, :pos + 1].astype(np.float64)
+        assert np.array_equal(fs[r, :pos + 1], got_all[r, :pos + 1]), f"row {r}: fused scores differ"
+        if variant == "int":
+            assert np.array_equal(got, ref), f"row {r}: scaled scores not bit-exact"
+            assert fi[r].tolist() == oracle.topk_row(ref, wl.k).tolist(), f"row {r}: top-k differs"
+        else:
+            eps = score_bound_row(sq, x["qI"], x["kI"], x["w"], r, delta, qs, ks)
+            bad = np.abs(got - ref) > eps
+            assert not bad.any(), f"row {r}: worst {np.max(np.abs(got - ref) / eps)}"
+
+
 def test_indexer_weight_extremes(gpu):
     """Rows whose head weights span the fp32 range (huge, tiny, zero, all negative, a single
     nonzero head): the per-row scaling of the FP8 prefill path's linear term must hold the error
