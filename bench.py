@@ -110,8 +110,9 @@ def setup(torch, dsa, dg, name, seed=0):
     return wl, x, T, seqs
 
 
-def measure(torch, dsa, wl, T, seqs, steps, warmup):
-    """Fused step time and per-kernel times for one workload."""
+def measure(torch, dsa, wl, T, seqs, steps, warmup, scales=None):
+    """Fused step time and per-kernel times for one workload (and, with `scales`, the indexer on
+    scaled inputs)."""
     fwd = dsa.Forward(seqs, T["qI"], T["kI"], T["w"], T["q"], T["kv"], wl.k, wl.scale, wl.d_v)
     scores = torch.empty((wl.T, dsa.scores_ld(wl.max_seqlen_k)), dtype=torch.float32, device="cuda")
     idx = torch.empty((wl.T, wl.k), dtype=torch.int32, device="cuda")
@@ -130,7 +131,15 @@ def measure(torch, dsa, wl, T, seqs, steps, warmup):
     t_attn = time_loop(torch, lambda: dsa.sparse_mla_attn(seqs, T["q"], T["kv"], idx, wl.scale, wl.d_v,
                                                           out=out, lse=lse, ws=aws), steps, warmup)
     t_fwd = time_loop(torch, fwd, steps, warmup)
-    return dict(fused_ms=t_fwd, indexer_ms=t_idx, topk_ms=t_topk, attn_ms=t_attn)
+    res = dict(fused_ms=t_fwd, indexer_ms=t_idx, topk_ms=t_topk, attn_ms=t_attn)
+    if scales is not None:
+        qs, ks = to_dev(torch, scales["q_scale"]), to_dev(torch, scales["k_scale"])
+        sws_n = dsa.indexer_scaled_workspace_size(seqs, wl.H_I, wl.d_I, dsa._dtype_code(T["qI"]))
+        sws = torch.empty(max(sws_n, 1), dtype=torch.uint8, device="cuda")
+        res["indexer_scaled_ms"] = time_loop(
+            torch, lambda: dsa.indexer_scores_scaled(seqs, T["qI"], qs, T["kI"], ks, T["w"], scores=scores,
+                                                     ws=sws), steps, warmup)
+    return res
 
 
 def cpu_baseline(wl, x, seconds):
@@ -184,7 +193,8 @@ def main():
     wl, x, T, seqs = setup(torch, dsa, dg, args.workload)
     alg = algorithmic(wl)
     log(f"[bench] timing {args.workload}: warmup {args.warmup}, steps {args.steps}")
-    tm = measure(torch, dsa, wl, T, seqs, args.steps, args.warmup)
+    tm = measure(torch, dsa, wl, T, seqs, args.steps, args.warmup,
+                 scales=dg.gen_scales(wl, "normal") if wl.idx_dtype == "fp8" else None)
     log(f"[bench] {args.workload}: {tm}")
 
     prefill = wl.max_seqlen_q > 1
@@ -199,6 +209,9 @@ def main():
         attention=dict(ms=tm["attn_ms"], tflops=attn_tflops, frac_bf16=attn_tflops / PEAK_BF16_TFLOPS,
                        flop=alg["attn_flop"]),
     )
+    if "indexer_scaled_ms" in tm:   # scaled FP8 inputs (per row and head, per key)
+        st = alg["indexer_flop"] / (tm["indexer_scaled_ms"] / 1e3) / 1e12
+        stages["indexer_scaled"] = dict(ms=tm["indexer_scaled_ms"], tflops=st, frac_fp8=st / PEAK_FP8_TFLOPS)
     if prefill:
         roof = dict(kernel="indexer_fp8", bound="mfma", achieved=idx_tflops, peak=PEAK_FP8_TFLOPS,
                     unit="TFLOP/s", frac=idx_tflops / PEAK_FP8_TFLOPS,
