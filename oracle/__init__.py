@@ -16,9 +16,10 @@ fp32 inputs with the oracle's own tables.
 
 Modules:
   numerics  decoding of OCP FP8 e4m3fn codes and bf16 bit patterns (own tables)
-  dsa       the vectorised float64 oracle (indexer, top-k, attention, composition)
+  dsa       the vectorised float64 oracle (indexer, top-k, attention, composition, and the
+            indexer-alignment target with its KL divergence)
   brute     pure-Python loop versions for tiny inputs (cross-check of `dsa`)
 """
 from .numerics import decode, fp8_e4m3fn_table, bf16_bits_to_f64  # noqa: F401
 from .dsa import (Seqs, indexer_scores_row, indexer_scores, topk_row, topk, attn_row,  # noqa: F401
-                  sparse_mla_attn, forward_rows, indexer_error_bound_row)
+                  sparse_mla_attn, forward_rows, indexer_error_bound_row, alignment_row)

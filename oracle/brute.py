@@ -61,3 +61,33 @@ def attn_row(q_r, rows, scale, d_v):
         outs.append(o)
         lses.append(m + math.log(l))
     return outs, lses
+
+
+def alignment_row(q_r, rows, scale, scores_sel):
+    """Head-averaged attention distribution over the given latent rows and its KL divergence from
+    the softmax of the indexer scores of the same rows. Loops and math.exp / math.log only."""
+    n = len(rows)
+    if n == 0:
+        return [], 0.0
+    H = len(q_r)
+    p = [0.0] * n
+    for h in range(H):
+        z = []
+        for c in rows:
+            acc = 0.0
+            for a, b in zip(q_r[h], c):
+                acc += a * b
+            z.append(scale * acc)
+        m = max(z)
+        e = [math.exp(v - m) for v in z]
+        tot = sum(e)
+        for i in range(n):
+            p[i] += e[i] / tot / H
+    mi = max(scores_sel)
+    ei = [math.exp(v - mi) for v in scores_sel]
+    ti = sum(ei)
+    kl = 0.0
+    for i in range(n):
+        if p[i] > 0.0:
+            kl += p[i] * (math.log(p[i]) - math.log(ei[i] / ti))
+    return p, kl

@@ -179,3 +179,42 @@ def forward_rows(seqs: Seqs, qI, kI, w, q, kv, k: int, scale: float, d_v: int, r
     idx = topk(sc, k)
     out, lse = sparse_mla_attn(seqs, q, kv, idx, scale, d_v, rows)
     return dict(scores=sc, indices=idx, out=out, lse=lse)
+
+
+# ------------------------------------------------------------------ indexer-alignment target
+
+def alignment_row(seqs: Seqs, q, kv, indices_row, scale: float, scores_row, r: int):
+    """Training target of the indexer for row r and its KL divergence from the indexer's own
+    distribution ([digest] Key claims and Method, paper section 2.1.1, Eq. 3-4: the indexer is
+    trained with a KL loss towards the main attention distribution aggregated over the heads --
+    over all preceding keys in the dense warm-up, over the selected ones in the sparse stage).
+
+    Readings (the pages print neither equation): the set S is the given index list restricted to
+    causal candidates 0..pos (entries -1 or outside are skipped; repeats count as listed); each
+    head's attention softmax over S (logits scale * q_h . c_s, natural exp) is averaged over the
+    H heads, p[s] = (1/H) sum_h softmax_h[s] (the head sum renormalised); the indexer's
+    distribution is softmax over S of I[r, s]; the loss is KL(p || softmax(I)) =
+    sum_s p[s] (ln p[s] - ln softmax(I)[s]), with 0 ln 0 = 0.
+    Returns (target [len(indices_row)] float64, 0 at skipped entries; kl float).
+    """
+    _, pos, k0, _ = seqs.locate(r)
+    idx = np.asarray(indices_row, np.int64)
+    valid = (idx >= 0) & (idx <= pos)
+    target = np.zeros(idx.shape[0])
+    if not valid.any():
+        return target, 0.0
+    sel = idx[valid]
+    qr = decode(q[r])                                             # [H, d_qk]
+    c = decode(kv[k0 + sel])                                      # [|S|, d_qk]
+    z = scale * (qr @ c.T)                                        # [H, |S|]
+    z = z - z.max(axis=1, keepdims=True)
+    ph = np.exp(z)
+    ph /= ph.sum(axis=1, keepdims=True)
+    p = ph.mean(axis=0)                                           # [|S|]
+    i_sel = np.asarray(scores_row, np.float64)[sel]
+    lq = i_sel - i_sel.max()
+    lq = lq - np.log(np.exp(lq).sum())                            # ln softmax(I) over S
+    pos_p = p > 0
+    kl = float(np.sum(p[pos_p] * (np.log(p[pos_p]) - lq[pos_p])))
+    target[valid] = p
+    return target, kl

@@ -334,3 +334,77 @@ def test_error_bound_covers_float32_evaluations():
         b = b + w32[j] * np.maximum(d, np.float32(0))
     assert np.all(np.abs(a - exact) <= eps) and np.all(np.abs(b - exact) <= eps)
     assert np.all(eps > 0)
+
+
+# ------------------------------------------------------------------ indexer-alignment target
+
+@pytest.mark.parametrize("case", _golden()["alignment"], ids=lambda c: c["name"])
+def test_handworked_alignment(case):
+    sq = Seqs(np.cumsum([0] + case["seqlens_q"]), np.cumsum([0] + case["seqlens_k"]))
+    q = np.asarray(case["q"], np.float64)
+    kv = np.asarray(case["kv"], np.float64)
+    for r in range(len(case["indices"])):
+        tgt, kl = oracle.alignment_row(sq, q, kv, case["indices"][r], case["scale"], case["scores"][r], r)
+        assert np.allclose(tgt, case["target"][r], rtol=0, atol=1e-15)
+        assert abs(kl - case["kl"][r]) <= 1e-15
+
+
+@pytest.mark.parametrize("variant", ["normal", "int"])
+@pytest.mark.parametrize("seed", [0, 1])
+def test_alignment_brute_force(variant, seed):
+    wl, x = _tiny(seed, variant)
+    sq = Seqs(wl.cu_seqlens_q, wl.cu_seqlens_k)
+    seq_of, pos_of = wl.row_positions()
+    dqq, dkv = oracle.decode(x["q"]).tolist(), oracle.decode(x["kv"]).tolist()
+    for r in range(wl.T):
+        b, pos = int(seq_of[r]), int(pos_of[r])
+        k0 = int(wl.cu_seqlens_k[b])
+        sc = oracle.indexer_scores_row(sq, x["qI"], x["kI"], x["w"], r)
+        sel = oracle.topk_row(sc, 3)
+        tgt, kl = oracle.alignment_row(sq, x["q"], x["kv"], sel, wl.scale, sc, r)
+        valid = [s for s in sel if s >= 0]
+        bp, bkl = brute.alignment_row(dqq[r], [dkv[k0 + s] for s in valid], wl.scale, [sc[s] for s in valid])
+        assert np.allclose(tgt[:len(valid)], bp, rtol=1e-12, atol=1e-15)
+        assert np.all(tgt[len(valid):] == 0)
+        assert abs(kl - bkl) <= 1e-12 * max(1.0, abs(bkl))
+
+
+def test_alignment_single_head_is_relative_entropy():
+    """With one head the target is that head's softmax and the loss is the relative entropy
+    between two softmaxes: checked with scipy's softmax and rel_entr (independent routines)."""
+    from scipy.special import rel_entr, softmax
+    rng = np.random.default_rng(11)
+    n = 7
+    sq = Seqs([0, 1], [0, n])
+    q = rng.standard_normal((1, 1, 5))
+    kv = rng.standard_normal((n, 5))
+    scores = rng.standard_normal(n) * 2
+    idx = [6, 2, 0, 5]
+    tgt, kl = oracle.alignment_row(sq, q, kv, idx, 0.7, scores, 0)
+    p = softmax(0.7 * (kv[idx] @ q[0, 0]))
+    qi = softmax(scores[idx])
+    assert np.allclose(tgt, p, rtol=1e-13, atol=0)
+    assert abs(kl - rel_entr(p, qi).sum()) <= 1e-13
+
+
+def test_alignment_invariants():
+    """KL >= 0; zero queries give the uniform target; an indexer whose softmax equals the target
+    gives KL = 0; adding a constant to every score changes nothing; no valid entry gives 0."""
+    wl, x = _tiny(3, "normal")
+    sq = Seqs(wl.cu_seqlens_q, wl.cu_seqlens_k)
+    for r in range(wl.T):
+        sc = oracle.indexer_scores_row(sq, x["qI"], x["kI"], x["w"], r)
+        sel = oracle.topk_row(sc, 4)
+        tgt, kl = oracle.alignment_row(sq, x["q"], x["kv"], sel, wl.scale, sc, r)
+        assert kl >= -1e-15
+        _, kl2 = oracle.alignment_row(sq, x["q"], x["kv"], sel, wl.scale, sc + 5.25, r)
+        assert abs(kl2 - kl) <= 1e-12
+        v = np.asarray(sel) >= 0
+        matched = np.full(sc.shape[0], -np.inf)
+        matched[np.asarray(sel)[v]] = np.log(tgt[v])
+        _, kl0 = oracle.alignment_row(sq, x["q"], x["kv"], sel, wl.scale, matched, r)
+        assert abs(kl0) <= 1e-12
+        tz, _ = oracle.alignment_row(sq, np.zeros((wl.T, wl.H, wl.d_qk)), x["kv"], sel, wl.scale, sc, r)
+        assert np.allclose(tz[v], 1.0 / v.sum(), rtol=0, atol=1e-15)
+    t_e, k_e = oracle.alignment_row(sq, x["q"], x["kv"], [-1, -1], wl.scale, sc, 0)
+    assert k_e == 0.0 and np.all(t_e == 0)
