@@ -209,6 +209,31 @@ size_t dsa_forward_workspace_size(const dsa_seqs_t* seqs, const dsa_forward_args
 dsa_status_t dsa_forward(const dsa_seqs_t* seqs, const dsa_forward_args_t* args, void* ws,
                          size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------- indexer-alignment target
+ * The training signal of the indexer (paper digest page, "Key claims", paper section 2.1.1,
+ * Eq. 3-4, and "Method": a KL loss pulls the indexer's output towards the main attention's
+ * distribution aggregated over the heads -- over all preceding keys in the dense warm-up, over
+ * the selected entries in the sparse stage). The pages print neither equation; the reading taken:
+ * for row r and its index list (entries outside 0..pos are skipped, repeats count as listed),
+ *   p[r,e]  = (1/H) sum_h exp(z_{r,h,e} - lse[r,h]),  z = softmax_scale * q[r,h] . kv[kofs_b + s_e]
+ *   kl[r]   = sum_e p[r,e] * (ln p[r,e] - ln softmax_e(scores[r, s_e]))       (0 ln 0 = 0)
+ * i.e. each head's attention softmax over the list, averaged over the heads, against the
+ * indexer's softmax over the same entries. The dense warm-up is the list 0..pos.
+ *   dtype    DSA_BF16 with (H, d_qk) = (128, 576) (others: DSA_ERR_UNSUPPORTED)
+ *   q, kv    as in dsa_sparse_mla_attn; indices [T, k] int32 whose entries are -1 or causal
+ *            candidates (as dsa_topk produces them)
+ *   lse      [T, H] fp32: the attention's log-sum-exp over the same list (dsa_sparse_mla_attn's
+ *            lse output); other values give unspecified results
+ *   scores   [T, ld_scores] fp32 indexer scores (entries 0..pos read)
+ *   target   [T, k] fp32 (output) or NULL: p per list entry, 0 for skipped entries
+ *   kl       [T] fp32 (output): 0 for a row without a valid entry
+ * No workspace.
+ */
+dsa_status_t dsa_indexer_alignment(const dsa_seqs_t* seqs, int32_t H, int32_t d_qk, dsa_dtype_t dtype,
+                                   const void* q, const void* kv, const int32_t* indices, int32_t k,
+                                   float softmax_scale, const float* lse, const float* scores,
+                                   int64_t ld_scores, float* target, float* kl, void* stream);
+
 /* ---------------------------------------------------------------- misc */
 const char* dsa_status_string(dsa_status_t status); /* static text, never NULL               */
 const char* dsa_last_error(void);                   /* thread-local detail of the last error */

@@ -86,13 +86,17 @@ _c_attn = _proto("dsa_sparse_mla_attn", ctypes.c_int,
 _c_fwd_ws = _proto("dsa_forward_workspace_size", ctypes.c_size_t, [ctypes.POINTER(_Seqs), ctypes.POINTER(_FwdArgs)])
 _c_fwd = _proto("dsa_forward", ctypes.c_int,
                 [ctypes.POINTER(_Seqs), ctypes.POINTER(_FwdArgs), _vp, ctypes.c_size_t, _vp])
+_c_align = _proto("dsa_indexer_alignment", ctypes.c_int,
+                  [ctypes.POINTER(_Seqs), ctypes.c_int32, ctypes.c_int32, ctypes.c_int, _vp, _vp, _vp,
+                   ctypes.c_int32, ctypes.c_float, _vp, _vp, ctypes.c_int64, _vp, _vp, _vp])
 _c_status = _proto("dsa_status_string", ctypes.c_char_p, [ctypes.c_int])
 _c_last = _proto("dsa_last_error", ctypes.c_char_p, [])
 _c_abi = _proto("dsa_abi_version", ctypes.c_int32, [])
 
 EXPORTS = ("dsa_indexer_workspace_size", "dsa_indexer_scores", "dsa_indexer_scaled_workspace_size",
            "dsa_indexer_scores_scaled", "dsa_topk_workspace_size", "dsa_topk", "dsa_sparse_mla_attn_workspace_size",
-           "dsa_sparse_mla_attn", "dsa_forward_workspace_size", "dsa_forward", "dsa_status_string",
+           "dsa_sparse_mla_attn", "dsa_forward_workspace_size", "dsa_forward", "dsa_indexer_alignment",
+           "dsa_status_string",
            "dsa_last_error", "dsa_abi_version")
 
 
@@ -275,6 +279,24 @@ def sparse_mla_attn(seqs: Seqs, q, kv, indices, scale: float, d_v: int = None, o
     _check(_c_attn(ctypes.byref(cs), H, d_qk, d_v, dt, _ptr(q), _ptr(kv), _ptr(indices), k, float(scale),
                    _ptr(out), _ptr(lse), _ptr(ws), wsz, _stream(stream)), "dsa_sparse_mla_attn")
     return out, lse
+
+
+def indexer_alignment(seqs: Seqs, q, kv, indices, scale: float, lse, scores, with_target=True,
+                      kl=None, target=None, stream=None):
+    """Indexer-alignment target (head-averaged attention distribution over each row's index list)
+    and its KL divergence from the softmax of the indexer scores; returns (target or None, kl)."""
+    torch = _torch()
+    T, H, d_qk = (int(x) for x in q.shape)
+    k = int(indices.shape[1])
+    if kl is None:
+        kl = torch.empty((T,), dtype=torch.float32, device=q.device)
+    if target is None and with_target:
+        target = torch.empty((T, k), dtype=torch.float32, device=q.device)
+    cs = seqs.c()
+    _check(_c_align(ctypes.byref(cs), H, d_qk, _dtype_code(q), _ptr(q), _ptr(kv), _ptr(indices), k,
+                    float(scale), _ptr(lse), _ptr(scores), int(scores.stride(0)), _ptr(target), _ptr(kl),
+                    _stream(stream)), "dsa_indexer_alignment")
+    return target, kl
 
 
 class Forward:

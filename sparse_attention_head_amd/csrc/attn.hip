@@ -488,6 +488,217 @@ attn_bf16_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restr
     lse[(int64_t)r * MH + head] = ltot > 0.f ? (st.m + __log2f(ltot)) * 0.6931471805599453f : -INFINITY;
 }
 
+// ---------------------------------------------------------------------------- alignment target
+// Indexer-alignment target (page "DeepSeek-V3.2: Pushing the Frontier of Open Large Language
+// Models" (paper digest), sections "Key claims" (paper section 2.1.1, Eq. 3-4) and "Method": the
+// indexer learns, through a KL loss, the main attention's distribution aggregated over the
+// heads, over all preceding keys or the selected ones). For query row r and its index list
+// (entries outside 0..pos skipped, repeats counted as listed):
+//   p[e]  = (1/H) sum_h exp(z_{h,e} - lse_h),   z_{h,e} = scale * q[r,h] . kv[row s_e]
+//   KL[r] = sum_e p[e] * (ln p[e] - ln softmax_e(I[r, s_e]))
+// with lse the attention's log-sum-exp over the same entries. One workgroup per row: the
+// indexer normaliser first (two block reductions over the listed scores), then the latent rows
+// stream through the attention's double-buffered LDS blocks; per half block each wave computes
+// the logits of its 32 heads on the matrix core (as the attention does), turns them into
+// probabilities against the given lse, and sums them over its heads with a reduce-scatter across
+// lanes; the four waves' sums meet in LDS, where the first wave forms p and the KL terms.
+
+__device__ __forceinline__ float block_reduce_256(float v, float* red, bool is_max) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float t = __shfl_xor(v, o);
+    v = is_max ? fmaxf(v, t) : v + t;
+  }
+  __syncthreads();   // red is free (earlier readers are done)
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  return is_max ? fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])) : (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+// Logits of one half block for the wave's heads (same operand layout as attend_half).
+__device__ __forceinline__ v16f half_logits(const uint8_t* buf, int kbase, const bf16x8 (&qreg)[MT],
+                                            int lane) {
+  const int g = lane >> 5, c32 = lane & 31;
+  const uint8_t* kb_lane = buf + (((kbase + c32) >> 3) * 64 + (c32 & 7) * 8) * 16;
+  const int ksw = kv_swz(c32 & 15);
+  const uint8_t* kb[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) kb[q] = kb_lane + ((2 * q + g) ^ ksw) * 16;
+  auto kop = [&](int t) -> bf16x8 {
+    return *reinterpret_cast<const bf16x8*>(kb[t & 3] + (t >> 2) * 8192);
+  };
+  v16f s = {};
+  bf16x8 ka[KRING];
+#pragma unroll
+  for (int t = 0; t < KRING - 1; ++t) ka[t] = kop(t);
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    if (t + KRING - 1 < MT) ka[(t + KRING - 1) % KRING] = kop(t + KRING - 1);
+    s = mfma_bf16_32x32x16(ka[t % KRING], qreg[t], s);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  return s;
+}
+
+__global__ void __launch_bounds__(256, 1)
+align_bf16_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
+                  const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv,
+                  const int32_t* __restrict__ idx, int k, float scale, const float* __restrict__ lse,
+                  const float* __restrict__ scores, int64_t ld, float* __restrict__ target,
+                  float* __restrict__ kl) {
+  __shared__ __attribute__((aligned(1024))) uint8_t buf0[MBUF];
+  __shared__ __attribute__((aligned(1024))) uint8_t buf1[MBUF];
+  __shared__ float psum[4][MBLK];   // per wave: head sums of the block's keys
+  __shared__ float red[4];
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, c32 = lane & 31;
+  const RowLoc L = locate_row(cu_q, cu_k, B, r);
+  const int32_t* ir = idx + (int64_t)r * k;
+  const float* srow = scores + (int64_t)r * ld;
+  float* trow = target ? target + (int64_t)r * k : nullptr;
+  auto valid_entry = [&](int s) { return s >= 0 && s <= L.pos; };
+
+  // 1. ln of the indexer softmax normaliser over the valid entries
+  float mx = -INFINITY;
+  for (int e = tid; e < k; e += 256) {
+    const int s = ir[e];
+    if (valid_entry(s)) mx = fmaxf(mx, srow[s]);
+  }
+  mx = block_reduce_256(mx, red, true);
+  if (mx == -INFINITY) {   // uniform: no valid entry
+    if (trow)
+      for (int e = tid; e < k; e += 256) trow[e] = 0.f;
+    if (tid == 0) kl[r] = 0.f;
+    return;
+  }
+  float se = 0.f;
+  for (int e = tid; e < k; e += 256) {
+    const int s = ir[e];
+    if (valid_entry(s)) se += __expf(srow[s] - mx);
+  }
+  se = block_reduce_256(se, red, false);
+  const float lnz = mx + __logf(se);
+
+  // 2. query block of this wave (head 32w + c32) and the head's lse (log2 domain)
+  bf16x8 qreg[MT];
+  {
+    const uint16_t* qh = q + ((int64_t)r * MH + 32 * wave + c32) * MDQK + 8 * g;
+#pragma unroll
+    for (int t = 0; t < MT; ++t) qreg[t] = *reinterpret_cast<const bf16x8*>(qh + 16 * t);
+  }
+  const float sl2 = scale * 1.4426950408889634f;
+  const float nl2 = -lse[(int64_t)r * MH + 32 * wave + c32] * 1.4426950408889634f;
+  const int nblk = (k + MBLK - 1) / MBLK;
+  const __amdgpu_buffer_rsrc_t seq = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(kv + (int64_t)L.kofs * (MDQK * 2)), 0, L.n * (MDQK * 2), 0x00020000);
+  auto load_idx = [&](int blk) -> int {
+    const int j = blk * MBLK + lane;
+    return (blk < nblk && j < k) ? ir[j] : -1;
+  };
+  auto prep = [&](int sidx, int& ra, int& rb, uint64_t& vm) {
+    const bool v = valid_entry(sidx);
+    vm = __ballot(v);
+    const int row = v ? sidx : 0;
+    ra = __shfl(row, 16 * wave + (lane >> 3));
+    rb = __shfl(row, 16 * wave + 8 + (lane >> 3));
+  };
+  int ra, rb;
+  uint64_t vm_cur, vm_next;
+  int sidx_cur = load_idx(0);
+  prep(sidx_cur, ra, rb, vm_cur);
+  if (vm_cur) gather_block(buf0, seq, ra, rb, wave, lane);
+  int sidx_next = load_idx(1);
+  float klacc = 0.f;   // first wave: this lane's KL terms
+
+  for (int blk = 0; blk < nblk; ++blk) {
+    const uint8_t* cur = (blk & 1) ? buf1 : buf0;
+    uint8_t* nxt = (blk & 1) ? buf0 : buf1;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();   // the block is in LDS; every wave is done with the other buffer and psum
+    prep(sidx_next, ra, rb, vm_next);
+    if (blk + 1 < nblk && vm_next) gather_block(nxt, seq, ra, rb, wave, lane);
+    const int sidx_after = load_idx(blk + 2);
+    if (vm_cur) {   // uniform
+#pragma unroll 1
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t m32 = (uint32_t)(vm_cur >> (32 * h));
+        if (!m32) continue;   // uniform; its keys are skipped below
+        const v16f sv = half_logits(cur, 32 * h, qreg, lane);
+        float v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int b = 8 * (i >> 2) + (i & 3);
+          const uint64_t lanes = (((m32 >> b) & 1u) ? 0x00000000FFFFFFFFull : 0ull) |
+                                 (((m32 >> (b + 4)) & 1u) ? 0xFFFFFFFF00000000ull : 0ull);
+          v[i] = __builtin_amdgcn_inverse_ballot_w64(lanes) ? __builtin_amdgcn_exp2f(fmaf(sv[i], sl2, nl2)) : 0.f;
+        }
+        // sum over the 32 heads of the wave (lanes of equal g): reduce-scatter; lane bits
+        // (16, 8, 4, 2) pick value index 8*b16 + 4*b8 + 2*b4 + b2, the last step adds lane pairs
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const bool hi = (lane & 16) != 0;
+          const float keep = hi ? v[j + 8] : v[j], give = hi ? v[j] : v[j + 8];
+          v[j] = keep + __shfl_xor(give, 16);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bool hi = (lane & 8) != 0;
+          const float keep = hi ? v[j + 4] : v[j], give = hi ? v[j] : v[j + 4];
+          v[j] = keep + __shfl_xor(give, 8);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const bool hi = (lane & 4) != 0;
+          const float keep = hi ? v[j + 2] : v[j], give = hi ? v[j] : v[j + 2];
+          v[j] = keep + __shfl_xor(give, 4);
+        }
+        {
+          const bool hi = (lane & 2) != 0;
+          const float keep = hi ? v[1] : v[0], give = hi ? v[0] : v[1];
+          v[0] = keep + __shfl_xor(give, 2);
+        }
+        v[0] += __shfl_xor(v[0], 1);
+        if ((lane & 1) == 0) {
+          const int i = 8 * ((lane >> 4) & 1) + 4 * ((lane >> 3) & 1) + 2 * ((lane >> 2) & 1) + ((lane >> 1) & 1);
+          psum[wave][32 * h + 8 * (i >> 2) + 4 * g + (i & 3)] = v[0];
+        }
+      }
+      __syncthreads();
+      if (wave == 0) {
+        const int e = blk * MBLK + lane;
+        const bool ok = (vm_cur >> lane) & 1ull;
+        const float p = ok ? (psum[0][lane] + psum[1][lane] + psum[2][lane] + psum[3][lane]) * (1.f / MH) : 0.f;
+        if (trow && e < k) trow[e] = p;
+        if (p > 0.f) klacc += p * (__logf(p) - (srow[sidx_cur] - lnz));
+      }
+    } else if (wave == 0) {
+      const int e = blk * MBLK + lane;
+      if (trow && e < k) trow[e] = 0.f;
+    }
+    vm_cur = vm_next;
+    sidx_cur = sidx_next;
+    sidx_next = sidx_after;
+  }
+  if (wave == 0) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) klacc += __shfl_xor(klacc, o);
+    if (lane == 0) kl[r] = klacc;
+  }
+}
+
+hipError_t launch_align_bf16(const SeqInfo& s, const uint16_t* q, const uint16_t* kv,
+                             const int32_t* idx, int k, float scale, const float* lse,
+                             const float* scores, int64_t ld, float* target, float* kl,
+                             hipStream_t st) {
+  if (s.T == 0) return hipSuccess;
+  hipLaunchKernelGGL(align_bf16_kernel, dim3(s.T), dim3(256), 0, st, s.B, s.cu_q, s.cu_k, q,
+                     reinterpret_cast<const uint8_t*>(kv), idx, k, scale, lse, scores, ld, target, kl);
+  return hipGetLastError();
+}
+
 // Merges the splits of one (row, head) per wave: with M the largest partial log2-sum-exp, split
 // s weighs 2^(lse_s - M); out = sum of weighted partial outputs / sum of weights, lse = M +
 // log2(sum of weights) (natural log on output). Splits without a valid entry have weight 0; a

@@ -410,6 +410,39 @@ dsa_status_t dsa_forward(const dsa_seqs_t* seqs, const dsa_forward_args_t* a, vo
                   p.attn_bytes, hs);
 }
 
+dsa_status_t dsa_indexer_alignment(const dsa_seqs_t* seqs, int32_t H, int32_t d_qk, dsa_dtype_t dtype,
+                                   const void* q, const void* kv, const int32_t* indices, int32_t k,
+                                   float softmax_scale, const float* lse, const float* scores,
+                                   int64_t ld_scores, float* target, float* kl, void* stream) {
+  dsa::SeqInfo s;
+  dsa_status_t st = check_seqs(seqs, s);
+  if (st != DSA_OK) return st;
+  if (s.B == 0) return ok();
+  if (dtype != DSA_BF16 && dtype != DSA_F32)
+    return fail(DSA_ERR_DTYPE, "alignment inputs must be DSA_BF16 (DSA_F32 is not implemented)");
+  if (dtype != DSA_BF16 || H != 128 || d_qk != 576)
+    return fail(DSA_ERR_UNSUPPORTED, "the alignment target needs bf16 with (H, d_qk) = (128, 576)");
+  if (k < 1 || k > 16384) return fail(DSA_ERR_UNSUPPORTED, "k = %d outside 1..16384", k);
+  if (ld_scores < s.max_n || ld_scores % 4 != 0)
+    return fail(DSA_ERR_SHAPE, "ld_scores = %lld must be >= max_seqlen_k (%d) and a multiple of 4",
+                (long long)ld_scores, s.max_n);
+  if (!(softmax_scale > 0.f) || softmax_scale > 3.0e38f)
+    return fail(DSA_ERR_SHAPE, "softmax_scale must be positive and finite (got %g)", softmax_scale);
+  if ((int64_t)s.max_n * d_qk * 2 > INT32_MAX)
+    return fail(DSA_ERR_UNSUPPORTED, "needs max_seqlen_k * 1152 < 2^31 (got %d keys)", s.max_n);
+  if (s.T == 0) return ok();
+  if (!q || !kv || !indices || !lse || !scores || !kl)
+    return fail(DSA_ERR_NULL, "alignment tensor pointer is NULL");
+  if (!aligned16(q) || !aligned16(kv) || !aligned16(indices) || !aligned16(lse) || !aligned16(scores) ||
+      !aligned16(kl) || (target && !aligned16(target)))
+    return fail(DSA_ERR_ALIGN, "alignment tensors must be 16-byte aligned");
+  return hip_status(dsa::launch_align_bf16(s, static_cast<const uint16_t*>(q),
+                                           static_cast<const uint16_t*>(kv), indices, k, softmax_scale,
+                                           lse, scores, ld_scores, target, kl,
+                                           static_cast<hipStream_t>(stream)),
+                    "alignment launch");
+}
+
 const char* dsa_status_string(dsa_status_t status) {
   switch (status) {
     case DSA_OK: return "ok";

@@ -51,6 +51,12 @@ hipError_t launch_attn_bf16(const SeqInfo& s, const uint16_t* q, const uint16_t*
                             const int32_t* idx, int k, float scale, uint16_t* out, float* lse,
                             void* ws, size_t ws_bytes, hipStream_t st);
 
+// Indexer-alignment target p [T, k] (or NULL) and KL [T] for the bf16 (128, 576) shapes.
+hipError_t launch_align_bf16(const SeqInfo& s, const uint16_t* q, const uint16_t* kv,
+                             const int32_t* idx, int k, float scale, const float* lse,
+                             const float* scores, int64_t ld, float* target, float* kl,
+                             hipStream_t st);
+
 // Number of compute units of the current device (cached per device).
 int device_cu_count();
 

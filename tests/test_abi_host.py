@@ -199,6 +199,21 @@ def test_forward_short_context_workspace(dsa):
     assert dsa._c_fwd_ws(sq.ref, ctypes.byref(a)) >= 100 * 100 * 4 + 100 * 99 * 4
 
 
+def test_alignment_validation(dsa):
+    sq = FakeSeqs(dsa, [0, 10], [0, 20])
+    keep, p = buf(64)
+    A = dsa._c_align
+    assert A(sq.ref, 128, 576, dsa.DSA_FP8_E4M3, p, p, p, 64, 0.04, p, p, 20, p, p, None) == dsa.DSA_ERR_DTYPE
+    assert A(sq.ref, 8, 80, dsa.DSA_F32, p, p, p, 64, 0.04, p, p, 20, p, p, None) == dsa.DSA_ERR_UNSUPPORTED
+    assert A(sq.ref, 128, 576, dsa.DSA_BF16, p, p, p, 0, 0.04, p, p, 20, p, p, None) == dsa.DSA_ERR_UNSUPPORTED
+    assert A(sq.ref, 128, 576, dsa.DSA_BF16, p, p, p, 64, 0.04, p, p, 18, p, p, None) == dsa.DSA_ERR_SHAPE
+    assert A(sq.ref, 128, 576, dsa.DSA_BF16, p, p, p, 64, -1.0, p, p, 20, p, p, None) == dsa.DSA_ERR_SHAPE
+    assert A(sq.ref, 128, 576, dsa.DSA_BF16, p, p, p, 64, 0.04, None, p, 20, p, p, None) == dsa.DSA_ERR_NULL
+    assert A(sq.ref, 128, 576, dsa.DSA_BF16, p, p, p, 64, 0.04, p, p, 20, p, None, None) == dsa.DSA_ERR_NULL
+    _, pm = buf(64, misalign=4)
+    assert A(sq.ref, 128, 576, dsa.DSA_BF16, p, p, p, 64, 0.04, p, p, 20, pm, p, None) == dsa.DSA_ERR_ALIGN
+
+
 def test_last_error_is_descriptive(dsa):
     sq = FakeSeqs(dsa, [0, 10], [0, 5])
     indexer(dsa, sq)

@@ -218,6 +218,84 @@ def test_scaled_indexer(gpu, case, variant, sides):
             assert not bad.any(), f"row {r}: worst {np.max(np.abs(got - ref) / eps)}"
 
 
+def _alignment_check(sq, x, wl, idx, scores_gpu, lse_gpu, tgt, kl):
+    """Per entry, the GPU's p differs from the exact one by the logit error (fp32 accumulation:
+    gamma(d_qk + 1) * scale * sum_d |q_hd c_ed|) plus its lse error (GPU lse against the exact
+    lse over the same entries), both in the exponent; the KL bound follows term by term."""
+    for r in range(wl.T):
+        _, pos, k0, _ = sq.locate(r)
+        ref_t, ref_kl = oracle.alignment_row(sq, x["q"], x["kv"], idx[r], wl.scale, scores_gpu[r].astype(np.float64), r)
+        row = np.asarray(idx[r], np.int64)
+        v = (row >= 0) & (row <= pos)
+        if not v.any():
+            assert np.all(tgt[r] == 0) and kl[r] == 0
+            continue
+        qr = oracle.decode(x["q"][r])
+        c = oracle.decode(x["kv"][k0 + row[v]])
+        _, lse_ex = oracle.attn_row(sq, x["q"], x["kv"], row[v], wl.scale, wl.d_v, r)
+        dl = np.abs(lse_gpu[r].astype(np.float64) - lse_ex)                    # [H]
+        ez = gamma(wl.d_qk + 1) * wl.scale * (np.abs(qr) @ np.abs(c).T)        # [H, |S|]
+        delta = np.max(ez + dl[:, None], axis=0) + 1e-6                        # + exp/rounding
+        rel = np.expm1(delta)
+        p = ref_t[v]
+        got = tgt[r][v].astype(np.float64)
+        assert np.all(np.abs(got - p) <= rel * p + 1e-12), f"row {r}: target outside the bound"
+        assert np.all(tgt[r][~v] == 0)
+        sv = scores_gpu[r].astype(np.float64)[row[v]]
+        lq = sv - sv.max() - np.log(np.sum(np.exp(sv - sv.max())))
+        bound = np.sum(p * (rel * (np.abs(np.log(p) - lq) + 1) + delta)) + 1e-5
+        assert abs(float(kl[r]) - ref_kl) <= bound, f"row {r}: kl {kl[r]} vs {ref_kl} (bound {bound})"
+
+
+@pytest.mark.parametrize("case", ["prefill", "decode"])
+def test_indexer_alignment(gpu, case):
+    """Alignment target and KL on the GPU's own indices, scores and lse (the steps before are
+    tested on their own) against the oracle; prefill rows with short (k > candidates) and long
+    rows, and a decode batch."""
+    if case == "prefill":
+        sq_q, sq_k, k = [5, 37, 70], [40, 37, 1500], 128
+    else:
+        sq_q, sq_k, k = [1, 1, 1], [17, 2100, 5000], 2048
+    wl = dg.custom(name="align", seqlens_q=sq_q, seqlens_k=sq_k, H_I=64, d_I=128, k=k, H=128,
+                   d_qk=576, d_v=512, idx_dtype="fp8", attn_dtype="bf16", wid=35)
+    x = dg.gen_inputs(wl, "normal", seed=9)
+    seqs = gpu.Seqs(wl.cu_seqlens_q, wl.cu_seqlens_k)
+    T = {kk: dev(v) for kk, v in x.items() if kk not in ("cu_seqlens_q", "cu_seqlens_k")}
+    scores = gpu.indexer_scores(seqs, T["qI"], T["kI"], T["w"])
+    idx = gpu.topk(seqs, scores, wl.k)
+    _, lse = gpu.sparse_mla_attn(seqs, T["q"], T["kv"], idx, wl.scale, wl.d_v)
+    tgt, kl = gpu.indexer_alignment(seqs, T["q"], T["kv"], idx, wl.scale, lse, scores)
+    _, kl2 = gpu.indexer_alignment(seqs, T["q"], T["kv"], idx, wl.scale, lse, scores, with_target=False)
+    torch.cuda.synchronize()
+    assert np.array_equal(kl.cpu().numpy(), kl2.cpu().numpy())
+    sq = Seqs(wl.cu_seqlens_q, wl.cu_seqlens_k)
+    _alignment_check(sq, x, wl, idx.cpu().numpy(), scores.cpu().numpy(), lse.cpu().numpy(),
+                     tgt.cpu().numpy(), kl.cpu().numpy())
+
+
+def test_indexer_alignment_edge_lists(gpu):
+    """-1 entries, repeats, an entry list with a single valid key, a row without one."""
+    wl = dg.custom(name="align_edge", seqlens_q=[4], seqlens_k=[50], H_I=64, d_I=128, k=70, H=128,
+                   d_qk=576, d_v=512, idx_dtype="fp8", attn_dtype="bf16", wid=36)
+    x = dg.gen_inputs(wl, "normal", seed=4)
+    rng = np.random.default_rng(8)
+    idx = np.full((4, 70), -1, np.int32)
+    idx[0, :40] = rng.integers(0, 47, 40)      # row 0 sits at position 46: repeats, unsorted
+    idx[1, 5:9] = [40, 3, 3, 47]               # position 47
+    idx[2, 69] = 11                            # single valid entry at the end
+    seqs = gpu.Seqs(wl.cu_seqlens_q, wl.cu_seqlens_k)
+    T = {kk: dev(v) for kk, v in x.items() if kk not in ("cu_seqlens_q", "cu_seqlens_k")}
+    scores = gpu.indexer_scores(seqs, T["qI"], T["kI"], T["w"])
+    didx = dev(idx)
+    _, lse = gpu.sparse_mla_attn(seqs, T["q"], T["kv"], didx, wl.scale, wl.d_v)
+    tgt, kl = gpu.indexer_alignment(seqs, T["q"], T["kv"], didx, wl.scale, lse, scores)
+    torch.cuda.synchronize()
+    sq = Seqs(wl.cu_seqlens_q, wl.cu_seqlens_k)
+    _alignment_check(sq, x, wl, idx, scores.cpu().numpy(), lse.cpu().numpy(), tgt.cpu().numpy(),
+                     kl.cpu().numpy())
+    assert kl[3].item() == 0.0
+
+
 def test_indexer_weight_extremes(gpu):
     """Rows whose head weights span the fp32 range (huge, tiny, zero, all negative, a single
     nonzero head): the per-row scaling of the FP8 prefill path's linear term must hold the error
