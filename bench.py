@@ -132,6 +132,12 @@ def measure(torch, dsa, wl, T, seqs, steps, warmup, scales=None):
                                                           out=out, lse=lse, ws=aws), steps, warmup)
     t_fwd = time_loop(torch, fwd, steps, warmup)
     res = dict(fused_ms=t_fwd, indexer_ms=t_idx, topk_ms=t_topk, attn_ms=t_attn)
+    if scales is not None and wl.attn_dtype == "bf16":   # the indexer-alignment target of the same rows
+        kl = torch.empty((wl.T,), dtype=torch.float32, device="cuda")
+        tgt = torch.empty((wl.T, wl.k), dtype=torch.float32, device="cuda")
+        res["alignment_ms"] = time_loop(
+            torch, lambda: dsa.indexer_alignment(seqs, T["q"], T["kv"], idx, wl.scale, lse, scores,
+                                                 kl=kl, target=tgt), steps, warmup)
     if scales is not None:
         qs, ks = to_dev(torch, scales["q_scale"]), to_dev(torch, scales["k_scale"])
         sws_n = dsa.indexer_scaled_workspace_size(seqs, wl.H_I, wl.d_I, dsa._dtype_code(T["qI"]))
@@ -209,6 +215,10 @@ def main():
         attention=dict(ms=tm["attn_ms"], tflops=attn_tflops, frac_bf16=attn_tflops / PEAK_BF16_TFLOPS,
                        flop=alg["attn_flop"]),
     )
+    if "alignment_ms" in tm:   # logits of every selected entry again: 2 H d_qk flop each
+        af = 2.0 * wl.H * wl.d_qk * alg["selected"]
+        at = af / (tm["alignment_ms"] / 1e3) / 1e12
+        stages["alignment"] = dict(ms=tm["alignment_ms"], tflops=at, frac_bf16=at / PEAK_BF16_TFLOPS, flop=af)
     if "indexer_scaled_ms" in tm:   # scaled FP8 inputs (per row and head, per key)
         st = alg["indexer_flop"] / (tm["indexer_scaled_ms"] / 1e3) / 1e12
         stages["indexer_scaled"] = dict(ms=tm["indexer_scaled_ms"], tflops=st, frac_fp8=st / PEAK_FP8_TFLOPS)

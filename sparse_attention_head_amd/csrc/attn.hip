@@ -496,9 +496,10 @@ attn_bf16_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restr
 // (entries outside 0..pos skipped, repeats counted as listed):
 //   p[e]  = (1/H) sum_h exp(z_{h,e} - lse_h),   z_{h,e} = scale * q[r,h] . kv[row s_e]
 //   KL[r] = sum_e p[e] * (ln p[e] - ln softmax_e(I[r, s_e]))
-// with lse the attention's log-sum-exp over the same entries. One workgroup per row: the
-// indexer normaliser first (two block reductions over the listed scores), then the latent rows
-// stream through the attention's double-buffered LDS blocks; per half block each wave computes
+// with lse the attention's log-sum-exp over the same entries. One workgroup per row, two per
+// compute unit: the indexer normaliser first (two block reductions over the listed scores), then
+// the latent rows stream through one LDS block buffer laid out as the attention's; per half
+// block each wave computes
 // the logits of its 32 heads on the matrix core (as the attention does), turns them into
 // probabilities against the given lse, and sums them over its heads with a reduce-scatter across
 // lanes; the four waves' sums meet in LDS, where the first wave forms p and the KL terms.
@@ -516,9 +517,11 @@ __device__ __forceinline__ float block_reduce_256(float v, float* red, bool is_m
   return is_max ? fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])) : (red[0] + red[1]) + (red[2] + red[3]);
 }
 
-// Logits of one half block for the wave's heads (same operand layout as attend_half).
+// Logits of one half block for the wave's heads (same operand layout as attend_half); with gdst
+// set, the next block's gather goes out one load every other matrix instruction (as there).
 __device__ __forceinline__ v16f half_logits(const uint8_t* buf, int kbase, const bf16x8 (&qreg)[MT],
-                                            int lane) {
+                                            int lane, __amdgpu_buffer_rsrc_t gseq, uint8_t* gdst,
+                                            int gvoff0, int gvoff1) {
   const int g = lane >> 5, c32 = lane & 31;
   const uint8_t* kb_lane = buf + (((kbase + c32) >> 3) * 64 + (c32 & 7) * 8) * 16;
   const int ksw = kv_swz(c32 & 15);
@@ -536,20 +539,25 @@ __device__ __forceinline__ v16f half_logits(const uint8_t* buf, int kbase, const
   for (int t = 0; t < MT; ++t) {
     if (t + KRING - 1 < MT) ka[(t + KRING - 1) % KRING] = kop(t + KRING - 1);
     s = mfma_bf16_32x32x16(ka[t % KRING], qreg[t], s);
+    if ((t & 1) == 0 && gdst)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          gseq, (__attribute__((address_space(3))) void*)(gdst + ((t / 2) / 9) * 1024 + ((t / 2) % 9) * 8192),
+          16, (t / 2) / 9 ? gvoff1 : gvoff0, ((t / 2) % 9) * 128, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
   }
   return s;
 }
 
-__global__ void __launch_bounds__(256, 1)
+__global__ void __launch_bounds__(256, 2)
 align_bf16_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
                   const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv,
                   const int32_t* __restrict__ idx, int k, float scale, const float* __restrict__ lse,
                   const float* __restrict__ scores, int64_t ld, float* __restrict__ target,
                   float* __restrict__ kl) {
-  __shared__ __attribute__((aligned(1024))) uint8_t buf0[MBUF];
-  __shared__ __attribute__((aligned(1024))) uint8_t buf1[MBUF];
-  __shared__ float psum[4][MBLK];   // per wave: head sums of the block's keys
+  // one block buffer (72 KB), so that two rows share a compute unit: one row's gather overlaps
+  // the other's matrix work
+  __shared__ __attribute__((aligned(1024))) uint8_t buf[MBUF];
+  __shared__ float psum[2][4][MBLK];   // per block parity and wave: head sums of the block's keys
   __shared__ float red[4];
   const int r = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -609,24 +617,37 @@ align_bf16_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __rest
   uint64_t vm_cur, vm_next;
   int sidx_cur = load_idx(0);
   prep(sidx_cur, ra, rb, vm_cur);
-  if (vm_cur) gather_block(buf0, seq, ra, rb, wave, lane);
+  if (vm_cur) gather_block(buf, seq, ra, rb, wave, lane);
   int sidx_next = load_idx(1);
   float klacc = 0.f;   // first wave: this lane's KL terms
+  // the first wave forms p and the KL terms of a block after the next barrier (the waves' head
+  // sums of block b sit in psum[b & 1]); its entry's index and validity are kept until then
+  int sidx_prev = -1;
+  bool ok_prev = false, have_prev = false;
+  auto finish_prev = [&](int pblk) {
+    if (wave == 0 && have_prev) {
+      const int e = pblk * MBLK + lane;
+      const float p = ok_prev ? (psum[pblk & 1][0][lane] + psum[pblk & 1][1][lane] + psum[pblk & 1][2][lane] +
+                                 psum[pblk & 1][3][lane]) * (1.f / MH)
+                              : 0.f;
+      if (trow && e < k) trow[e] = p;
+      if (p > 0.f) klacc += p * (__logf(p) - (srow[sidx_prev] - lnz));
+    }
+  };
 
   for (int blk = 0; blk < nblk; ++blk) {
-    const uint8_t* cur = (blk & 1) ? buf1 : buf0;
-    uint8_t* nxt = (blk & 1) ? buf0 : buf1;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();   // the block is in LDS; every wave is done with the other buffer and psum
+    __syncthreads();   // the block is in LDS; the previous block's head sums are complete
+    finish_prev(blk - 1);
     prep(sidx_next, ra, rb, vm_next);
-    if (blk + 1 < nblk && vm_next) gather_block(nxt, seq, ra, rb, wave, lane);
+    const bool gon = blk + 1 < nblk && vm_next;
     const int sidx_after = load_idx(blk + 2);
     if (vm_cur) {   // uniform
 #pragma unroll 1
       for (int h = 0; h < 2; ++h) {
         const uint32_t m32 = (uint32_t)(vm_cur >> (32 * h));
-        if (!m32) continue;   // uniform; its keys are skipped below
-        const v16f sv = half_logits(cur, 32 * h, qreg, lane);
+        if (!m32) continue;   // uniform; its keys are skipped when the block is finished
+        const v16f sv = half_logits(buf, 32 * h, qreg, lane, seq, nullptr, 0, 0);
         float v[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -636,52 +657,54 @@ align_bf16_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __rest
           v[i] = __builtin_amdgcn_inverse_ballot_w64(lanes) ? __builtin_amdgcn_exp2f(fmaf(sv[i], sl2, nl2)) : 0.f;
         }
         // sum over the 32 heads of the wave (lanes of equal g): reduce-scatter; lane bits
-        // (16, 8, 4, 2) pick value index 8*b16 + 4*b8 + 2*b4 + b2, the last step adds lane pairs
+        // (16, 8, 4, 2) pick value index 8*b16 + 4*b8 + 2*b4 + b2, the last step adds lane pairs.
+        // Partner values by lane-xor: swizzles (xor 16, 4) and row-local moves (xor 8, 2, 1).
+        auto xor16 = [](float x) { return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), (16 << 10) | 0x1F)); };
+        auto xor4 = [](float x) { return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), (4 << 10) | 0x1F)); };
+        auto xor8 = [](float x) { return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, false)); };
+        auto xor2 = [](float x) { return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false)); };
+        auto xor1 = [](float x) { return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false)); };
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const bool hi = (lane & 16) != 0;
           const float keep = hi ? v[j + 8] : v[j], give = hi ? v[j] : v[j + 8];
-          v[j] = keep + __shfl_xor(give, 16);
+          v[j] = keep + xor16(give);
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const bool hi = (lane & 8) != 0;
           const float keep = hi ? v[j + 4] : v[j], give = hi ? v[j] : v[j + 4];
-          v[j] = keep + __shfl_xor(give, 8);
+          v[j] = keep + xor8(give);
         }
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const bool hi = (lane & 4) != 0;
           const float keep = hi ? v[j + 2] : v[j], give = hi ? v[j] : v[j + 2];
-          v[j] = keep + __shfl_xor(give, 4);
+          v[j] = keep + xor4(give);
         }
         {
           const bool hi = (lane & 2) != 0;
           const float keep = hi ? v[1] : v[0], give = hi ? v[0] : v[1];
-          v[0] = keep + __shfl_xor(give, 2);
+          v[0] = keep + xor2(give);
         }
-        v[0] += __shfl_xor(v[0], 1);
+        v[0] += xor1(v[0]);
         if ((lane & 1) == 0) {
           const int i = 8 * ((lane >> 4) & 1) + 4 * ((lane >> 3) & 1) + 2 * ((lane >> 2) & 1) + ((lane >> 1) & 1);
-          psum[wave][32 * h + 8 * (i >> 2) + 4 * g + (i & 3)] = v[0];
+          psum[blk & 1][wave][32 * h + 8 * (i >> 2) + 4 * g + (i & 3)] = v[0];
         }
       }
-      __syncthreads();
-      if (wave == 0) {
-        const int e = blk * MBLK + lane;
-        const bool ok = (vm_cur >> lane) & 1ull;
-        const float p = ok ? (psum[0][lane] + psum[1][lane] + psum[2][lane] + psum[3][lane]) * (1.f / MH) : 0.f;
-        if (trow && e < k) trow[e] = p;
-        if (p > 0.f) klacc += p * (__logf(p) - (srow[sidx_cur] - lnz));
-      }
-    } else if (wave == 0) {
-      const int e = blk * MBLK + lane;
-      if (trow && e < k) trow[e] = 0.f;
     }
+    __syncthreads();   // every wave is done with the buffer
+    if (gon) gather_block(buf, seq, ra, rb, wave, lane);
+    have_prev = true;
+    ok_prev = (vm_cur >> lane) & 1ull;
+    sidx_prev = sidx_cur;
     vm_cur = vm_next;
     sidx_cur = sidx_next;
     sidx_next = sidx_after;
   }
+  __syncthreads();   // the last block's head sums
+  finish_prev(nblk - 1);
   if (wave == 0) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) klacc += __shfl_xor(klacc, o);
