@@ -857,9 +857,10 @@ hipError_t launch_topk(const SeqInfo& s, const float* scores, int64_t ld, int k,
   if (s.T == 0) return hipSuccess;
   const int tiles = (s.max_n + TK_TILE - 1) / TK_TILE;
   const dim3 grid(s.T), block(TK_THREADS);
-  // the streaming kernel needs enough rows to keep two per compute unit busy; small batches
-  // (decode) use the register-resident kernel, whose 16 waves per row finish one row faster
-  if (k <= TS_MAXK && s.max_n <= TS_MAXN && s.T >= 2 * device_cu_count())
+  // the streaming kernel for k <= 2048 and rows up to 131072 candidates, large batches and decode
+  // alike (it also finishes a lone row sooner than the register-resident kernel); the others for
+  // larger k and longer rows
+  if (k <= TS_MAXK && s.max_n <= TS_MAXN)
     hipLaunchKernelGGL(topk_stream_kernel, grid, dim3(TS_THREADS), 0, st, s.B, s.cu_q, s.cu_k, scores, ld,
                        k, idx);
   else if (tiles <= 2)

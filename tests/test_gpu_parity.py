@@ -369,15 +369,14 @@ def test_topk_ties_and_zeros(gpu):
         assert idx[r].tolist() == oracle.topk_row(sc[r, :pos + 1].astype(np.float64), k).tolist()
 
 
-@pytest.mark.parametrize("rows", [5, 600])
+@pytest.mark.parametrize("rows,k", [(5, 2048), (600, 2048), (5, 4096)])
 @pytest.mark.parametrize("n", [5000, 30000, 131072, 140000])
-def test_topk_row_lengths_and_degenerate_rows(gpu, n, rows):
-    """Every top-k code path: register-resident rows of 1, 2..8, 9..32 tiles of 4096 (small
-    batches), the streaming kernel with its exact fallback (batches of at least two rows per
-    compute unit), the multi-pass kernel beyond 131072 -- each with degenerate rows: all equal,
+def test_topk_row_lengths_and_degenerate_rows(gpu, n, rows, k):
+    """Every top-k code path: the streaming kernel with its exact fallback (k <= 2048, rows up to
+    131072, small and large batches), register-resident rows of 1, 2..8, 9..32 tiles of 4096
+    (larger k), the multi-pass kernel beyond 131072 -- each with degenerate rows: all equal,
     all +-0, one distinct value, integer ties, random floats, and a row whose largest values all
     sit outside the sampled runs."""
-    k = 2048
     rng = np.random.default_rng(n + rows)
     late = rng.standard_normal(n).astype(np.float32)
     late[n - 3000:] += 50.0   # the top scores cluster in one stretch of the row
