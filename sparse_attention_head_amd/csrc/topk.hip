@@ -9,11 +9,13 @@
 // Ties prefer the lower position, +0 equals -0, output ascending and padded with -1.
 //
 // Method (exact, deterministic): scores map to order-preserving 32-bit keys. A radix select over
-// the key digits (11, 11 and 10 bits, most significant first) finds the k-th largest key T and the
-// number `need` of keys equal to T that belong to the selection. An ordered compaction pass then
-// keeps, in position order, every key > T and the first `need` keys == T; its output is ascending
-// by construction. Per tile of the row, the prefix counts come from wavefront ballots
-// (mbcnt-style popcounts) plus one small exchange across waves.
+// the key digits (at most 11 bits each, most significant first) finds the k-th largest key T and
+// the number `need` of keys equal to T that belong to the selection; the output keeps every key > T
+// and the `need` lowest positions with key == T, in ascending position order. Three kernels share
+// these semantics: a streaming kernel that reads each row once and selects over a short list of
+// candidates above a sampled floor (k <= 2048, rows up to 131072), a register-resident kernel for
+// larger k, and a multi-pass kernel straight from global memory for longer rows (also the
+// streaming kernel's fallback).
 #include "dsa_internal.h"
 #include "device_common.h"
 
@@ -519,10 +521,10 @@ topk_reg_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restri
 }
 
 // ------------------------------------------------------------------------------------------
-// Streaming variant for k <= 2048 and rows of up to 131072 candidates: one pass over the row with
-// about two vector instructions per score, so that the pass runs at memory speed, and workgroups
-// of eight waves with 76 KB of LDS, two per compute unit, so that the selection work of one row
-// overlaps the streaming of another.
+// Streaming variant for k <= 2048 and rows of up to 131072 candidates (any batch size): one pass
+// over the row with about two vector instructions per score, so that the pass runs at memory
+// speed, and workgroups of eight waves with 76 KB of LDS, two per compute unit, so that the
+// selection work of one row overlaps the streaming of another.
 //  1. A sample of the row (all of it up to 8192 positions, else 8 evenly spaced runs of 1024) is
 //     kept in LDS; two radix digits (22 key bits) locate its `want`-th largest key and the floor F
 //     is that 22-bit bin's lower edge. With the whole row as sample want = k, so at least k keys
@@ -538,7 +540,8 @@ topk_reg_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restri
 //     keys tie at the threshold, the row is redone exactly from global memory.
 //  5. Radix select over the list: the k-th largest key T and how many keys equal to T are taken
 //     (`need`, the lowest positions first; when fewer than all, a radix select over the tied
-//     positions finds the last one taken).
+//     positions finds the last one taken). The digits start at the highest bit where F and the
+//     list's largest key differ (every listed key lies between them).
 //  6. The selected positions are marked in a bitmap; each thread owns a run of its words, one
 //     block-wide exclusive scan of their popcounts gives the output offsets, and every thread
 //     writes its positions in ascending order.
