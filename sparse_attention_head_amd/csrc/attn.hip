@@ -134,10 +134,12 @@ __device__ __forceinline__ v16f mfma_bf16_32x32x16(const bf16x8& a, const bf16x8
 }
 
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two floats rounded to bf16 (nearest-even; NaN stays NaN), a in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
 }
 
 // Bank swizzle of the 8 chunk positions of key s (s16 = s % 16): a GF(2)-linear map whose values
@@ -263,9 +265,14 @@ __device__ __forceinline__ bool attend_half(const uint8_t* buf, int kbase, uint3
     lsum += p;
     pb[i >> 3][i & 7] = (__bf16)p;
   }
-  if (__any(!(lsum <= 0x1p60f))) {
-    st.seen = fmaxf(st.seen, half_max());
-    return true;
+  const bool over = !(lsum <= 0x1p60f);
+  if (__any(over)) {
+    const float hm = half_max();
+    st.seen = fmaxf(st.seen, hm);
+    // with finite logits an overflowing lane always has a larger maximum to restart from, and
+    // each restart raises some head's reference; NaN or infinite logits have none, and their
+    // pass goes on (its output is then not finite) instead of restarting forever
+    if (__any(over && hm > st.m)) return true;
   }
   st.l += lsum;
   // O^T[v, head] += V^T[v, keys] P^T[keys, head]. K step j covers keys 16j + 8h + 4g + jj
@@ -333,6 +340,34 @@ __device__ __forceinline__ bool attend_block(const uint8_t* buf, uint64_t vmask,
   return false;
 }
 
+// Stores a wave's output block, O^T in the accumulators (head c32 of the wave, values
+// 32 vt + 8 i + 4 g + 0..3 in acc_o[vt][4 i .. 4 i + 3]), times inv, as bf16 rows dst + h * MDV
+// (h = 0..31). The rows go through 32 KB of LDS (row h at h * 1024 bytes, its 16-byte chunk c at
+// position c ^ (h % 16)), so that each global store writes one head's whole row (1 KB) instead
+// of 16-byte pieces of 32 rows.
+__device__ __forceinline__ void store_head_rows(uint16_t* dst, const v16f (&acc_o)[MDV / 32], float inv,
+                                                uint8_t* stage, int lane) {
+  const int g = lane >> 5, c32 = lane & 31;
+  uint8_t* const mine = stage + c32 * (MDV * 2) + g * 8;
+#pragma unroll
+  for (int vt = 0; vt < MDV / 32; ++vt) {
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      uint2 pk;
+      pk.x = pack_bf16x2(acc_o[vt][4 * i4 + 0] * inv, acc_o[vt][4 * i4 + 1] * inv);
+      pk.y = pack_bf16x2(acc_o[vt][4 * i4 + 2] * inv, acc_o[vt][4 * i4 + 3] * inv);
+      *reinterpret_cast<uint2*>(mine + (((4 * vt + i4) ^ (c32 & 15)) * 16)) = pk;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // (one wave writes and reads its own rows: its LDS operations complete in order)
+#pragma unroll 4
+  for (int h = 0; h < 32; ++h) {
+    const uint4 v = *reinterpret_cast<const uint4*>(stage + h * (MDV * 2) + ((lane ^ (h & 15)) * 16));
+    *reinterpret_cast<uint4*>(dst + (int64_t)h * MDV + 8 * lane) = v;
+  }
+}
+
 // One workgroup per (query row, split of its index list): the row's entries are split into
 // gridDim.y runs of whole blocks. A null idx stands for the list 0, 1, ..., pos, -1, ... (every
 // causal candidate: the selection when a sequence has at most k keys). With one split the
@@ -364,6 +399,18 @@ attn_bf16_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restr
   const int kk = min(k - b0 * MBLK, (b1 - b0) * MBLK);
   const int nblk = b1 - b0;
 
+  // lane l's key of block blk is entry blk*64 + l of the index row
+  auto load_idx = [&](int blk) -> int {
+    const int j = blk * MBLK + lane;
+    if (blk >= nblk || j >= kk) return -1;
+    if (ir) return ir[j];
+    const int e = b0 * MBLK + j;
+    return e <= L.pos ? e : -1;
+  };
+  // the first block's entries are requested before the query block, so that the first gather
+  // waits for them only (a decode workgroup has few blocks to hide this start-up behind)
+  const int idx_first = load_idx(0);
+
   // query block of this wave as B operand: head 32w + c32, dims 16t + 8g .. +8
   bf16x8 qreg[MT];
   {
@@ -375,15 +422,6 @@ attn_bf16_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restr
   SoftmaxState st{-INFINITY, -INFINITY, 0.f};
   const float sl2 = scale * 1.4426950408889634f;
   if (threadIdx.x == 0) s_flag[0] = s_flag[1] = -1;
-
-  // lane l's key of block blk is entry blk*64 + l of the index row
-  auto load_idx = [&](int blk) -> int {
-    const int j = blk * MBLK + lane;
-    if (blk >= nblk || j >= kk) return -1;
-    if (ir) return ir[j];
-    const int e = b0 * MBLK + j;
-    return e <= L.pos ? e : -1;
-  };
   // the sequence's latent rows as a buffer (byte offsets fit 32 bits: n * 1152 < 2^31 is checked
   // on the host); out-of-range offsets would read as zero
   const __amdgpu_buffer_rsrc_t seq = __builtin_amdgcn_make_buffer_rsrc(
@@ -404,15 +442,15 @@ attn_bf16_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restr
   // A wave that needs a restart records it in s_flag[step & 1] = step (before the next barrier);
   // every wave reads the previous step's slot right after that barrier, so all waves agree.
   int step = 0;
-  for (int pass = 0;; ++pass) {
+  int ra, rb;
+  uint64_t vm_cur, vm_next;
+  prep(idx_first, ra, rb, vm_cur);
+  if (vm_cur) gather_block(buf0, seq, ra, rb, wave, lane);
+  for (;;) {
 #pragma unroll
     for (int vt = 0; vt < MDV / 32; ++vt) acc_o[vt] = (v16f){};
     st.m = st.seen;  // -inf on the first pass, the largest recorded half maximum on a restart
     st.l = 0.f;
-    int ra, rb;
-    uint64_t vm_cur, vm_next;
-    prep(load_idx(0), ra, rb, vm_cur);
-    if (vm_cur) gather_block(buf0, seq, ra, rb, wave, lane);
     int idx_next = load_idx(1);
     bool restart = false;
     for (int blk = 0; blk < nblk; blk += 2) {
@@ -444,48 +482,25 @@ attn_bf16_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restr
     __syncthreads();
     if (!restart && s_flag[(step - 1) & 1] == step - 1) restart = true;
     if (!restart) break;
+    // restart: gather the first block again
+    prep(load_idx(0), ra, rb, vm_cur);
+    if (vm_cur) gather_block(buf0, seq, ra, rb, wave, lane);
   }
 
-  // finish: combine the two lane halves' sums (same head), normalise, store
+  // finish: combine the two lane halves' sums (same head), normalise, store (the block buffers
+  // are free after the last barrier: each wave stages its 32 heads' rows in 32 KB of them)
   const float ltot = st.l + __shfl_xor(st.l, 32);
   const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
   const int head = 32 * wave + c32;
-  if (nsplit > 1) {
-    const int64_t rh = ((int64_t)split * T + r) * MH + head;
-    uint16_t* po = part_o + rh * MDV;
-#pragma unroll
-    for (int vt = 0; vt < MDV / 32; ++vt) {
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        uint2 pk;
-        pk.x = (uint32_t)f32_to_bf16_rne(acc_o[vt][4 * i4 + 0] * inv) |
-               ((uint32_t)f32_to_bf16_rne(acc_o[vt][4 * i4 + 1] * inv) << 16);
-        pk.y = (uint32_t)f32_to_bf16_rne(acc_o[vt][4 * i4 + 2] * inv) |
-               ((uint32_t)f32_to_bf16_rne(acc_o[vt][4 * i4 + 3] * inv) << 16);
-        *reinterpret_cast<uint2*>(po + 32 * vt + 8 * i4 + 4 * g) = pk;
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if (g == 0) part_lse[rh] = ltot > 0.f ? st.m + __log2f(ltot) : -INFINITY;
-    return;
+  uint8_t* const stage = (wave < 2 ? buf0 : buf1) + (wave & 1) * (32 * MDV * 2);
+  const int64_t rh = ((int64_t)(nsplit > 1 ? split * T : 0) + r) * MH + head;
+  store_head_rows((nsplit > 1 ? part_o : out) + (rh - c32) * MDV, acc_o, inv, stage, lane);
+  if (g == 0) {
+    // log2-sum-exp (-inf for no valid entry, NaN after non-finite logits)
+    const float l2 = ltot == 0.f ? -INFINITY : st.m + __log2f(ltot);
+    if (nsplit > 1) part_lse[rh] = l2;
+    else if (lse) lse[rh] = l2 * 0.6931471805599453f;
   }
-  uint16_t* orow = out + ((int64_t)r * MH + head) * MDV;
-#pragma unroll
-  for (int vt = 0; vt < MDV / 32; ++vt) {
-#pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      const int v0 = 32 * vt + 8 * i4 + 4 * g;
-      uint2 pk;
-      pk.x = (uint32_t)f32_to_bf16_rne(acc_o[vt][4 * i4 + 0] * inv) |
-             ((uint32_t)f32_to_bf16_rne(acc_o[vt][4 * i4 + 1] * inv) << 16);
-      pk.y = (uint32_t)f32_to_bf16_rne(acc_o[vt][4 * i4 + 2] * inv) |
-             ((uint32_t)f32_to_bf16_rne(acc_o[vt][4 * i4 + 3] * inv) << 16);
-      *reinterpret_cast<uint2*>(orow + v0) = pk;
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  if (lse && g == 0)
-    lse[(int64_t)r * MH + head] = ltot > 0.f ? (st.m + __log2f(ltot)) * 0.6931471805599453f : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------- alignment target
@@ -735,7 +750,12 @@ attn_combine_kernel(int T, int nsplit, const uint16_t* __restrict__ part_o,
   if (rh >= (int64_t)T * MH) return;
   const int64_t stride = (int64_t)T * MH;
   float M = -INFINITY;
-  for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, part_lse[sp * stride + rh]);
+  bool nan_part = false;
+  for (int sp = 0; sp < nsplit; ++sp) {
+    const float ls = part_lse[sp * stride + rh];
+    nan_part |= ls != ls;
+    M = fmaxf(M, ls);
+  }
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
   if (M != -INFINITY) {
@@ -753,14 +773,16 @@ attn_combine_kernel(int T, int nsplit, const uint16_t* __restrict__ part_o,
       }
     }
   }
-  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  // a NaN partial (non-finite logits in that split) makes the head's output and lse NaN
+  const float inv = nan_part ? __builtin_nanf("") : wsum > 0.f ? 1.f / wsum : 0.f;
   uint4 pk;
-  pk.x = (uint32_t)f32_to_bf16_rne(acc[0] * inv) | ((uint32_t)f32_to_bf16_rne(acc[1] * inv) << 16);
-  pk.y = (uint32_t)f32_to_bf16_rne(acc[2] * inv) | ((uint32_t)f32_to_bf16_rne(acc[3] * inv) << 16);
-  pk.z = (uint32_t)f32_to_bf16_rne(acc[4] * inv) | ((uint32_t)f32_to_bf16_rne(acc[5] * inv) << 16);
-  pk.w = (uint32_t)f32_to_bf16_rne(acc[6] * inv) | ((uint32_t)f32_to_bf16_rne(acc[7] * inv) << 16);
+  pk.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+  pk.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+  pk.z = pack_bf16x2(acc[4] * inv, acc[5] * inv);
+  pk.w = pack_bf16x2(acc[6] * inv, acc[7] * inv);
   *reinterpret_cast<uint4*>(out + rh * MDV + 8 * lane) = pk;
-  if (lse && lane == 0) lse[rh] = wsum > 0.f ? (M + __log2f(wsum)) * 0.6931471805599453f : -INFINITY;
+  if (lse && lane == 0)
+    lse[rh] = nan_part ? __builtin_nanf("") : wsum > 0.f ? (M + __log2f(wsum)) * 0.6931471805599453f : -INFINITY;
 }
 
 // Splits of each row's index list: batches with fewer rows than compute units (decode) split

@@ -15,16 +15,24 @@ struct RowLoc {
   int n;
 };
 
-// Largest b with cu[b] <= r (cu is non-decreasing, cu[0] = 0 <= r < cu[B]).
+// Largest b with cu[b] <= r (cu is non-decreasing, cu[0] = 0 <= r < cu[B]; r wave-uniform). All
+// 64 lanes of the wave take part: each round tests 64 evenly spaced candidates at once (the true
+// ones are a prefix of the lanes), so a batch of up to 64 sequences costs one round of loads where
+// a binary search would chain log2(B) dependent loads.
 __device__ __forceinline__ int find_seq(const int32_t* __restrict__ cu, int B, int r) {
-  int lo = 0, hi = B - 1;
+  const int lane = (int)__lane_id();
+  int lo = 0, hi = B - 1;   // invariant: cu[lo] <= r < cu[hi + 1]
   while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if (__ldg(cu + mid) <= r) lo = mid; else hi = mid - 1;
+    const int step = (hi - lo + 63) >> 6;   // >= 1
+    const int p = lo + (lane + 1) * step;   // candidates lo + step .. lo + 64 step
+    const bool t = p <= hi && __ldg(cu + p) <= r;
+    lo += __popcll(__ballot(t)) * step;     // the largest true candidate (or lo)
+    hi = min(hi, lo + step - 1);            // the next candidate is false or beyond hi
   }
   return lo;
 }
 
+// (every lane of the wave calls it: see find_seq)
 __device__ __forceinline__ RowLoc locate_row(const int32_t* __restrict__ cu_q,
                                              const int32_t* __restrict__ cu_k, int B, int r) {
   RowLoc L;

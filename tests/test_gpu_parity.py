@@ -350,6 +350,67 @@ def test_attention_edge_indices(gpu):
     assert np.all(oracle.decode(outs[3]) == 0) and np.all(lses[3] == -np.inf)
 
 
+@pytest.mark.parametrize("T", [300, 3])
+def test_attention_reference_restart(gpu, T):
+    """Latent rows whose rope part is 64 times larger in the second half of every 64-entry block:
+    those logits exceed the reference taken from the first half by far more than the weights'
+    fp32 range allows, so rows restart with a larger reference (T = 300: one workgroup per row;
+    T = 3: each row split into one-block runs, each of which restarts, then merged)."""
+    nk, k = 2048, 1024
+    wl = dg.custom(name="restart", seqlens_q=[T], seqlens_k=[nk], H=128, d_qk=576, d_v=512,
+                   idx_dtype="fp8", attn_dtype="bf16", wid=33, k=k)
+    x = dg.gen_inputs(wl, "normal", seed=4, parts=("attn",))
+    q, kv = oracle.decode(x["q"]), oracle.decode(x["kv"])
+    q[..., 512:] *= 2.0                                  # powers of two: exact in bf16
+    kv[(np.arange(nk) // 32) % 2 == 1, 512:] *= 64.0
+    x["q"], x["kv"] = dg.to_bf16_bits(q), dg.to_bf16_bits(kv)
+    idx = np.tile(np.arange(k, dtype=np.int32), (T, 1))
+    seqs = gpu.Seqs(wl.cu_seqlens_q, wl.cu_seqlens_k)
+    out, lse = gpu.sparse_mla_attn(seqs, dev(x["q"]), dev(x["kv"]), dev(idx), wl.scale, 512)
+    torch.cuda.synchronize()
+    sq = Seqs(wl.cu_seqlens_q, wl.cu_seqlens_k)
+    outs, lses = to_np_bf16(out), lse.cpu().numpy()
+    for r in range(0, T, 7 if T > 50 else 1):
+        o, l = oracle.attn_row(sq, x["q"], x["kv"], idx[r], wl.scale, 512, r)
+        err = np.abs(oracle.decode(outs[r]) - o)
+        # the weights are nearly one-hot here, so outputs are single latent values (up to ~4.5):
+        # the bf16 rounding of the weights (2^-9 relative, in the numerator only) and of the
+        # output (2^-9 relative) reach one bf16 step of such values, beyond the absolute 2e-2
+        assert np.all(err <= 2e-2 + np.abs(o) * 2.0 ** -7), f"row {r}: worst {np.max(err - np.abs(o) * 2.0 ** -7)}"
+        assert err.mean() <= 2e-3, f"row {r}: mean {err.mean()}"
+        assert np.all(np.abs(lses[r] - l) <= 1e-3), f"row {r}: lse {np.max(np.abs(lses[r] - l))}"
+
+
+@pytest.mark.parametrize("T", [4, 260])
+def test_attention_nonfinite_query(gpu, T):
+    """A NaN or an infinity in one head's query makes only that head's output non-finite (T = 4:
+    split rows, merged; T = 260: one workgroup per row): the other heads match the oracle, and
+    the row does not keep restarting (no larger reference exists for such logits)."""
+    nk, k = 600, 512
+    wl = dg.custom(name="nonfinite", seqlens_q=[T], seqlens_k=[nk], H=128, d_qk=576, d_v=512,
+                   idx_dtype="fp8", attn_dtype="bf16", wid=34, k=k)
+    x = dg.gen_inputs(wl, "normal", seed=6, parts=("attn",))
+    q = oracle.decode(x["q"])
+    bad = {0: (5, np.nan), 1: (40, np.inf), 2: (100, -np.inf)}
+    for r, (h, v) in bad.items():
+        q[r, h, 3] = v
+    x["q"] = dg.to_bf16_bits(q)
+    idx = np.tile(np.arange(k, dtype=np.int32), (T, 1))
+    seqs = gpu.Seqs(wl.cu_seqlens_q, wl.cu_seqlens_k)
+    out, lse = gpu.sparse_mla_attn(seqs, dev(x["q"]), dev(x["kv"]), dev(idx), wl.scale, 512)
+    torch.cuda.synchronize()
+    sq = Seqs(wl.cu_seqlens_q, wl.cu_seqlens_k)
+    outs = oracle.decode(to_np_bf16(out))
+    for r in sorted(set(bad) | set(range(0, T, 37))):
+        o, _ = oracle.attn_row(sq, x["q"], x["kv"], idx[r], wl.scale, 512, r)
+        keep = np.ones(128, bool)
+        if r in bad:
+            keep[bad[r][0]] = False
+            assert not np.isfinite(outs[r, bad[r][0]]).all(), f"row {r}: the head with a non-finite query"
+        err = np.abs(outs[r, keep] - o[keep])
+        assert err.max() <= 2e-2 and err.mean() <= 2e-3, f"row {r}: max {err.max()} mean {err.mean()}"
+
+
 def test_topk_ties_and_zeros(gpu):
     """Many equal scores and signed zeros: lower positions win, +0 == -0."""
     T, n, k = 6, 3000, 100
