@@ -35,7 +35,9 @@
  *     problem (thread-local text). A failed kernel launch returns DSA_ERR_HIP. Faults inside a
  *     kernel surface at the caller's next stream synchronisation. No C++ exception crosses
  *     this interface.
- *   - Inputs must be finite; NaN or infinite inputs give unspecified results.
+ *   - Inputs must be finite; NaN or infinite inputs give unspecified values. Every call still
+ *     terminates on them, and in the attention a head whose logits are not finite only makes
+ *     that head's output (and lse) non-finite.
  */
 #ifndef DSA_H
 #define DSA_H
