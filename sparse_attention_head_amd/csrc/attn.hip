@@ -7,17 +7,22 @@
 // the query heads). Key = the whole d_qk-dim row, value = its first d_v
 // dims.
 //
-// BF16 matrix path (H = 128, d_qk = 576, d_v = 512), one workgroup per query row, 4 waves, wave w
-// owns heads 32w..32w+31:
-//   * the selected rows are gathered 64 at a time from HBM straight into LDS with
-//     global_load_lds_dwordx4 (no register staging), double buffered: 2 x 72 KB;
-//   * S^T = K Q^T (M = 64 keys, N = 32 heads, K = 576) with v_mfma_f32_32x32x16_bf16; the query
-//     block of the wave stays in registers as the B operand for the whole row;
-//   * online softmax in fp32 on S^T (each lane owns one head, so the running max and sum are
-//     per lane); rescaling of the output is skipped while the running max grows by < 2^8;
-//   * O^T += V^T P^T (M = 512 value dims, N = 32 heads, K = 64 keys); P never leaves registers:
+// BF16 matrix path (H = 128, d_qk = 576, d_v = 512), one workgroup per query row (or per run of
+// whole blocks of its list, for batches with fewer rows than compute units), 4 waves, wave w owns
+// heads 32w..32w+31:
+//   * the selected rows are gathered 64 at a time from memory straight into LDS with
+//     buffer_load_dwordx4 ... lds (no register staging), double buffered: 2 x 72 KB;
+//   * S^T = K Q^T (M = 32 keys per half block, N = 32 heads, K = 576) with
+//     v_mfma_f32_32x32x16_bf16; the query block of the wave stays in registers as the B operand
+//     for the whole row;
+//   * softmax weights in fp32 against a reference fixed for a whole pass over the row (each lane
+//     owns one head), so the output accumulators are never rescaled; a half block whose weights
+//     would overflow restarts the row with a larger reference;
+//   * O^T += V^T P^T (M = 512 value dims, N = 32 heads, K = 32 keys); P never leaves registers:
 //     the S^T accumulator layout is used directly as the B operand, and V^T is read from LDS with
-//     the same permutation of the key index.
+//     the same permutation of the key index;
+//   * the normalised rows go back to memory through LDS, one head's whole row per store; split
+//     rows write bf16 partial rows and log2-sum-exps that attn_combine_kernel merges.
 // LDS layout of a gathered block (16-byte slots): chunk c (dims 8c..8c+7) of key s lives in slot
 //   (c / 8) * 512 + (s / 8) * 64 + (s % 8) * 8 + ((c % 8) ^ kv_swz(s % 16)).
 // One DMA instruction fills 64 consecutive slots = 8 chunks of 8 keys, i.e. 8 whole 128-byte

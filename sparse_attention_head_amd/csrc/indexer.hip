@@ -23,6 +23,10 @@
 // lane groups are added with cross-lane swaps at the end of each key block.
 // The K (d_I) index is split across lane groups identically for A (queries) and B (keys), so the
 // contraction does not depend on the hardware's byte order within a lane.
+// That is the mapping of the decode (one row per workgroup) kernel. The prefill kernel further
+// down swaps the roles (keys as the A operand, 4 rows x 4 heads per tile as B), stages the keys
+// in LDS for all 8 waves of a workgroup, and halves the epilogue with the split ReLU identity
+// and an extra matrix tile for its linear term.
 #include "dsa_internal.h"
 #include "device_common.h"
 
@@ -474,9 +478,9 @@ __device__ __forceinline__ void stage_pipeline(const uint8_t* __restrict__ buf, 
 // Workgroup = 8 waves x 4 rows = 32 query rows of one sequence against a chunk of keys. The keys
 // stream through a ring of LDS stages (256 keys = 32 KB each) filled by DMA (global_load_lds); all
 // waves share them. Inside a stage, key s occupies 128 bytes whose 16-byte chunk c sits at
-// position c ^ key_swz(s % 16). A B-operand read of 16 consecutive keys (lane l: key l%16, one
-// chunk per lane) then touches distinct banks both within each group of 8 lanes (32 four-byte
-// banks cover one key row) and within each group of 16 lanes (64 banks cover two rows).
+// position c ^ key_swz(s % 16). A read of 16 consecutive keys for the A operand (lane l: key
+// l%16, one chunk per lane) then touches distinct banks both within each group of 8 lanes (32
+// four-byte banks cover one key row) and within each group of 16 lanes (64 banks cover two rows).
 __device__ __forceinline__ int key_swz(int s16) { return ((s16 >> 1) ^ ((s16 & 1) << 2)) & 7; }
 
 constexpr int PF_W = 8;                 // waves per workgroup
