@@ -754,27 +754,35 @@ attn_combine_kernel(int T, int nsplit, const uint16_t* __restrict__ part_o,
   const int64_t rh = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // row * H + head
   if (rh >= (int64_t)T * MH) return;
   const int64_t stride = (int64_t)T * MH;
-  float M = -INFINITY;
-  bool nan_part = false;
-  for (int sp = 0; sp < nsplit; ++sp) {
-    const float ls = part_lse[sp * stride + rh];
-    nan_part |= ls != ls;
-    M = fmaxf(M, ls);
-  }
+  // lane s < nsplit holds split s's log2-sum-exp (nsplit <= 32)
+  const float my_ls = lane < nsplit ? part_lse[lane * stride + rh] : -INFINITY;
+  float M = my_ls;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  const bool nan_part = __any(my_ls != my_ls);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
   if (M != -INFINITY) {
-    for (int sp = 0; sp < nsplit; ++sp) {
-      const float ls = part_lse[sp * stride + rh];
-      if (ls == -INFINITY) continue;
-      const float w = __builtin_amdgcn_exp2f(ls - M);
-      wsum += w;
-      const uint4 pk = *reinterpret_cast<const uint4*>(part_o + (sp * stride + rh) * MDV + 8 * lane);
-      const uint32_t wd[4] = {pk.x, pk.y, pk.z, pk.w};
+    // four splits per step, their partial rows requested together (an empty split weighs
+    // 2^-inf = 0; steps past the last split re-read split 0 with weight 0)
+    for (int sp = 0; sp < nsplit; sp += 4) {
+      uint4 pk[4];
+      float w[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        acc[2 * j] += w * __uint_as_float(wd[j] << 16);
-        acc[2 * j + 1] += w * __uint_as_float(wd[j] & 0xFFFF0000u);
+      for (int i = 0; i < 4; ++i) {
+        const int s2 = sp + i < nsplit ? sp + i : 0;
+        pk[i] = *reinterpret_cast<const uint4*>(part_o + (s2 * stride + rh) * MDV + 8 * lane);
+        w[i] = sp + i < nsplit ? __builtin_amdgcn_exp2f(__shfl(my_ls, sp + i) - M) : 0.f;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        wsum += w[i];
+        const uint32_t wd[4] = {pk[i].x, pk[i].y, pk[i].z, pk[i].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[2 * j] += w[i] * __uint_as_float(wd[j] << 16);
+          acc[2 * j + 1] += w[i] * __uint_as_float(wd[j] & 0xFFFF0000u);
+        }
       }
     }
   }
