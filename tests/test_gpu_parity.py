@@ -475,14 +475,18 @@ FULL_ROWS = {
 }
 
 
+@pytest.mark.parametrize("variant", ["int", "normal"])
 @pytest.mark.parametrize("name", list(FULL_ROWS))
-def test_full_size_sampled_rows(gpu, name):
-    """The shapes and launch configuration the benchmark times, int variant for the indexer:
-    indices bit-exact and attention within tolerance on sampled rows."""
+def test_full_size_sampled_rows(gpu, name, variant):
+    """The shapes and launch configuration the benchmark times, on sampled rows: int variant,
+    scores and indices bit-exact; N(0,1) variant (the benchmark's data), scores within the error
+    bound and the top-k eps-valid; attention within tolerance on the GPU's indices."""
     wl = dg.workload(name)
-    say(f"full {name}: generating T={wl.T} Nk={wl.Nk}")
-    x = dg.gen_inputs(wl, "int", seed=0)
+    say(f"full {name} ({variant}): generating T={wl.T} Nk={wl.Nk}")
+    x = dg.gen_inputs(wl, variant, seed=0)
     say("  running")
     res = run_all(gpu, wl, x)
     say("  checking")
-    check_rows(wl, x, res, FULL_ROWS[name], "int", DELTA_FP8_MFMA)
+    ov = check_rows(wl, x, res, FULL_ROWS[name], variant, DELTA_FP8_MFMA)
+    if ov:
+        say(f"  mean overlap with the oracle set {np.mean(ov):.4f}")
