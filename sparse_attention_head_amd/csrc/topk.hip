@@ -525,7 +525,8 @@ topk_reg_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restri
 // over the row with about two vector instructions per score, so that the pass runs at memory
 // speed, and workgroups of eight waves with 76 KB of LDS, two per compute unit, so that the
 // selection work of one row overlaps the streaming of another.
-//  1. A sample of the row (all of it up to 8192 positions, else 8 evenly spaced runs of 1024) is
+//  1. A sample of the row (all of it up to 8192 positions, else 8 evenly spaced runs of 256, 512
+//     or 1024 positions, about n/16 in all) is
 //     kept in LDS; two radix digits (22 key bits) locate its `want`-th largest key and the floor F
 //     is that 22-bit bin's lower edge. With the whole row as sample want = k, so at least k keys
 //     reach F; otherwise want = 1.3 k S / n aims at about 1.3 k keys (3 sigma above k and about
@@ -553,7 +554,7 @@ constexpr int TS_GCAP = 3392;              // group slots
 constexpr int TS_GSTRIDE = TS_GCAP + 64;   // words per group array: the slots, then one spare per lane
 static_assert(TS_GSTRIDE % 64 == 0, "group arrays are 256-byte aligned (paired-store offsets)");
 constexpr int TS_HCAP = 4096;              // keys in the compacted list
-constexpr int TS_SEG = 1024;               // positions per sample run
+constexpr int TS_SEG = 1024;               // positions per sample run, at most
 constexpr int TS_SEGS = 8;
 constexpr int TS_SAMPLE = TS_SEG * TS_SEGS;   // 8192
 constexpr int TS_MAXEQ = 2048;             // tied keys handled in LDS
@@ -641,16 +642,17 @@ topk_stream_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __res
 
   // 1. sample and floor
   const bool whole = n <= TS_SAMPLE;
-  const int S = whole ? n : TS_SAMPLE;
+  // a sample of about n/16 positions (2048 .. 8192) in 8 evenly spaced runs: the floor's target
+  // rank in it (~166 at k = 2048) stays the same for every row length
+  const int seg = n >= 12 * TS_SAMPLE ? TS_SEG : n >= 6 * TS_SAMPLE ? TS_SEG / 2 : TS_SEG / 4;
+  const int S = whole ? n : TS_SEGS * seg;
   if (whole) {
     for (int i = tid; i < n; i += TS_THREADS) region[i] = float_to_ordered(row[i]);
   } else {
-#pragma unroll
-    for (int j = 0; j < TS_SEGS; ++j) {
-      const int start = (int)((int64_t)j * (n - TS_SEG) / (TS_SEGS - 1));
-#pragma unroll
-      for (int c = 0; c < TS_SEG / TS_THREADS; ++c)
-        region[j * TS_SEG + c * TS_THREADS + tid] = float_to_ordered(row[start + c * TS_THREADS + tid]);
+    for (int i = tid; i < S; i += TS_THREADS) {
+      const int j = i / seg, o = i - j * seg;
+      const int start = (int)((int64_t)j * (n - seg) / (TS_SEGS - 1));
+      region[i] = float_to_ordered(row[start + o]);
     }
   }
   if (tid == 0) {
