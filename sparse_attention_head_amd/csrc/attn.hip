@@ -156,6 +156,33 @@ __device__ __forceinline__ int kv_swz(int s16) {
   return b0 | (b1 << 1) | (b2 << 2);
 }
 
+// One 16-byte-per-lane LDS DMA (buffer_load_dwordx4 ... lds): lane i's 16 bytes at voffset +
+// soff of the resource land at LDS byte address lds_base + lds_off + 16 i (lds_base, lds_off and
+// soff wave-uniform). Written as inline assembly so that the compiler does not track it: its
+// waits for LDS DMA are per LDS variable and cannot tell the two block buffers apart for the
+// transposing reads, so the value product of the current block would wait for the next block's
+// gather (an HBM round trip in decode). The callers wait (vmcnt(0)) and synchronise before
+// reading a buffer the DMA wrote. M0 is saved and restored around it.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds_base, int lds_off,
+                                          int voff, int soff) {
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_add_u32 m0, %1, %2\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %3, %4, %5 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_base), "s"(lds_off), "v"(voff), "s"(rsrc), "s"(soff)
+      : "memory", "scc");
+}
+
+// LDS byte address of a shared-memory pointer, wave-uniform.
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+  return __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p);
+}
+
 // Issue the gather of one block into `buf`. Wave w copies key groups R = 2w + u (u = 0, 1; keys
 // 8R .. 8R+7) for chunk groups G = 0..8. In each instruction lane l covers key 8R + l/8 (key % 16
 // = 8u + l/8) and chunk 8G + ((l % 8) ^ kv_swz(8u + l/8)), which lands in slot G*512 + R*64 + l:
@@ -164,6 +191,7 @@ __device__ __forceinline__ int kv_swz(int s16) {
 // Buffer (not global) loads: the compiler then keeps exact LDS-read waits while they are in flight.
 __device__ __forceinline__ void gather_block(uint8_t* buf, __amdgpu_buffer_rsrc_t seq, int row0,
                                              int row1, int wave, int lane, int u0 = 0, int u1 = 2) {
+  const uint32_t lbase = lds_addr(buf);
 #pragma unroll
   for (int u = u0; u < u1; ++u) {
     const int sw = ((lane & 7) ^ kv_swz(8 * u + (lane >> 3))) * 16;
@@ -171,9 +199,7 @@ __device__ __forceinline__ void gather_block(uint8_t* buf, __amdgpu_buffer_rsrc_
     const int R = 2 * wave + u;
 #pragma unroll
     for (int G = 0; G < MCH / 8; ++G)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          seq, (__attribute__((address_space(3))) void*)(buf + (G * 512 + R * 64) * 16), 16,
-          voff + G * 128, 0, 0, 0);
+      lds_dma16(seq, lbase, (G * 512 + R * 64) * 16, voff, G * 128);
   }
 }
 
@@ -220,6 +246,7 @@ __device__ __forceinline__ bool attend_half(const uint8_t* buf, int kbase, uint3
   auto kop = [&](int t) -> bf16x8 {
     return *reinterpret_cast<const bf16x8*>(kb[t & 3] + (t >> 2) * 8192);
   };
+  const uint32_t gbase = gdst ? lds_addr(gdst) : 0u;
   v16f s = {};
   {
     bf16x8 ka[KRING];
@@ -232,9 +259,8 @@ __device__ __forceinline__ bool attend_half(const uint8_t* buf, int kbase, uint3
       // gather load i = t/2 of the next block (key group 2*wave + i/9, chunk group i%9) every
       // other matrix instruction
       if ((t & 1) == 0 && gdst)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            gseq, (__attribute__((address_space(3))) void*)(gdst + ((t / 2) / 9) * 1024 + ((t / 2) % 9) * 8192),
-            16, (t / 2) / 9 ? gvoff1 : gvoff0, ((t / 2) % 9) * 128, 0, 0);
+        lds_dma16(gseq, gbase, ((t / 2) / 9) * 1024 + ((t / 2) % 9) * 8192,
+                  (t / 2) / 9 ? gvoff1 : gvoff0, ((t / 2) % 9) * 128);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
