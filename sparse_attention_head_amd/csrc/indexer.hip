@@ -223,38 +223,44 @@ indexer_fp8_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __res
   // key blocks: prefill walks every block of [kbeg, kend); decode wave w takes blocks w, w+W, ...
   const int step = DECODE ? 16 * W : 16;
   const int first = DECODE ? kbeg + 16 * wave : kbeg;
-  v8i ring[PF];
-  float kring[PF];   // the lane's key scale, loaded with the key (KS only)
-#pragma unroll
-  for (int p = 0; p < PF; ++p) {
-    ring[p] = load_slice(k, k0 + min(first + p * step + c, n - 1), g);
-    if (KS) kring[p] = kscale[k0 + min(first + p * step + c, n - 1)];
-  }
-
-  for (int kb0 = first; kb0 < kend; kb0 += PF * step) {
+  // two register sets of PF key slices used in turn (no register copies, so each block waits
+  // for its own loads only): blocks of one set are scored while the other set's loads are in
+  // flight
+  v8i ra[PF], rb[PF];
+  float ka[PF], kb_[PF];   // the lanes' key scales, loaded with the keys (KS only)
+  auto load_set = [&](int base, v8i (&r)[PF], float (&ks)[PF]) {
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
-      const int kb = kb0 + p * step;
-      const v8i cur = ring[p];
-      ring[p] = load_slice(k, k0 + min(kb + PF * step + c, n - 1), g);
-      float kcur = 1.f;
-      if (KS) {
-        kcur = kring[p];
-        kring[p] = kscale[k0 + min(kb + PF * step + c, n - 1)];
-      }
+      const int key = k0 + min(base + p * step + c, n - 1);
+      r[p] = load_slice(k, key, g);
+      if (KS) ks[p] = kscale[key];
+    }
+  };
+  auto score_set = [&](int base, const v8i (&r)[PF], const float (&ks)[PF]) {
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+      const int kb = base + p * step;
       if (kb < kend) {
-        float acc = score_block<RW>(a, cur, wv);
+        float acc = score_block<RW>(a, r[p], wv);
         // keep the epilogue in this block (it would otherwise sink into the store's branch and
         // lose its interleaving with the matrix instructions)
         asm volatile("" ::"v"(acc));
         if (RW <= 2) acc += __shfl_xor(acc, 16);
         if (RW == 1) acc += __shfl_xor(acc, 32);
-        if (KS) acc *= kcur;
+        if (KS) acc *= ks[p];
         const int s = kb + c;
         const bool owner = (RW == 4) || (RW == 2 ? (g & 1) == 0 : g == 0);
         if (owner && row_ok && s <= my_pos && s < kend) srow[s] = acc;
       }
     }
+  };
+  load_set(first, ra, ka);
+  for (int kb0 = first; kb0 < kend; kb0 += 2 * PF * step) {
+    load_set(kb0 + PF * step, rb, kb_);
+    score_set(kb0, ra, ka);
+    if (kb0 + PF * step >= kend) break;
+    load_set(kb0 + 2 * PF * step, ra, ka);
+    score_set(kb0 + PF * step, rb, kb_);
   }
 }
 
