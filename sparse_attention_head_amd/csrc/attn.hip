@@ -162,7 +162,8 @@ __device__ __forceinline__ int kv_swz(int s16) {
 // waits for LDS DMA are per LDS variable and cannot tell the two block buffers apart for the
 // transposing reads, so the value product of the current block would wait for the next block's
 // gather (an HBM round trip in decode). The callers wait (vmcnt(0)) and synchronise before
-// reading a buffer the DMA wrote. M0 is saved and restored around it.
+// reading a buffer the DMA wrote. M0 is saved and restored around it, one wait state after
+// its write (the hazard the compiler observes for its own LDS DMA) and one before its restore.
 __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds_base, int lds_off,
                                           int voff, int soff) {
   int saved;
@@ -171,6 +172,7 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t 
       "s_add_u32 m0, %1, %2\n\t"
       "s_nop 0\n\t"
       "buffer_load_dwordx4 %3, %4, %5 offen lds\n\t"
+      "s_nop 0\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
       : "s"(lds_base), "s"(lds_off), "v"(voff), "s"(rsrc), "s"(soff)
@@ -183,15 +185,30 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
       (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p);
 }
 
+// One gather instruction, untracked (UT: inline assembly, lds_dma16) or through the builtin,
+// which the compiler tracks. The untracked form pays in decode, where the value product would
+// otherwise wait for the next block's gather from HBM; the single-split prefill launch keeps the
+// builtin.
+template <bool UT>
+__device__ __forceinline__ void gather16(__amdgpu_buffer_rsrc_t rsrc, uint8_t* lds, int lds_off, int voff,
+                                         int soff) {
+  if constexpr (UT) {
+    lds_dma16(rsrc, lds_addr(lds), lds_off, voff, soff);
+  } else {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rsrc, (__attribute__((address_space(3))) void*)(lds + lds_off), 16, voff, soff, 0, 0);
+  }
+}
+
 // Issue the gather of one block into `buf`. Wave w copies key groups R = 2w + u (u = 0, 1; keys
 // 8R .. 8R+7) for chunk groups G = 0..8. In each instruction lane l covers key 8R + l/8 (key % 16
 // = 8u + l/8) and chunk 8G + ((l % 8) ^ kv_swz(8u + l/8)), which lands in slot G*512 + R*64 + l:
 // the lane-linear LDS writes of the DMA match the swizzled layout. row_u is the sequence-local
 // latent row of key 8(2w + u) + l/8; `seq` addresses the sequence's rows (n * 1152 bytes).
 // Buffer (not global) loads: the compiler then keeps exact LDS-read waits while they are in flight.
+template <bool UT>
 __device__ __forceinline__ void gather_block(uint8_t* buf, __amdgpu_buffer_rsrc_t seq, int row0,
                                              int row1, int wave, int lane, int u0 = 0, int u1 = 2) {
-  const uint32_t lbase = lds_addr(buf);
 #pragma unroll
   for (int u = u0; u < u1; ++u) {
     const int sw = ((lane & 7) ^ kv_swz(8 * u + (lane >> 3))) * 16;
@@ -199,7 +216,7 @@ __device__ __forceinline__ void gather_block(uint8_t* buf, __amdgpu_buffer_rsrc_
     const int R = 2 * wave + u;
 #pragma unroll
     for (int G = 0; G < MCH / 8; ++G)
-      lds_dma16(seq, lbase, (G * 512 + R * 64) * 16, voff, G * 128);
+      gather16<UT>(seq, buf, (G * 512 + R * 64) * 16, voff, G * 128);
   }
 }
 
@@ -226,6 +243,7 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const uint8_t* p) {
 // reference by too much (see SoftmaxState); the caller then restarts the row. LDS operands are
 // prefetched several MFMAs ahead; scheduling barriers keep the compiler from hoisting further
 // (which would cost registers the resident query block needs).
+template <bool UT>
 __device__ __forceinline__ bool attend_half(const uint8_t* buf, int kbase, uint32_t vmask,
                                             const bf16x8 (&qreg)[MT], v16f (&acc_o)[MDV / 32],
                                             SoftmaxState& st, float sl2, int lane,
@@ -246,7 +264,6 @@ __device__ __forceinline__ bool attend_half(const uint8_t* buf, int kbase, uint3
   auto kop = [&](int t) -> bf16x8 {
     return *reinterpret_cast<const bf16x8*>(kb[t & 3] + (t >> 2) * 8192);
   };
-  const uint32_t gbase = gdst ? lds_addr(gdst) : 0u;
   v16f s = {};
   {
     bf16x8 ka[KRING];
@@ -259,8 +276,8 @@ __device__ __forceinline__ bool attend_half(const uint8_t* buf, int kbase, uint3
       // gather load i = t/2 of the next block (key group 2*wave + i/9, chunk group i%9) every
       // other matrix instruction
       if ((t & 1) == 0 && gdst)
-        lds_dma16(gseq, gbase, ((t / 2) / 9) * 1024 + ((t / 2) % 9) * 8192,
-                  (t / 2) / 9 ? gvoff1 : gvoff0, ((t / 2) % 9) * 128);
+        gather16<UT>(gseq, gdst, ((t / 2) / 9) * 1024 + ((t / 2) % 9) * 8192,
+                     (t / 2) / 9 ? gvoff1 : gvoff0, ((t / 2) % 9) * 128);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -345,6 +362,7 @@ __device__ __forceinline__ bool attend_half(const uint8_t* buf, int kbase, uint3
 }
 
 // One gathered block of 64 keys, processed as two halves. Returns true if the row must restart.
+template <bool UT>
 __device__ __forceinline__ bool attend_block(const uint8_t* buf, uint64_t vmask,
                                              const bf16x8 (&qreg)[MT], v16f (&acc_o)[MDV / 32],
                                              SoftmaxState& st, float sl2, int lane,
@@ -361,13 +379,13 @@ __device__ __forceinline__ bool attend_block(const uint8_t* buf, uint64_t vmask,
   for (int h = 0; h < 2; ++h) {
     const uint32_t m32 = (uint32_t)(vmask >> (32 * h));
     if (m32) {
-      const bool rs = attend_half(buf, 32 * h, m32, qreg, acc_o, st, sl2, lane, gseq,
+      const bool rs = attend_half<UT>(buf, 32 * h, m32, qreg, acc_o, st, sl2, lane, gseq,
                                   pending && gon ? gdst : nullptr, gvoff0, gvoff1);
       pending = false;
       if (rs) return true;
     }
   }
-  if (pending && gon) gather_block(gbuf, seq, ra, rb, wave, lane);   // no half was computed
+  if (pending && gon) gather_block<UT>(gbuf, seq, ra, rb, wave, lane);   // no half was computed
   return false;
 }
 
@@ -405,6 +423,7 @@ __device__ __forceinline__ void store_head_rows(uint16_t* dst, const v16f (&acc_
 // workgroup writes the normalised output and lse; with several it writes, per head, its
 // normalised partial output and its partial log2-sum-exp to part_o [splits][T][H][d_v] (bf16)
 // and part_lse [splits][T][H] (fp32), which attn_combine_kernel merges.
+template <bool UT>
 __global__ void __launch_bounds__(256, 1)
 attn_bf16_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
                  const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv,
@@ -476,7 +495,7 @@ attn_bf16_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restr
   int ra, rb;
   uint64_t vm_cur, vm_next;
   prep(idx_first, ra, rb, vm_cur);
-  if (vm_cur) gather_block(buf0, seq, ra, rb, wave, lane);
+  if (vm_cur) gather_block<UT>(buf0, seq, ra, rb, wave, lane);
   for (;;) {
 #pragma unroll
     for (int vt = 0; vt < MDV / 32; ++vt) acc_o[vt] = (v16f){};
@@ -492,7 +511,7 @@ attn_bf16_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restr
       const bool gon1 = blk + 1 < nblk && vm_next;
       idx_next = load_idx(blk + 2);
       // (a block without a valid key skips both halves but still issues the second loads)
-      if (attend_block(buf0, vm_cur, qreg, acc_o, st, sl2, lane, buf1, seq, ra, rb, gon1, wave)) s_flag[step & 1] = step;
+      if (attend_block<UT>(buf0, vm_cur, qreg, acc_o, st, sl2, lane, buf1, seq, ra, rb, gon1, wave)) s_flag[step & 1] = step;
       ++step;
       vm_cur = vm_next;
       if (blk + 1 >= nblk) break;
@@ -504,7 +523,7 @@ attn_bf16_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restr
       const bool gon0 = blk + 2 < nblk && vm_next;
       idx_next = load_idx(blk + 3);
       // (a block without a valid key skips both halves but still issues the second loads)
-      if (attend_block(buf1, vm_cur, qreg, acc_o, st, sl2, lane, buf0, seq, ra, rb, gon0, wave)) s_flag[step & 1] = step;
+      if (attend_block<UT>(buf1, vm_cur, qreg, acc_o, st, sl2, lane, buf0, seq, ra, rb, gon0, wave)) s_flag[step & 1] = step;
       ++step;
       vm_cur = vm_next;
     }
@@ -515,7 +534,7 @@ attn_bf16_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restr
     if (!restart) break;
     // restart: gather the first block again
     prep(load_idx(0), ra, rb, vm_cur);
-    if (vm_cur) gather_block(buf0, seq, ra, rb, wave, lane);
+    if (vm_cur) gather_block<UT>(buf0, seq, ra, rb, wave, lane);
   }
 
   // finish: combine the two lane halves' sums (same head), normalise, store (the block buffers
@@ -663,7 +682,7 @@ align_bf16_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __rest
   uint64_t vm_cur, vm_next;
   int sidx_cur = load_idx(0);
   prep(sidx_cur, ra, rb, vm_cur);
-  if (vm_cur) gather_block(buf, seq, ra, rb, wave, lane);
+  if (vm_cur) gather_block<false>(buf, seq, ra, rb, wave, lane);
   int sidx_next = load_idx(1);
   float klacc = 0.f;   // first wave: this lane's KL terms
   // the first wave forms p and the KL terms of a block after the next barrier (the waves' head
@@ -741,7 +760,7 @@ align_bf16_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __rest
       }
     }
     __syncthreads();   // every wave is done with the buffer
-    if (gon) gather_block(buf, seq, ra, rb, wave, lane);
+    if (gon) gather_block<false>(buf, seq, ra, rb, wave, lane);
     have_prev = true;
     ok_prev = (vm_cur >> lane) & 1ull;
     sidx_prev = sidx_cur;
@@ -846,9 +865,14 @@ hipError_t launch_attn_bf16(const SeqInfo& s, const uint16_t* q, const uint16_t*
   const int ns = attn_splits(s, k);
   uint16_t* part_o = ns > 1 ? static_cast<uint16_t*>(ws) : nullptr;
   float* part_lse = ns > 1 ? reinterpret_cast<float*>(part_o + (size_t)ns * s.T * MH * MDV) : nullptr;
-  hipLaunchKernelGGL(attn_bf16_kernel, dim3(s.T, ns), dim3(256), 0, st, s.B, s.cu_q, s.cu_k, q,
-                     reinterpret_cast<const uint8_t*>(kv), idx, k, scale, out, lse, s.T, part_o,
-                     part_lse);
+  if (ns > 1)
+    hipLaunchKernelGGL(attn_bf16_kernel<true>, dim3(s.T, ns), dim3(256), 0, st, s.B, s.cu_q, s.cu_k, q,
+                       reinterpret_cast<const uint8_t*>(kv), idx, k, scale, out, lse, s.T, part_o,
+                       part_lse);
+  else
+    hipLaunchKernelGGL(attn_bf16_kernel<false>, dim3(s.T, ns), dim3(256), 0, st, s.B, s.cu_q, s.cu_k, q,
+                       reinterpret_cast<const uint8_t*>(kv), idx, k, scale, out, lse, s.T, part_o,
+                       part_lse);
   if (ns > 1)
     hipLaunchKernelGGL(attn_combine_kernel, dim3((s.T * MH + 3) / 4), dim3(256), 0, st, s.T, ns,
                        part_o, part_lse, out, lse);
