@@ -241,8 +241,9 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const uint8_t* p) {
 // One half block (32 keys starting at kbase inside the LDS block): logits, softmax weights,
 // value accumulation. Returns true (uniform over the wave) when some head's logits exceed its
 // reference by too much (see SoftmaxState); the caller then restarts the row. LDS operands are
-// prefetched several MFMAs ahead; scheduling barriers keep the compiler from hoisting further
-// (which would cost registers the resident query block needs).
+// prefetched several MFMAs ahead. The logits loop is left to the scheduler (measured ~3 % faster
+// than pinning every matrix instruction in place); in the value loop scheduling barriers keep the
+// compiler from hoisting the operand reads further (which costs time and registers).
 template <bool UT>
 __device__ __forceinline__ bool attend_half(const uint8_t* buf, int kbase, uint32_t vmask,
                                             const bf16x8 (&qreg)[MT], v16f (&acc_o)[MDV / 32],
@@ -278,7 +279,6 @@ __device__ __forceinline__ bool attend_half(const uint8_t* buf, int kbase, uint3
       if ((t & 1) == 0 && gdst)
         gather16<UT>(gseq, gdst, ((t / 2) / 9) * 1024 + ((t / 2) % 9) * 8192,
                      (t / 2) / 9 ? gvoff1 : gvoff0, ((t / 2) % 9) * 128);
-      __builtin_amdgcn_sched_barrier(0);
     }
   }
   // Softmax weights against the fixed reference st.m (log2 domain): p = 2^(sl2 * s - m). The
