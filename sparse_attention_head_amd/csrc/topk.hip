@@ -523,8 +523,9 @@ topk_reg_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restri
 // ------------------------------------------------------------------------------------------
 // Streaming variant for k <= 2048 and rows of up to 131072 candidates (any batch size): one pass
 // over the row with about two vector instructions per score, so that the pass runs at memory
-// speed, and workgroups of eight waves with 76 KB of LDS, two per compute unit, so that the
-// selection work of one row overlaps the streaming of another.
+// speed, and workgroups of sixteen waves with 76 KB of LDS, two per compute unit (the full 32
+// waves), so that the selection work of one row overlaps the streaming of another and the
+// latency-bound selection phases run on more threads.
 //  1. A sample of the row (all of it up to 8192 positions, else 8 evenly spaced runs of 256, 512
 //     or 1024 positions, about n/16 in all) is
 //     kept in LDS; two radix digits (22 key bits) locate its `want`-th largest key and the floor F
@@ -533,7 +534,7 @@ topk_reg_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restri
 //     4 sigma below the list's capacity for independent scores).
 //  2. The stream works on groups of 4 consecutive scores (one float4 per lane): a group whose
 //     maximum reaches F is appended whole, with its position, to a list in LDS (structure of
-//     arrays). Per batch of 8 groups per lane one atomic per wave reserves the slots; each lane
+//     arrays). Per batch of 4 groups per lane one atomic per wave reserves the slots; each lane
 //     then stores every group unconditionally, to its slot or, without a hit, to a spare slot of
 //     its own, so the loop has no per-group branch.
 //  3. The groups are compacted into a list of single keys >= F with their positions.
@@ -546,7 +547,7 @@ topk_reg_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restri
 //  6. The selected positions are marked in a bitmap; each thread owns a run of its words, one
 //     block-wide exclusive scan of their popcounts gives the output offsets, and every thread
 //     writes its positions in ascending order.
-constexpr int TS_THREADS = 512;
+constexpr int TS_THREADS = 1024;
 constexpr int TS_WAVES = TS_THREADS / 64;
 constexpr int TS_MAXN = 131072;            // positions covered by the bitmap
 constexpr int TS_MAXK = 2048;
@@ -561,7 +562,7 @@ constexpr int TS_MAXEQ = 2048;             // tied keys handled in LDS
 constexpr int TS_REGION = 5 * TS_GSTRIDE;  // sample | group arrays x, y, z, w, position | keys, positions, bitmap
 static_assert(TS_SAMPLE <= TS_REGION, "the sample shares the region");
 static_assert(2 * TS_HCAP + TS_MAXN / 32 <= TS_REGION, "compacted list and bitmap share the region");
-constexpr int TS_UNROLL = 8;               // float4 loads in flight per thread
+constexpr int TS_UNROLL = 4;               // float4 loads per thread and batch (two batches in flight)
 constexpr int TS_GPT = (TS_GCAP + TS_THREADS - 1) / TS_THREADS;   // groups per thread in the compaction
 
 // Largest of the four values (finite inputs: no NaN handling, which fmaxf would add per operand).
