@@ -687,7 +687,7 @@ topk_stream_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __res
   // next batch is in flight while the current one is scanned. Buffer loads: one resource per
   // batch (starting at the batch, covering the whole groups left in the row) and fixed lane
   // offsets, so no per-load address arithmetic; groups past the end read as zero (scan_batch then
-  // sets them to -inf), so every batch issues the same eight loads.
+  // sets them to -inf), so every batch issues the same TS_UNROLL loads.
   constexpr int BATCH = TS_THREADS * 4 * TS_UNROLL;
   auto load_batch = [&](int base, float4 (&v)[TS_UNROLL]) {
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
