@@ -17,7 +17,9 @@ shared latent row of d_qk dims whose first d_v dims are the value):
 Value recipe: q^I, k^I, q and the latent rows are N(0,1); w is N(0,1)/sqrt(H_I). FP8 and bf16
 tensors are produced by rounding the fp32 draws to nearest-even (torch's host cast). The
 "int" variant replaces q^I, k^I by integers uniform in [-3, 3] and w by multiples of 1/8 in
-[-1, 1], so that every indexer score is exactly representable in fp32.
+[-1, 1], so that every indexer score is exactly representable in fp32. The "e4m3" variant
+(FP8 indexer inputs only) draws q^I and k^I as uniformly random non-NaN e4m3fn codes, i.e.
+values over the format's whole exponent range (subnormals to +-448), with w as for "normal".
 
 Draws are counter-based: every tensor is generated in chunks of CHUNK leading-dim rows, chunk c
 of tensor t of workload/variant/seed uses SeedSequence([seed, workload_id, variant_id, t, c]),
@@ -36,7 +38,7 @@ CHUNK = 4096
 
 # tensor ids for the counter-based streams
 T_QI, T_KI, T_W, T_Q, T_KV, T_LEN, T_QS, T_KS = 0, 1, 2, 3, 4, 5, 6, 7
-VARIANTS = {"normal": 0, "int": 1}
+VARIANTS = {"normal": 0, "int": 1, "e4m3": 2}
 
 
 @dataclass
@@ -158,6 +160,11 @@ def _draw(seed, wid, variant, tid, rows, inner, kind, row_lo=0, row_hi=None):
             blk = np.exp2(rng.integers(-1, 1, endpoint=True, size=(hi - lo, inner))).astype(np.float32)
         elif kind == "logu":
             blk = np.exp2(rng.uniform(-2.0, 2.0, size=(hi - lo, inner))).astype(np.float32)
+        elif kind == "e4m3code":   # uniform over the 254 non-NaN codes (0x7F and 0xFF skipped)
+            c = rng.integers(0, 253, endpoint=True, size=(hi - lo, inner))
+            blk = (c + (c >= 0x7F)).astype(np.float32)
+        elif kind == "ternary":
+            blk = rng.integers(-1, 1, endpoint=True, size=(hi - lo, inner), dtype=np.int8).astype(np.float32)
         else:
             raise ValueError(kind)
         a, b = max(lo, row_lo), min(hi, row_hi)
@@ -196,14 +203,18 @@ def gen_inputs(wl: Workload, variant: str = "normal", seed: int = 0, parts=("idx
     T, Nk = wl.T, wl.Nk
     out = dict(cu_seqlens_q=wl.cu_seqlens_q, cu_seqlens_k=wl.cu_seqlens_k)
     if "idx" in parts:
-        qk_kind = "int3" if variant == "int" else "normal"
+        if variant == "e4m3" and wl.idx_dtype != "fp8":
+            raise ValueError("the e4m3 variant needs FP8 indexer inputs")
+        qk_kind = {"int": "int3", "e4m3": "e4m3code"}.get(variant, "normal")
         qI = _draw(seed, wl.wid, v, T_QI, T, wl.H_I * wl.d_I, qk_kind).reshape(T, wl.H_I, wl.d_I)
         kI = _draw(seed, wl.wid, v, T_KI, Nk, wl.d_I, qk_kind)
         if variant == "int":
             w = _draw(seed, wl.wid, v, T_W, T, wl.H_I, "eighths")
         else:
             w = _draw(seed, wl.wid, v, T_W, T, wl.H_I, "normal") / np.float32(math.sqrt(wl.H_I))
-        if wl.idx_dtype == "fp8":
+        if variant == "e4m3":   # the draws are the codes themselves
+            qI, kI = qI.astype(np.uint8), kI.astype(np.uint8)
+        elif wl.idx_dtype == "fp8":
             qI, kI = to_fp8_e4m3fn_bytes(qI), to_fp8_e4m3fn_bytes(kI)
         out.update(qI=qI, kI=kI, w=np.ascontiguousarray(w, np.float32))
     if "attn" in parts:
@@ -214,6 +225,40 @@ def gen_inputs(wl: Workload, variant: str = "normal", seed: int = 0, parts=("idx
             q, kv = to_bf16_bits(q), to_bf16_bits(kv)
         out.update(q=q, kv=kv)
     return out
+
+
+def gen_ternary(wl: Workload, seed: int = 0) -> dict:
+    """Indexer queries and keys with entries in {-1, 0, 1} (FP8 codes for FP8 workloads, else
+    float32), for cases whose head weights the caller constructs."""
+    qI = _draw(seed, wl.wid, 3, T_QI, wl.T, wl.H_I * wl.d_I, "ternary").reshape(wl.T, wl.H_I, wl.d_I)
+    kI = _draw(seed, wl.wid, 3, T_KI, wl.Nk, wl.d_I, "ternary")
+    if wl.idx_dtype == "fp8":
+        qI, kI = to_fp8_e4m3fn_bytes(qI), to_fp8_e4m3fn_bytes(kI)
+    return dict(qI=qI, kI=kI)
+
+
+# Head weights with 17 to 19 significant bits (c * 128 in [128, 256)): products with integers up to
+# 32 stay exact in fp32, and rounding c * 128 to 4 significant bits, then 16 times the remainder,
+# and so on, leaves a nonzero part at each of four steps.
+SPLIT_WEIGHTS = (133.193359375 / 128, 246.2861328125 / 128, 136.63623046875 / 128)
+
+
+def gen_linear_split(wl: Workload, seed: int = 0) -> dict:
+    """Indexer inputs whose weighted query sum needs many significant bits, with every score
+    exact in fp32: q^I, k^I in {-1, 0, 1}; row r weighs a single head j_r = r % H_I by
+    +-SPLIT_WEIGHTS[r % 3] * 2^m (m cycling through -6, 0, 3, 9), all other heads 0; that head's
+    query keeps at most 32 nonzero entries (so |q^I . k^I| <= 32)."""
+    x = gen_ternary(wl, seed)
+    qI = x["qI"].copy()
+    zero = 0 if wl.idx_dtype != "fp8" else to_fp8_e4m3fn_bytes(np.zeros(1, np.float32))[0]
+    w = np.zeros((wl.T, wl.H_I), np.float32)
+    ms = (-6, 0, 3, 9)
+    for r in range(wl.T):
+        j = r % wl.H_I
+        qI[r, j, 32:] = zero
+        sign = -1.0 if (r // 3) % 2 else 1.0
+        w[r, j] = np.float32(sign * SPLIT_WEIGHTS[r % 3] * 2.0 ** ms[(r // 2) % 4])
+    return dict(qI=qI, kI=x["kI"], w=w)
 
 
 def gen_scales(wl: Workload, variant: str = "normal", seed: int = 0) -> dict:

@@ -26,8 +26,8 @@
  *     as one byte per value; DSA_BF16 = bfloat16; DSA_F32 = IEEE binary32. Inputs are taken as
  *     they are: the library never quantises and applies no scale factors.
  *   - Ownership. The caller allocates and frees every buffer, including workspaces. The
- *     library does not allocate device memory and keeps no state between calls apart from a
- *     cached device-property query. All work is enqueued on `stream` (a hipStream_t; NULL is
+ *     library does not allocate device memory and keeps no state between calls. All work is
+ *     enqueued on `stream` (a hipStream_t; NULL is
  *     the default stream) and returns without waiting; results are valid once the stream has
  *     reached that point, and inputs must stay untouched until then.
  *   - Errors. Arguments are validated on the host before anything is enqueued; on failure the
@@ -51,7 +51,16 @@ extern "C" {
 
 #define DSA_ABI_VERSION 3
 
-typedef enum {
+/* Both enums are 32-bit integers. Compiled as C++ they get int32_t as their fixed underlying
+ * type, so that any int32 value a caller passes (an unknown type code, a status from a newer
+ * library) is a value of the type and is rejected or reported, not undefined behaviour. */
+#ifdef __cplusplus
+#define DSA_ENUM_BASE : int32_t
+#else
+#define DSA_ENUM_BASE
+#endif
+
+typedef enum DSA_ENUM_BASE {
   DSA_OK = 0,
   DSA_ERR_NULL = 1,        /* a required pointer is NULL                                     */
   DSA_ERR_SHAPE = 2,       /* sizes inconsistent (negative, m_b > n_b, ld too small, ...)    */
@@ -62,7 +71,7 @@ typedef enum {
   DSA_ERR_HIP = 7          /* a HIP runtime call or kernel launch failed                     */
 } dsa_status_t;
 
-typedef enum { DSA_F32 = 0, DSA_BF16 = 1, DSA_FP8_E4M3 = 2 } dsa_dtype_t;
+typedef enum DSA_ENUM_BASE { DSA_F32 = 0, DSA_BF16 = 1, DSA_FP8_E4M3 = 2 } dsa_dtype_t;
 
 /* A ragged batch of sequences. The device and host arrays must hold the same values. The
  * host copies are read during the call only (validation and launch planning); the device
@@ -162,8 +171,9 @@ dsa_status_t dsa_topk(const dsa_seqs_t* seqs, const float* scores, int64_t ld_sc
  *            aligned (may be NULL when that size is 0); contents on entry do not matter. The bf16
  *            path splits each row's index list over several workgroups when the batch has fewer
  *            rows than the device has compute units, and keeps the per-split partial outputs
- *            (bf16) and log-sum-exps (fp32) there (splits * T * H * (2 d_v + 4) bytes); the size
- *            depends on the current device's compute unit count.
+ *            (bf16) and log-sum-exps (fp32) there (splits * T * H * (2 d_v + 4) bytes). Like every
+ *            *_workspace_size call, the size is a function of the arguments alone (no device
+ *            query, no HIP call).
  */
 size_t dsa_sparse_mla_attn_workspace_size(const dsa_seqs_t* seqs, int32_t H, int32_t d_qk,
                                           int32_t d_v, int32_t k, dsa_dtype_t dtype);

@@ -22,4 +22,4 @@ Modules:
 """
 from .numerics import decode, fp8_e4m3fn_table, bf16_bits_to_f64  # noqa: F401
 from .dsa import (Seqs, indexer_scores_row, indexer_scores, topk_row, topk, attn_row,  # noqa: F401
-                  sparse_mla_attn, forward_rows, indexer_error_bound_row, alignment_row)
+                  sparse_mla_attn, forward_rows, alignment_row)

@@ -88,23 +88,6 @@ def indexer_scores(seqs: Seqs, qI, kI, w, rows=None, q_scale=None, k_scale=None)
     return [indexer_scores_row(seqs, qI, kI, w, int(r), q_scale, k_scale) for r in rows]
 
 
-def indexer_error_bound_row(seqs: Seqs, qI, kI, w, r: int) -> np.ndarray:
-    """Forward error bound for an fp32 evaluation of I[r, :] in any summation order.
-
-    eps[s] = 4 * gamma(d_I + H_I + 1) * sum_j |w[r,j]| * sum_d |qI[r,j,d] * kI[s,d]|,
-    gamma(n) = n u / (1 - n u), u = 2^-24 (recursive-summation bound; factor 4 of margin for
-    the unknown accumulation order inside a matrix instruction).
-    """
-    _, pos, k0, _ = seqs.locate(r)
-    q = np.abs(decode(qI[r]))
-    keys = np.abs(decode(kI[k0:k0 + pos + 1]))
-    H_I, d_I = q.shape
-    u = 2.0 ** -24
-    n = d_I + H_I + 1
-    gamma = n * u / (1 - n * u)
-    return 4.0 * gamma * (np.abs(decode(w[r])) @ (q @ keys.T))
-
-
 # ------------------------------------------------------------------ step 2: top-k selection
 
 def topk_row(scores: np.ndarray, k: int) -> np.ndarray:

@@ -185,6 +185,86 @@ def scores_ld(max_seqlen_k: int) -> int:
     return max(4, (max_seqlen_k + 3) // 4 * 4)
 
 
+# ---------------------------------------------------------------- argument checks
+# The C layer sees pointers only, so shapes, storage types, layouts and devices are checked here,
+# before any library call: a wrong one would make the kernels read or write outside the buffers.
+
+def _dtypes(kind):
+    torch = _torch()
+    return {"fp8": (torch.float8_e4m3fn, torch.uint8), "f32": (torch.float32,), "bf16": (torch.bfloat16,),
+            "i32": (torch.int32,), "u8": (torch.uint8,)}[kind]
+
+
+def _need(name, t, kinds, shape):
+    """t must be a tensor of one of the storage kinds, of the given shape (None: any extent),
+    and contiguous."""
+    torch = _torch()
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    allowed = tuple(d for k in kinds for d in _dtypes(k))
+    if t.dtype not in allowed:
+        raise TypeError(f"{name} must have dtype {' or '.join(str(d) for d in allowed)}, got {t.dtype}")
+    if t.dim() != len(shape) or any(w is not None and g != w for g, w in zip(t.shape, shape)):
+        want = ", ".join("*" if w is None else str(w) for w in shape)
+        raise ValueError(f"{name} must have shape [{want}], got {list(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _need_scores(name, t, seqs):
+    """Score rows: fp32 [T, >= max_seqlen_k] with unit column stride; the row stride is the
+    leading dimension passed to the library."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != torch.float32:
+        raise TypeError(f"{name} must have dtype torch.float32, got {t.dtype}")
+    if t.dim() != 2 or t.shape[0] != seqs.T or t.shape[1] < seqs.max_n:
+        raise ValueError(f"{name} must have shape [{seqs.T}, >= {seqs.max_n}], got {list(t.shape)}")
+    if t.stride(1) != 1 or t.stride(0) < t.shape[1]:
+        raise ValueError(f"{name} rows must be dense (column stride 1), got strides {t.stride()}")
+
+
+def _need_ws(name, t):
+    if t is not None:
+        _need(name, t, ("u8",), (None,))
+
+
+def _same_device(seqs, *named):
+    """Every tensor on the GPU that holds the sequence description."""
+    dev = seqs.cu_q.device
+    if dev.type != "cuda":
+        raise ValueError(f"the sequence description must be on a GPU device, it is on {dev}")
+    for name, t in named:
+        if t is not None and t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the sequence description on {dev}")
+
+
+def _check_indexer_args(seqs, q_idx, k_idx, w):
+    _need("q_idx", q_idx, ("fp8", "f32"), (seqs.T, None, None))
+    H_I, d_I = int(q_idx.shape[1]), int(q_idx.shape[2])
+    kind = "f32" if q_idx.dtype == _torch().float32 else "fp8"
+    _need("k_idx", k_idx, (kind,), (seqs.Nk, d_I))
+    _need("w", w, ("f32",), (seqs.T, H_I))
+    return H_I, d_I
+
+
+def _check_attn_args(seqs, q, kv, indices, d_v, out, lse):
+    _need("q", q, ("bf16", "f32"), (seqs.T, None, None))
+    T, H, d_qk = (int(x) for x in q.shape)
+    kind = "bf16" if q.dtype == _torch().bfloat16 else "f32"
+    _need("kv", kv, (kind,), (seqs.Nk, d_qk))
+    if indices is not None:
+        _need("indices", indices, ("i32",), (T, None))
+    if out is not None:
+        _need("out", out, (kind,), (T, H, d_v))
+    if lse is not None:
+        _need("lse", lse, ("f32",), (T, H))
+    return T, H, d_qk
+
+
 # ---------------------------------------------------------------- the four calls
 
 def indexer_workspace_size(seqs: Seqs, H_I: int, d_I: int, qk_dtype: int) -> int:
@@ -194,9 +274,15 @@ def indexer_workspace_size(seqs: Seqs, H_I: int, d_I: int, qk_dtype: int) -> int
 
 def indexer_scores(seqs: Seqs, q_idx, k_idx, w, scores=None, ws=None, stream=None):
     """I[r, s] for s <= pos(r); returns scores [T, ld] fp32 (entries beyond pos unspecified).
-    `ws` (uint8 device tensor of indexer_workspace_size bytes) is allocated when not given."""
+    q_idx [T, H_I, d_I] and k_idx [Nk, d_I] both FP8 (float8_e4m3fn / uint8 codes) or both
+    fp32, w [T, H_I] fp32. `ws` (uint8 device tensor of indexer_workspace_size bytes) is
+    allocated when not given."""
     torch = _torch()
-    H_I, d_I = int(q_idx.shape[1]), int(q_idx.shape[2])
+    H_I, d_I = _check_indexer_args(seqs, q_idx, k_idx, w)
+    if scores is not None:
+        _need_scores("scores", scores, seqs)
+    _need_ws("ws", ws)
+    _same_device(seqs, ("q_idx", q_idx), ("k_idx", k_idx), ("w", w), ("scores", scores), ("ws", ws))
     if scores is None:
         scores = torch.empty((seqs.T, scores_ld(seqs.max_n)), dtype=torch.float32, device=q_idx.device)
     cs = seqs.c()
@@ -221,7 +307,16 @@ def indexer_scores_scaled(seqs: Seqs, q_idx, q_scale, k_idx, k_scale, w, scores=
                           stream=None):
     """Scores of scaled inputs: q_scale [T, H_I] and k_scale [Nk] fp32 (positive) or None."""
     torch = _torch()
-    H_I, d_I = int(q_idx.shape[1]), int(q_idx.shape[2])
+    H_I, d_I = _check_indexer_args(seqs, q_idx, k_idx, w)
+    if q_scale is not None:
+        _need("q_scale", q_scale, ("f32",), (seqs.T, H_I))
+    if k_scale is not None:
+        _need("k_scale", k_scale, ("f32",), (seqs.Nk,))
+    if scores is not None:
+        _need_scores("scores", scores, seqs)
+    _need_ws("ws", ws)
+    _same_device(seqs, ("q_idx", q_idx), ("k_idx", k_idx), ("w", w), ("q_scale", q_scale),
+                 ("k_scale", k_scale), ("scores", scores), ("ws", ws))
     if scores is None:
         scores = torch.empty((seqs.T, scores_ld(seqs.max_n)), dtype=torch.float32, device=q_idx.device)
     cs = seqs.c()
@@ -241,6 +336,10 @@ def indexer_scores_scaled(seqs: Seqs, q_idx, q_scale, k_idx, k_scale, w, scores=
 def topk(seqs: Seqs, scores, k: int, indices=None, stream=None):
     """Top-k positions per row: ascending, ties to the lower position, -1 padded."""
     torch = _torch()
+    _need_scores("scores", scores, seqs)
+    if indices is not None:
+        _need("indices", indices, ("i32",), (seqs.T, k))
+    _same_device(seqs, ("scores", scores), ("indices", indices))
     if indices is None:
         indices = torch.empty((seqs.T, k), dtype=torch.int32, device=scores.device)
     cs = seqs.c()
@@ -259,11 +358,15 @@ def attn_workspace_size(seqs: Seqs, H: int, d_qk: int, d_v: int, k: int, dtype: 
 def sparse_mla_attn(seqs: Seqs, q, kv, indices, scale: float, d_v: int = None, out=None, lse=None,
                     with_lse=True, ws=None, stream=None):
     """Attention of every head over the selected latent rows; returns (out, lse).
+    q [T, H, d_qk] and kv [Nk, d_qk] both bf16 or both fp32, indices [T, k] int32.
     `ws` (uint8 device tensor of attn_workspace_size bytes) is allocated when not given."""
     torch = _torch()
-    T, H, d_qk = (int(x) for x in q.shape)
+    _need("q", q, ("bf16", "f32"), (seqs.T, None, None))
     if d_v is None:
-        d_v = 512 if d_qk == 576 else d_qk
+        d_v = 512 if int(q.shape[2]) == 576 else int(q.shape[2])
+    T, H, d_qk = _check_attn_args(seqs, q, kv, indices, d_v, out, lse)
+    _need_ws("ws", ws)
+    _same_device(seqs, ("q", q), ("kv", kv), ("indices", indices), ("out", out), ("lse", lse), ("ws", ws))
     k = int(indices.shape[1])
     if out is None:
         out = torch.empty((T, H, d_v), dtype=q.dtype, device=q.device)
@@ -286,8 +389,17 @@ def indexer_alignment(seqs: Seqs, q, kv, indices, scale: float, lse, scores, wit
     """Indexer-alignment target (head-averaged attention distribution over each row's index list)
     and its KL divergence from the softmax of the indexer scores; returns (target or None, kl)."""
     torch = _torch()
-    T, H, d_qk = (int(x) for x in q.shape)
+    _need("q", q, ("bf16", "f32"), (seqs.T, None, None))
+    T, H, d_qk = _check_attn_args(seqs, q, kv, indices, None, None, lse)
+    _need("lse", lse, ("f32",), (T, H))
+    _need_scores("scores", scores, seqs)
     k = int(indices.shape[1])
+    if kl is not None:
+        _need("kl", kl, ("f32",), (T,))
+    if target is not None:
+        _need("target", target, ("f32",), (T, k))
+    _same_device(seqs, ("q", q), ("kv", kv), ("indices", indices), ("lse", lse), ("scores", scores),
+                 ("kl", kl), ("target", target))
     if kl is None:
         kl = torch.empty((T,), dtype=torch.float32, device=q.device)
     if target is None and with_target:
@@ -306,8 +418,17 @@ class Forward:
                  keep_scores=False, keep_indices=False, with_lse=True, q_idx_scale=None, k_idx_scale=None):
         torch = _torch()
         self.seqs = seqs
+        H_I, d_I = _check_indexer_args(seqs, q_idx, k_idx, w)
+        _need("q", q, ("bf16", "f32"), (seqs.T, None, None))
         T, H, d_qk = (int(x) for x in q.shape)
         d_v = d_v if d_v is not None else (512 if d_qk == 576 else d_qk)
+        _check_attn_args(seqs, q, kv, None, d_v, None, None)
+        if q_idx_scale is not None:
+            _need("q_idx_scale", q_idx_scale, ("f32",), (seqs.T, H_I))
+        if k_idx_scale is not None:
+            _need("k_idx_scale", k_idx_scale, ("f32",), (seqs.Nk,))
+        _same_device(seqs, ("q_idx", q_idx), ("k_idx", k_idx), ("w", w), ("q", q), ("kv", kv),
+                     ("q_idx_scale", q_idx_scale), ("k_idx_scale", k_idx_scale))
         dev = q.device
         self.out = torch.empty((T, H, d_v), dtype=q.dtype, device=dev)
         self.lse = torch.empty((T, H), dtype=torch.float32, device=dev) if with_lse else None
@@ -315,7 +436,7 @@ class Forward:
                        if keep_scores else None)
         self.indices = torch.empty((T, k), dtype=torch.int32, device=dev) if keep_indices else None
         a = _FwdArgs()
-        a.H_I, a.d_I = int(q_idx.shape[1]), int(q_idx.shape[2])
+        a.H_I, a.d_I = H_I, d_I
         a.qk_dtype = _dtype_code(q_idx)
         a.q_idx, a.k_idx, a.w = _ptr(q_idx), _ptr(k_idx), _ptr(w)
         a.k = k

@@ -845,11 +845,11 @@ attn_combine_kernel(int T, int nsplit, const uint16_t* __restrict__ part_o,
 
 // Splits of each row's index list: batches with fewer rows than compute units (decode) split
 // every row into up to 32 runs of whole blocks so that each compute unit gets a workgroup.
+// A function of the arguments only (the workspace size depends on it).
 int attn_splits(const SeqInfo& s, int k) {
   const int nblk = (k + MBLK - 1) / MBLK;
-  const int cus = device_cu_count();
-  if (s.T <= 0 || s.T >= cus) return 1;
-  return max(1, min(min(nblk, 32), cus / s.T));
+  if (s.T <= 0 || s.T >= kTargetCUs) return 1;
+  return max(1, min(min(nblk, 32), kTargetCUs / s.T));
 }
 
 size_t attn_workspace_bytes(const SeqInfo& s, int, int, int, int k, bool bf16) {

@@ -7,8 +7,6 @@
 #include <climits>
 #include <cstdarg>
 #include <cstdio>
-#include <mutex>
-#include <vector>
 
 #include "dsa_internal.h"
 
@@ -231,25 +229,6 @@ ForwardPlan plan_forward(const dsa::SeqInfo& s, const dsa_forward_args_t* a) {
 
 }  // namespace
 
-namespace dsa {
-
-int device_cu_count() {
-  static std::mutex mu;
-  static std::vector<int> cache;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 256;
-  std::lock_guard<std::mutex> lock(mu);
-  if ((int)cache.size() <= dev) cache.resize(dev + 1, 0);
-  if (cache[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-    cache[dev] = n;
-  }
-  return cache[dev];
-}
-
-}  // namespace dsa
 
 extern "C" {
 

@@ -57,7 +57,9 @@ hipError_t launch_align_bf16(const SeqInfo& s, const uint16_t* q, const uint16_t
                              const float* scores, int64_t ld, float* target, float* kl,
                              hipStream_t st);
 
-// Number of compute units of the current device (cached per device).
-int device_cu_count();
+// Compute units of an MI355X: the launch planning targets this many workgroups. It is a constant
+// (not a device query) so that workspace sizes depend on the call's arguments only; on a device
+// with fewer units the same launches simply take more waves of workgroups.
+constexpr int kTargetCUs = 256;
 
 }  // namespace dsa

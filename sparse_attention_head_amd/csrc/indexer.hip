@@ -652,7 +652,7 @@ hipError_t launch_indexer_fp8_prefill(const SeqInfo& s, const uint8_t* q, const 
   hipLaunchKernelGGL(indexer_fp8_linear_kernel, dim3((s.T + 3) / 4), dim3(256), 0, st, s.T, q, w,
                      pieces, piece_exp);
   const int tiles = (s.max_m + PF_ROWS - 1) / PF_ROWS;
-  const int kc = pick_chunk((int64_t)tiles * s.B, s.max_n, device_cu_count(), PF_SK);
+  const int kc = pick_chunk((int64_t)tiles * s.B, s.max_n, kTargetCUs, PF_SK);
   dim3 grid(tiles, (s.max_n + kc - 1) / kc, s.B);
   static_assert(PF_KC_MAX >= 8192, "pick_chunk returns at most 8192 keys");
   if (kscale)

@@ -218,3 +218,91 @@ def test_last_error_is_descriptive(dsa):
     sq = FakeSeqs(dsa, [0, 10], [0, 5])
     indexer(dsa, sq)
     assert b"queries" in dsa._c_last()
+
+
+# ------------------------------------------------------------------ Python binding argument checks
+# The binding checks shapes, storage types, layouts and devices before any library call (the C
+# layer sees pointers only). Each case below fails in the binding: CPU tensors never reach the
+# library, the valid-shaped ones are stopped by the device check.
+
+def _binding_case(dsa):
+    import torch
+    seqs = dsa.Seqs([0, 3, 5], [0, 10, 16], device="cpu")       # T = 5, Nk = 16, max_n = 10
+    f8 = torch.float8_e4m3fn
+    x = dict(
+        qI=torch.zeros(5, 64, 128, dtype=f8), kI=torch.zeros(16, 128, dtype=f8),
+        w=torch.zeros(5, 64), q=torch.zeros(5, 128, 576, dtype=torch.bfloat16),
+        kv=torch.zeros(16, 576, dtype=torch.bfloat16), idx=torch.zeros(5, 64, dtype=torch.int32),
+        scores=torch.zeros(5, 12), lse=torch.zeros(5, 128))
+    return seqs, x
+
+
+def test_binding_rejects_bad_indexer_arguments(dsa):
+    import torch
+    seqs, x = _binding_case(dsa)
+    bad = [
+        (dict(qI=torch.zeros(4, 64, 128, dtype=torch.float8_e4m3fn)), ValueError, "q_idx"),   # rows != T
+        (dict(kI=torch.zeros(15, 128, dtype=torch.float8_e4m3fn)), ValueError, "k_idx"),      # keys != Nk
+        (dict(kI=torch.zeros(16, 128)), TypeError, "k_idx"),                                  # fp32 keys, FP8 queries
+        (dict(w=torch.zeros(5, 64, dtype=torch.float64)), TypeError, "w"),
+        (dict(w=torch.zeros(5, 32)), ValueError, "w"),
+        (dict(qI=torch.zeros(5, 64, 256, dtype=torch.float8_e4m3fn)[:, :, :128]), ValueError, "contiguous"),
+        (dict(qI=torch.zeros(5, 64, 128, dtype=torch.int16)), TypeError, "q_idx"),
+        (dict(scores=torch.zeros(5, 8)), ValueError, "scores"),                             # < max_n columns
+        (dict(scores=torch.zeros(5, 12, dtype=torch.float16)), TypeError, "scores"),
+        (dict(scores=torch.zeros(12, 5).t()), ValueError, "scores"),                         # column stride 5
+    ]
+    for change, exc, what in bad:
+        y = dict(x, **change)
+        with pytest.raises(exc, match=what):
+            dsa.indexer_scores(seqs, y["qI"], y["kI"], y["w"], scores=y["scores"])
+    with pytest.raises(ValueError, match="GPU"):
+        dsa.indexer_scores(seqs, x["qI"], x["kI"], x["w"], scores=x["scores"])
+    with pytest.raises(ValueError, match="q_scale"):
+        dsa.indexer_scores_scaled(seqs, x["qI"], torch.ones(5, 32), x["kI"], None, x["w"])
+    with pytest.raises(ValueError, match="k_scale"):
+        dsa.indexer_scores_scaled(seqs, x["qI"], None, x["kI"], torch.ones(10), x["w"])
+
+
+def test_binding_rejects_bad_topk_and_attention_arguments(dsa):
+    import torch
+    seqs, x = _binding_case(dsa)
+    with pytest.raises(TypeError, match="indices"):
+        dsa.topk(seqs, x["scores"], 64, indices=torch.zeros(5, 64, dtype=torch.int64))
+    with pytest.raises(ValueError, match="indices"):
+        dsa.topk(seqs, x["scores"], 64, indices=torch.zeros(5, 32, dtype=torch.int32))
+    with pytest.raises(ValueError, match="GPU"):
+        dsa.topk(seqs, x["scores"], 64)
+    bad = [
+        (dict(kv=torch.zeros(16, 576)), TypeError, "kv"),                                   # fp32 kv, bf16 q
+        (dict(kv=torch.zeros(12, 576, dtype=torch.bfloat16)), ValueError, "kv"),            # rows != Nk
+        (dict(q=torch.zeros(6, 128, 576, dtype=torch.bfloat16)), ValueError, "q"),
+        (dict(idx=torch.zeros(5, 64, dtype=torch.int64)), TypeError, "indices"),
+        (dict(idx=torch.zeros(64, 5, dtype=torch.int32).t()), ValueError, "indices"),        # not contiguous
+        (dict(lse=torch.zeros(5, 64)), ValueError, "lse"),
+    ]
+    for change, exc, what in bad:
+        y = dict(x, **change)
+        with pytest.raises(exc, match=what):
+            dsa.sparse_mla_attn(seqs, y["q"], y["kv"], y["idx"], 0.04, lse=y["lse"])
+    with pytest.raises(ValueError, match="out"):
+        dsa.sparse_mla_attn(seqs, x["q"], x["kv"], x["idx"], 0.04, out=torch.zeros(5, 128, 576, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="GPU"):
+        dsa.sparse_mla_attn(seqs, x["q"], x["kv"], x["idx"], 0.04)
+    with pytest.raises(ValueError, match="scores"):
+        dsa.indexer_alignment(seqs, x["q"], x["kv"], x["idx"], 0.04, x["lse"], torch.zeros(4, 12))
+    with pytest.raises(ValueError, match="GPU"):
+        dsa.indexer_alignment(seqs, x["q"], x["kv"], x["idx"], 0.04, x["lse"], x["scores"])
+
+
+def test_binding_rejects_bad_forward_arguments(dsa):
+    import torch
+    seqs, x = _binding_case(dsa)
+    with pytest.raises(ValueError, match="kv"):
+        dsa.Forward(seqs, x["qI"], x["kI"], x["w"], x["q"], x["kv"][:8], 64, 0.04)
+    with pytest.raises(TypeError, match="w"):
+        dsa.Forward(seqs, x["qI"], x["kI"], x["w"].double(), x["q"], x["kv"], 64, 0.04)
+    with pytest.raises(ValueError, match="k_idx_scale"):
+        dsa.Forward(seqs, x["qI"], x["kI"], x["w"], x["q"], x["kv"], 64, 0.04, k_idx_scale=torch.ones(5))
+    with pytest.raises(ValueError, match="GPU"):
+        dsa.Forward(seqs, x["qI"], x["kI"], x["w"], x["q"], x["kv"], 64, 0.04)

@@ -2,7 +2,10 @@
 
 Bars (see tests/dsa_check.py for the derivations):
   * integer-valued indexer inputs ("int" variant): scores and top-k indices bit-exact;
-  * N(0,1) inputs: scores within the accumulation error bound, top-k eps-valid;
+  * N(0,1) inputs, and FP8 codes over the whole e4m3 range ("e4m3" variant): scores within the
+    accumulation error bound, top-k eps-valid;
+  * inputs built so that the FP8 prefill kernel's linear term needs all four of its pieces
+    while every partial sum stays exact: scores and top-k bit-exact;
   * attention (bf16): max-abs <= 2e-2, mean-abs <= 2e-3 against the oracle evaluated on the GPU's
     own validated index set; lse within 1e-3; fp32 path within 1e-4.
 """
@@ -15,7 +18,7 @@ import pytest
 import dsa_datagen as dg
 import oracle
 from oracle.dsa import Seqs
-from tests.dsa_check import DELTA_FP8_MFMA, check_topk_row, gamma, score_bound_row
+from tests.dsa_check import DELTA_FP8_NORMAL, check_topk_row, fp8_delta, gamma, score_bound_row
 
 pytestmark = pytest.mark.gpu
 
@@ -59,12 +62,15 @@ def out_np(t):
     return to_np_bf16(t) if t.dtype == torch.bfloat16 else t.cpu().numpy()
 
 
-def check_rows(wl, x, res, rows, variant, delta):
+def check_rows(wl, x, res, rows, variant, delta, stats=None):
+    """Every listed row against the oracle; returns the top-k overlaps with the oracle's sets
+    (bounded variants). `stats`, if given, receives the largest |err| / eps of the scores."""
     sq = Seqs(wl.cu_seqlens_q, wl.cu_seqlens_k)
-    exact = variant == "int"
+    exact = variant in ("int", "split")
     outs = out_np(res["out"])
     fouts = out_np(res["fout"])
     overlaps = []
+    worst = 0.0
     for r in rows:
         _, pos, _, _ = sq.locate(r)
         ref = oracle.indexer_scores_row(sq, x["qI"], x["kI"], x["w"], r)
@@ -75,8 +81,9 @@ def check_rows(wl, x, res, rows, variant, delta):
             assert res["idx"][r].tolist() == oracle.topk_row(ref, wl.k).tolist(), f"row {r}: top-k differs"
         else:
             eps = score_bound_row(sq, x["qI"], x["kI"], x["w"], r, delta)
-            bad = np.abs(got - ref) > eps
-            assert not bad.any(), f"row {r}: {bad.sum()} scores outside the bound, worst {np.max(np.abs(got-ref)/eps)}"
+            ratio = np.abs(got - ref) / eps
+            worst = max(worst, float(ratio.max()))
+            assert np.all(ratio <= 1.0), f"row {r}: {(ratio > 1).sum()} scores outside the bound, worst {ratio.max()}"
             overlaps.append(check_topk_row(res["idx"][r], ref, eps, wl.k, pos))
         assert np.array_equal(res["fidx"][r], res["idx"][r]), "fused indices differ"
         # attention on the GPU's own indices
@@ -92,6 +99,8 @@ def check_rows(wl, x, res, rows, variant, delta):
         assert np.all(np.abs(res["lse"][r][fin] - l[fin]) <= 1e-3)
         assert np.array_equal(fouts[r], outs[r]), "fused output differs"
         assert np.array_equal(res["flse"][r], res["lse"][r])
+    if stats is not None:
+        stats["worst_ratio"] = worst
     return overlaps
 
 
@@ -104,7 +113,7 @@ SMALL = {
 }
 
 
-@pytest.mark.parametrize("variant", ["int", "normal"])
+@pytest.mark.parametrize("variant", ["int", "normal", "e4m3"])
 @pytest.mark.parametrize("case", list(SMALL))
 def test_small_fp8_bf16(gpu, case, variant):
     sqs, sks, k = SMALL[case]
@@ -113,9 +122,25 @@ def test_small_fp8_bf16(gpu, case, variant):
     say(f"case {case} variant {variant} T={wl.T} Nk={wl.Nk}")
     x = dg.gen_inputs(wl, variant, seed=7)
     res = run_all(gpu, wl, x)
-    ov = check_rows(wl, x, res, range(wl.T), variant, DELTA_FP8_MFMA)
+    st = {}
+    ov = check_rows(wl, x, res, range(wl.T), variant, fp8_delta(variant), st)
     if ov:
-        say(f"  mean overlap with the oracle set {np.mean(ov):.4f}")
+        say(f"  mean overlap with the oracle set {np.mean(ov):.4f}; worst |err|/eps {st['worst_ratio']:.3g}")
+
+
+@pytest.mark.parametrize("shape", [([40, 9], [600, 9]), ([1, 1, 1], [300, 77, 2500])])
+def test_indexer_linear_split_exact(gpu, shape):
+    """Inputs whose weighted query sum u needs all four FP8 pieces of the prefill kernel's linear
+    term, with every partial sum exact in fp32 (dsa_datagen.gen_linear_split; the CPU model check
+    is tests/test_score_bound.py): scores and top-k must equal the oracle bit for bit, so a piece
+    that is dropped or scaled wrongly shows. The second shape runs the decode kernel on the same
+    kind of rows."""
+    sq_q, sq_k = shape
+    wl = dg.custom(name="split", seqlens_q=sq_q, seqlens_k=sq_k, H_I=64, d_I=128, k=64, H=128, d_qk=576,
+                   d_v=512, idx_dtype="fp8", attn_dtype="bf16", wid=37)
+    x = dict(dg.gen_inputs(wl, "normal", seed=2, parts=("attn",)), **dg.gen_linear_split(wl, seed=2))
+    res = run_all(gpu, wl, x)
+    check_rows(wl, x, res, range(wl.T), "split", None)
 
 
 @pytest.mark.parametrize("variant", ["int", "normal"])
@@ -135,7 +160,7 @@ def test_dense_special_case_bf16(gpu):
     res = run_all(gpu, wl, x)
     for r in range(wl.T):
         assert res["idx"][r].tolist() == list(range(r + 1)) + [-1] * (wl.k - r - 1)
-    check_rows(wl, x, res, range(wl.T), "normal", DELTA_FP8_MFMA)
+    check_rows(wl, x, res, range(wl.T), "normal", DELTA_FP8_NORMAL)
 
 
 @pytest.mark.parametrize("shape", [([5, 40, 1], [40, 100, 7], 128), ([1, 1, 1, 1], [100, 2000, 2048, 64], 2048)])
@@ -203,7 +228,7 @@ def test_scaled_indexer(gpu, case, variant, sides):
     torch.cuda.synchronize()
     got_all, fs, fi = scores.cpu().numpy(), fwd.scores.cpu().numpy(), fwd.indices.cpu().numpy()
     sq = Seqs(wl.cu_seqlens_q, wl.cu_seqlens_k)
-    delta = DELTA_FP8_MFMA if idt == "fp8" else gamma(d_I)
+    delta = DELTA_FP8_NORMAL if idt == "fp8" else gamma(d_I)
     for r in range(wl.T):
         _, pos, _, _ = sq.locate(r)
         ref = oracle.indexer_scores_row(sq, x["qI"], x["kI"], x["w"], r, qs, ks)
@@ -319,7 +344,7 @@ def test_indexer_weight_extremes(gpu):
         _, pos, _, _ = sq.locate(r)
         ref = oracle.indexer_scores_row(sq, x["qI"], x["kI"], x["w"], r)
         got = res["scores"][r, :pos + 1].astype(np.float64)
-        eps = score_bound_row(sq, x["qI"], x["kI"], x["w"], r, DELTA_FP8_MFMA)
+        eps = score_bound_row(sq, x["qI"], x["kI"], x["w"], r, DELTA_FP8_NORMAL)
         assert np.all(np.abs(got - ref) <= eps), f"row {r}: worst {np.max(np.abs(got - ref) - eps)}"
         if r == 2:
             assert np.all(got == 0.0)
@@ -462,31 +487,49 @@ def test_topk_row_lengths_and_degenerate_rows(gpu, n, rows, k):
 def test_empty_batch_is_noop(gpu):
     seqs = gpu.Seqs([0], [0])
     z = torch.zeros(16, device="cuda")
-    gpu.indexer_scores(seqs, z.view(1, 1, 16)[:0], z.view(1, 16), z.view(1, 16), scores=z.view(4, 4))
+    gpu.indexer_scores(seqs, z.view(1, 1, 16)[:0], z.view(1, 16)[:0], z.view(16, 1)[:0], scores=z.view(4, 4)[:0])
+    e8 = torch.zeros(0, 64, 128, dtype=torch.float8_e4m3fn, device="cuda")
+    out, lse = gpu.forward(seqs, e8, torch.zeros(0, 128, dtype=torch.float8_e4m3fn, device="cuda"),
+                           torch.zeros(0, 64, device="cuda"),
+                           torch.zeros(0, 128, 576, dtype=torch.bfloat16, device="cuda"),
+                           torch.zeros(0, 576, dtype=torch.bfloat16, device="cuda"), 2048, 0.04)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 128, 512) and lse.shape == (0, 128)
 
 
-# ------------------------------------------------------------------ full-size workloads (sampled)
+# ------------------------------------------------------------------ full-size workloads
 
+# rows checked against the oracle: every row of the decode batches, sampled rows of the prefills
 FULL_ROWS = {
-    "prefill8k": [0, 1, 63, 2046, 2047, 2048, 4095, 5000, 8190, 8191],
-    "decode32k": [0, 17, 63],
-    "chunk128k": [0, 1, 2047, 4094, 4095],
-    "ragged": [0, 5, 64, 127],
+    "prefill8k": [0, 1, 63, 2046, 2047, 2048, 4095, 5000, 8190, 8191] + list(range(100, 8192, 173)),
+    "decode32k": None,
+    "chunk128k": [0, 1, 2047, 4094, 4095] + list(range(37, 4096, 211)),
+    "ragged": None,
 }
+# floor of the mean overlap of the GPU's top-k sets with the oracle's on N(0,1) data (different
+# sets are valid where scores lie within the rounding error of the k-th one; the eps-valid check
+# is the bar, this guards against a systematic shift)
+MIN_MEAN_OVERLAP = 0.99
 
 
 @pytest.mark.parametrize("variant", ["int", "normal"])
 @pytest.mark.parametrize("name", list(FULL_ROWS))
-def test_full_size_sampled_rows(gpu, name, variant):
-    """The shapes and launch configuration the benchmark times, on sampled rows: int variant,
-    scores and indices bit-exact; N(0,1) variant (the benchmark's data), scores within the error
-    bound and the top-k eps-valid; attention within tolerance on the GPU's indices."""
+def test_full_size_rows(gpu, name, variant):
+    """The shapes and launch configuration the benchmark times: int variant, scores and indices
+    bit-exact; N(0,1) variant (the benchmark's data), scores within the error bound, the top-k
+    eps-valid and its mean overlap with the oracle's sets at least MIN_MEAN_OVERLAP; attention
+    within tolerance on the GPU's indices. Every row of the decode batches, sampled rows of the
+    prefills."""
     wl = dg.workload(name)
     say(f"full {name} ({variant}): generating T={wl.T} Nk={wl.Nk}")
     x = dg.gen_inputs(wl, variant, seed=0)
     say("  running")
     res = run_all(gpu, wl, x)
-    say("  checking")
-    ov = check_rows(wl, x, res, FULL_ROWS[name], variant, DELTA_FP8_MFMA)
+    rows = FULL_ROWS[name] if FULL_ROWS[name] is not None else range(wl.T)
+    say(f"  checking {len(rows)} rows")
+    st = {}
+    ov = check_rows(wl, x, res, rows, variant, DELTA_FP8_NORMAL, st)
     if ov:
-        say(f"  mean overlap with the oracle set {np.mean(ov):.4f}")
+        say(f"  overlap with the oracle sets: mean {np.mean(ov):.5f} min {np.min(ov):.5f}; "
+            f"worst |err|/eps {st['worst_ratio']:.3g}")
+        assert np.mean(ov) >= MIN_MEAN_OVERLAP, f"mean overlap {np.mean(ov)}"

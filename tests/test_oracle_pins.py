@@ -315,13 +315,15 @@ def test_duplicate_indices_count_as_multiset():
 
 
 def test_error_bound_covers_float32_evaluations():
-    """The fp32 error bound used for GPU scores holds for fp32 evaluations in two different
-    summation orders (a check that the bound is not too tight to be usable)."""
+    """The score bound of the parity tests with the fp32 path's delta = gamma(d_I) holds for fp32
+    evaluations in two different summation orders, and is tight enough that an fp32 evaluation
+    leaving out one head's term (the head with the smallest weight) falls outside it."""
+    from tests.dsa_check import gamma, score_bound_row
     wl = dg.custom(seqlens_q=(1,), seqlens_k=(300,), H_I=64, d_I=128, k=16)
     x = dg.gen_inputs(wl, "normal", 4, parts=("idx",))
     sq = Seqs(wl.cu_seqlens_q, wl.cu_seqlens_k)
     exact = oracle.indexer_scores_row(sq, x["qI"], x["kI"], x["w"], 0)
-    eps = oracle.indexer_error_bound_row(sq, x["qI"], x["kI"], x["w"], 0)
+    eps = score_bound_row(sq, x["qI"], x["kI"], x["w"], 0, gamma(wl.d_I))
     q32 = x["qI"][0].astype(np.float32)
     k32 = x["kI"].astype(np.float32)
     w32 = x["w"][0].astype(np.float32)
@@ -334,6 +336,10 @@ def test_error_bound_covers_float32_evaluations():
         b = b + w32[j] * np.maximum(d, np.float32(0))
     assert np.all(np.abs(a - exact) <= eps) and np.all(np.abs(b - exact) <= eps)
     assert np.all(eps > 0)
+    j = int(np.argmin(np.abs(w32)))
+    keep = np.arange(64) != j
+    c = (w32[keep, None] * np.maximum(q32[keep] @ k32.T, np.float32(0))).sum(axis=0, dtype=np.float32)
+    assert np.any(np.abs(c - exact) > eps)
 
 
 # ------------------------------------------------------------------ indexer-alignment target
