@@ -7,9 +7,14 @@ inputs already resident in HBM. The headline workload is the 128K-context prefil
 query rows at positions 126976..131071 against 131072 causal keys, H_I = 64, d_I = 128 (FP8
 e4m3), k = 2048, 128 heads with 576/512 latent dims (bf16). value = query tokens per second.
 
-Besides the fused step, each kernel is timed alone with HIP events on the stream it runs on, and
-the dominant kernel's achieved rate is reported against the MI355X peak (roofline). The CPU
-oracle is timed on a bounded sample of the same workload's rows (cpu_baseline).
+Timing protocol: before every timed step a 1 GiB buffer is read (the inputs are then in
+neither L2 nor the 256 MB last-level cache), and the step runs between its own pair of HIP events on
+the stream the library launches on; value and ms_per_step come from the median step, the minimum
+and mean are reported beside it, and so is one back-to-back loop with warm caches. Besides the fused
+step, each stage is timed alone the same way, and the dominant kernel's achieved rate is reported
+against the MI355X peak (roofline). The other workloads -- prefill8k, decode32k (64 x 32K),
+ragged (128 decode rows of 4K..128K keys) and short2k -- are timed the same way under `secondary`.
+The CPU oracle is timed on a bounded sample of the headline workload's rows (cpu_baseline).
 
 Progress goes to stderr; the result is one JSON line on stdout.
 """
@@ -85,18 +90,48 @@ def to_dev(torch, a):
     return t.cuda()
 
 
-def time_loop(torch, fn, steps, warmup):
-    """Average milliseconds per call, HIP events on the current stream."""
-    for _ in range(warmup):
-        fn()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        fn()
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps
+FLUSH_BYTES = 1 << 30   # read between timed reps: 4x the 256 MB last-level cache
+
+
+class Timer:
+    """Cold-cache timing: before every timed rep a 1 GiB buffer is read (so L2 and the last-level
+    cache hold none of the inputs, only clean lines: a written buffer would leave dirty lines whose
+    write-back the next kernel pays for), then the rep runs between its own pair of HIP events on
+    the current stream (the stream the library launches on). Reports the median, min and mean of
+    the reps; `warm` also times one back-to-back loop (caches warm) for comparison."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.scratch = torch.ones(FLUSH_BYTES // 4, dtype=torch.int32, device="cuda")
+        self.sink = torch.empty((), dtype=torch.int32, device="cuda")
+
+    def flush(self):
+        torch = self.torch
+        torch.amax(self.scratch, dim=0, out=self.sink)
+
+    def __call__(self, fn, reps, warmup, warm=False):
+        torch = self.torch
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for e0, e1 in ev:
+            self.flush()
+            e0.record()
+            fn()
+            e1.record()
+        torch.cuda.synchronize()
+        t = np.array([e0.elapsed_time(e1) for e0, e1 in ev])
+        res = dict(median=float(np.median(t)), min=float(t.min()), mean=float(t.mean()), reps=reps)
+        if warm:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            res["warm_mean"] = e0.elapsed_time(e1) / reps
+        return res
 
 
 def setup(torch, dsa, dg, name, seed=0):
@@ -110,10 +145,13 @@ def setup(torch, dsa, dg, name, seed=0):
     return wl, x, T, seqs
 
 
-def measure(torch, dsa, wl, T, seqs, steps, warmup, scales=None):
-    """Fused step time and per-kernel times for one workload (and, with `scales`, the indexer on
-    scaled inputs)."""
+def measure(torch, dsa, timer, wl, T, seqs, steps, warmup, scales=None, fused_only=False):
+    """Fused step and per-stage times for one workload (and, with `scales`, the indexer on scaled
+    inputs and the indexer-alignment target); each a dict of median / min / mean ms."""
     fwd = dsa.Forward(seqs, T["qI"], T["kI"], T["w"], T["q"], T["kv"], wl.k, wl.scale, wl.d_v)
+    res = dict(fused=timer(fwd, steps, warmup, warm=True))
+    if fused_only:
+        return res
     scores = torch.empty((wl.T, dsa.scores_ld(wl.max_seqlen_k)), dtype=torch.float32, device="cuda")
     idx = torch.empty((wl.T, wl.k), dtype=torch.int32, device="cuda")
     out = torch.empty((wl.T, wl.H, wl.d_v), dtype=torch.bfloat16, device="cuda")
@@ -123,29 +161,50 @@ def measure(torch, dsa, wl, T, seqs, steps, warmup, scales=None):
     # the stages alone (each on its own, inputs produced by the previous stage)
     dsa.indexer_scores(seqs, T["qI"], T["kI"], T["w"], scores=scores, ws=iws)
     dsa.topk(seqs, scores, wl.k, indices=idx)
-    t_idx = time_loop(torch, lambda: dsa.indexer_scores(seqs, T["qI"], T["kI"], T["w"], scores=scores, ws=iws),
-                      steps, warmup)
-    t_topk = time_loop(torch, lambda: dsa.topk(seqs, scores, wl.k, indices=idx), steps, warmup)
+    res["indexer"] = timer(lambda: dsa.indexer_scores(seqs, T["qI"], T["kI"], T["w"], scores=scores, ws=iws),
+                           steps, warmup)
+    res["topk"] = timer(lambda: dsa.topk(seqs, scores, wl.k, indices=idx), steps, warmup)
     aws_n = dsa.attn_workspace_size(seqs, wl.H, wl.d_qk, wl.d_v, wl.k, dsa._dtype_code(T["q"]))
     aws = torch.empty(max(aws_n, 1), dtype=torch.uint8, device="cuda")
-    t_attn = time_loop(torch, lambda: dsa.sparse_mla_attn(seqs, T["q"], T["kv"], idx, wl.scale, wl.d_v,
-                                                          out=out, lse=lse, ws=aws), steps, warmup)
-    t_fwd = time_loop(torch, fwd, steps, warmup)
-    res = dict(fused_ms=t_fwd, indexer_ms=t_idx, topk_ms=t_topk, attn_ms=t_attn)
+    res["attention"] = timer(lambda: dsa.sparse_mla_attn(seqs, T["q"], T["kv"], idx, wl.scale, wl.d_v,
+                                                         out=out, lse=lse, ws=aws), steps, warmup)
     if scales is not None and wl.attn_dtype == "bf16":   # the indexer-alignment target of the same rows
         kl = torch.empty((wl.T,), dtype=torch.float32, device="cuda")
         tgt = torch.empty((wl.T, wl.k), dtype=torch.float32, device="cuda")
-        res["alignment_ms"] = time_loop(
-            torch, lambda: dsa.indexer_alignment(seqs, T["q"], T["kv"], idx, wl.scale, lse, scores,
-                                                 kl=kl, target=tgt), steps, warmup)
+        res["alignment"] = timer(
+            lambda: dsa.indexer_alignment(seqs, T["q"], T["kv"], idx, wl.scale, lse, scores, kl=kl, target=tgt),
+            steps, warmup)
     if scales is not None:
         qs, ks = to_dev(torch, scales["q_scale"]), to_dev(torch, scales["k_scale"])
         sws_n = dsa.indexer_scaled_workspace_size(seqs, wl.H_I, wl.d_I, dsa._dtype_code(T["qI"]))
         sws = torch.empty(max(sws_n, 1), dtype=torch.uint8, device="cuda")
-        res["indexer_scaled_ms"] = time_loop(
-            torch, lambda: dsa.indexer_scores_scaled(seqs, T["qI"], qs, T["kI"], ks, T["w"], scores=scores,
-                                                     ws=sws), steps, warmup)
+        res["indexer_scaled"] = timer(
+            lambda: dsa.indexer_scores_scaled(seqs, T["qI"], qs, T["kI"], ks, T["w"], scores=scores, ws=sws),
+            steps, warmup)
     return res
+
+
+def stage_report(wl, tm):
+    """Per-stage rates against the MI355X peaks (median times; min-time rates alongside)."""
+    alg = algorithmic(wl)
+
+    def rate(work, t, peak, unit, key):
+        r = work / (t["median"] / 1e3) / (1e12 if unit == "tflops" else 1e9)
+        best = work / (t["min"] / 1e3) / (1e12 if unit == "tflops" else 1e9)
+        return {"ms": t["median"], "ms_min": t["min"], unit: r, key: r / peak, key + "_at_min": best / peak}
+
+    out = {}
+    if "indexer" in tm:
+        out["indexer"] = rate(alg["indexer_flop"], tm["indexer"], PEAK_FP8_TFLOPS, "tflops", "frac_fp8")
+        out["topk"] = rate(alg["topk_bytes"], tm["topk"], PEAK_HBM_GBS, "gbs", "frac_hbm")
+        out["attention"] = rate(alg["attn_flop"], tm["attention"], PEAK_BF16_TFLOPS, "tflops", "frac_bf16")
+    if "alignment" in tm:   # logits of every selected entry again: 2 H d_qk flop each
+        out["alignment"] = rate(2.0 * wl.H * wl.d_qk * alg["selected"], tm["alignment"], PEAK_BF16_TFLOPS,
+                                "tflops", "frac_bf16")
+    if "indexer_scaled" in tm:
+        out["indexer_scaled"] = rate(alg["indexer_flop"], tm["indexer_scaled"], PEAK_FP8_TFLOPS, "tflops",
+                                     "frac_fp8")
+    return out
 
 
 def cpu_baseline(wl, x, seconds):
@@ -178,7 +237,7 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="chunk128k")
-    ap.add_argument("--secondary", default="decode32k,short2k",
+    ap.add_argument("--secondary", default="prefill8k,decode32k,ragged,short2k",
                     help="comma-separated extra workloads reported under 'secondary' ('' for none)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -196,38 +255,29 @@ def main():
     import sparse_attention_head_amd as dsa
 
     torch.cuda.set_device(0)
+    timer = Timer(torch)
     wl, x, T, seqs = setup(torch, dsa, dg, args.workload)
     alg = algorithmic(wl)
-    log(f"[bench] timing {args.workload}: warmup {args.warmup}, steps {args.steps}")
-    tm = measure(torch, dsa, wl, T, seqs, args.steps, args.warmup,
+    log(f"[bench] timing {args.workload}: warmup {args.warmup}, steps {args.steps} (cold cache, one event "
+        f"pair per step)")
+    torch.cuda.synchronize()
+    t_wall = time.time()
+    tm = measure(torch, dsa, timer, wl, T, seqs, args.steps, args.warmup,
                  scales=dg.gen_scales(wl, "normal") if wl.idx_dtype == "fp8" else None)
-    log(f"[bench] {args.workload}: {tm}")
+    torch.cuda.synchronize()
+    log(f"[bench] {args.workload}: {json.dumps(tm)} ({time.time() - t_wall:.1f}s)")
 
     prefill = wl.max_seqlen_q > 1
-    value = wl.T / (tm["fused_ms"] / 1e3)
-    idx_tflops = alg["indexer_flop"] / (tm["indexer_ms"] / 1e3) / 1e12
-    attn_tflops = alg["attn_flop"] / (tm["attn_ms"] / 1e3) / 1e12
-    topk_gbs = alg["topk_bytes"] / (tm["topk_ms"] / 1e3) / 1e9
-    stages = dict(
-        indexer=dict(ms=tm["indexer_ms"], tflops=idx_tflops, frac_fp8=idx_tflops / PEAK_FP8_TFLOPS,
-                     flop=alg["indexer_flop"]),
-        topk=dict(ms=tm["topk_ms"], gbs=topk_gbs, frac_hbm=topk_gbs / PEAK_HBM_GBS, bytes=alg["topk_bytes"]),
-        attention=dict(ms=tm["attn_ms"], tflops=attn_tflops, frac_bf16=attn_tflops / PEAK_BF16_TFLOPS,
-                       flop=alg["attn_flop"]),
-    )
-    if "alignment_ms" in tm:   # logits of every selected entry again: 2 H d_qk flop each
-        af = 2.0 * wl.H * wl.d_qk * alg["selected"]
-        at = af / (tm["alignment_ms"] / 1e3) / 1e12
-        stages["alignment"] = dict(ms=tm["alignment_ms"], tflops=at, frac_bf16=at / PEAK_BF16_TFLOPS, flop=af)
-    if "indexer_scaled_ms" in tm:   # scaled FP8 inputs (per row and head, per key)
-        st = alg["indexer_flop"] / (tm["indexer_scaled_ms"] / 1e3) / 1e12
-        stages["indexer_scaled"] = dict(ms=tm["indexer_scaled_ms"], tflops=st, frac_fp8=st / PEAK_FP8_TFLOPS)
+    fused = tm["fused"]
+    value = wl.T / (fused["median"] / 1e3)
+    stages = stage_report(wl, tm)
     if prefill:
-        roof = dict(kernel="indexer_fp8", bound="mfma", achieved=idx_tflops, peak=PEAK_FP8_TFLOPS,
-                    unit="TFLOP/s", frac=idx_tflops / PEAK_FP8_TFLOPS,
+        st = stages["indexer"]
+        roof = dict(kernel="indexer_fp8 (prep + prefill kernel)", bound="mfma", achieved=st["tflops"],
+                    peak=PEAK_FP8_TFLOPS, unit="TFLOP/s", frac=st["frac_fp8"],
                     traffic=measured_traffic() if wl.name == "chunk128k" else None)
     else:
-        gbs = alg["decode_bytes"] / (tm["fused_ms"] / 1e3) / 1e9
+        gbs = alg["decode_bytes"] / (fused["median"] / 1e3) / 1e9
         roof = dict(kernel="fused_decode", bound="hbm", achieved=gbs, peak=PEAK_HBM_GBS, unit="GB/s",
                     frac=gbs / PEAK_HBM_GBS, traffic=None)
 
@@ -236,23 +286,21 @@ def main():
         del T
         torch.cuda.empty_cache()
         wl2, x2, T, seqs2 = setup(torch, dsa, dg, name)
-        tm2 = measure(torch, dsa, wl2, T, seqs2, max(3, args.steps // 2), 1)
-        a2 = algorithmic(wl2)
-        q_s = wl2.T / (tm2["fused_ms"] / 1e3)
-        if wl2.max_seqlen_q == 1:   # decode: HBM-bound as a whole
-            secondary[name] = dict(
-                fused_ms=tm2["fused_ms"], per_s=q_s, unit="queries/s",
-                hbm_gbs=a2["decode_bytes"] / (tm2["fused_ms"] / 1e3) / 1e9,
-                hbm_frac=a2["decode_bytes"] / (tm2["fused_ms"] / 1e3) / 1e9 / PEAK_HBM_GBS,
-                indexer_ms=tm2["indexer_ms"], topk_ms=tm2["topk_ms"], attn_ms=tm2["attn_ms"])
-        else:   # prefill: stages alone, and the attention's share of the BF16 peak
-            secondary[name] = dict(
-                fused_ms=tm2["fused_ms"], per_s=q_s, unit="tokens/s",
-                indexer_ms=tm2["indexer_ms"], topk_ms=tm2["topk_ms"], attn_ms=tm2["attn_ms"],
-                attn_frac_bf16=a2["attn_flop"] / (tm2["attn_ms"] / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
-                short_context=bool(wl2.max_seqlen_k <= wl2.k))
-        log(f"[bench] {name}: {secondary[name]}")
         del x2
+        tm2 = measure(torch, dsa, timer, wl2, T, seqs2, args.steps, max(1, args.warmup // 2))
+        a2 = algorithmic(wl2)
+        f2 = tm2["fused"]
+        rec = dict(fused_ms=f2["median"], fused_ms_min=f2["min"], fused_ms_warm=f2["warm_mean"],
+                   per_s=wl2.T / (f2["median"] / 1e3), stages=stage_report(wl2, tm2))
+        if wl2.max_seqlen_q == 1:   # decode: HBM-bound as a whole
+            gbs = a2["decode_bytes"] / (f2["median"] / 1e3) / 1e9
+            rec.update(unit="queries/s", hbm_gbs=gbs, hbm_frac=gbs / PEAK_HBM_GBS,
+                       hbm_frac_at_min=a2["decode_bytes"] / (f2["min"] / 1e3) / 1e9 / PEAK_HBM_GBS,
+                       decode_bytes=a2["decode_bytes"])
+        else:
+            rec.update(unit="tokens/s", short_context=bool(wl2.max_seqlen_k <= wl2.k))
+        secondary[name] = rec
+        log(f"[bench] {name}: {json.dumps(rec)}")
 
     if args.copy_calibration:
         a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -269,10 +317,13 @@ def main():
     res = dict(
         metric="DSA prefill tokens/s @128K ctx; decode queries/s; % of MFMA/HBM roofline",
         value=value, unit="tokens/s" if prefill else "queries/s", n_gpus=1, steps=args.steps,
-        warmup=args.warmup, ms_per_step=tm["fused_ms"], higher_is_better=True, scaling="weak",
+        warmup=args.warmup, ms_per_step=fused["median"], higher_is_better=True, scaling="weak",
         vs_baseline=None, dtype="fp8-e4m3 indexer, bf16 attention (fp32 accumulate)", data="synthetic",
         config=dict(workload=wl.name, query_rows=wl.T, keys_per_seq=wl.max_seqlen_k, sequences=wl.num_seqs,
                     H_I=wl.H_I, d_I=wl.d_I, k=wl.k, H=wl.H, d_qk=wl.d_qk, d_v=wl.d_v),
+        timing=dict(protocol="cold cache: 1 GiB read before each step; one HIP event pair per step; "
+                             "value and ms_per_step from the median step", ms_min=fused["min"],
+                    ms_mean=fused["mean"], ms_warm_loop=fused["warm_mean"]),
         roofline=roof, cpu_baseline=cpu, stages=stages, secondary=secondary,
     )
     print(json.dumps(res), flush=True)
