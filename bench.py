@@ -164,6 +164,11 @@ def measure(torch, dsa, timer, wl, T, seqs, steps, warmup, scales=None, fused_on
     res["indexer"] = timer(lambda: dsa.indexer_scores(seqs, T["qI"], T["kI"], T["w"], scores=scores, ws=iws),
                            steps, warmup)
     res["topk"] = timer(lambda: dsa.topk(seqs, scores, wl.k, indices=idx), steps, warmup)
+    # the fused indexer -> top-k call (fused for decode batches, the two steps otherwise)
+    itws_n = dsa.indexer_topk_workspace_size(seqs, wl.H_I, wl.d_I, dsa._dtype_code(T["qI"]), wl.k)
+    itws = torch.empty(max(itws_n, 1), dtype=torch.uint8, device="cuda")
+    res["indexer_topk"] = timer(lambda: dsa.indexer_topk(seqs, T["qI"], T["kI"], T["w"], wl.k, scores=scores,
+                                                         indices=idx, ws=itws), steps, warmup)
     aws_n = dsa.attn_workspace_size(seqs, wl.H, wl.d_qk, wl.d_v, wl.k, dsa._dtype_code(T["q"]))
     aws = torch.empty(max(aws_n, 1), dtype=torch.uint8, device="cuda")
     res["attention"] = timer(lambda: dsa.sparse_mla_attn(seqs, T["q"], T["kv"], idx, wl.scale, wl.d_v,
@@ -198,6 +203,11 @@ def stage_report(wl, tm):
         out["indexer"] = rate(alg["indexer_flop"], tm["indexer"], PEAK_FP8_TFLOPS, "tflops", "frac_fp8")
         out["topk"] = rate(alg["topk_bytes"], tm["topk"], PEAK_HBM_GBS, "gbs", "frac_hbm")
         out["attention"] = rate(alg["attn_flop"], tm["attention"], PEAK_BF16_TFLOPS, "tflops", "frac_bf16")
+    if "indexer_topk" in tm:   # one call for both steps; against the two calls' medians
+        sep = tm["indexer"]["median"] + tm["topk"]["median"]
+        out["indexer_topk"] = {"ms": tm["indexer_topk"]["median"], "ms_min": tm["indexer_topk"]["min"],
+                               "fused": bool(wl.max_seqlen_q == 1 and wl.k <= 2048 and wl.max_seqlen_k <= 131072),
+                               "separate_ms": sep, "speedup_vs_separate": sep / tm["indexer_topk"]["median"]}
     if "alignment" in tm:   # logits of every selected entry again: 2 H d_qk flop each
         out["alignment"] = rate(2.0 * wl.H * wl.d_qk * alg["selected"], tm["alignment"], PEAK_BF16_TFLOPS,
                                 "tflops", "frac_bf16")

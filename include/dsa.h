@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 3
+#define DSA_ABI_VERSION 4
 
 /* Both enums are 32-bit integers. Compiled as C++ they get int32_t as their fixed underlying
  * type, so that any int32 value a caller passes (an unknown type code, a status from a newer
@@ -147,6 +147,29 @@ dsa_status_t dsa_indexer_scores_scaled(const dsa_seqs_t* seqs, int32_t H_I, int3
 size_t dsa_topk_workspace_size(const dsa_seqs_t* seqs, int32_t k);
 dsa_status_t dsa_topk(const dsa_seqs_t* seqs, const float* scores, int64_t ld_scores, int32_t k,
                       int32_t* indices, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- steps 1 + 2 fused
+ * The lightning-indexer scores and the top-k selection in one call: the same results as
+ * dsa_indexer_scores followed by dsa_topk, bit for bit (paper digest page, "Key claims": paper
+ * section 2.1, Eq. 1-2; 36kr page, section 02: the top-k entries by index score).
+ * For decode batches (every sequence has at most one query row) with FP8 inputs (H_I = 64,
+ * d_I = 128), 1 <= k <= 2048 and max_seqlen_k <= 131072, the selection is fused into the
+ * indexer: each workgroup scoring a chunk of 1024 keys also keeps every key at or above a cut that
+ * lets through at least the chunk's expected share of the row's top k plus six standard
+ * deviations, and a merge selects the top k among the kept keys; when the kept keys cannot prove
+ * the result (a chunk holding more of the top k than it kept, or too many ties), the merge selects
+ * the row exactly from its scores instead. Other batches run the two steps back to back.
+ *   Arguments as in dsa_indexer_scores (no scale factors) and dsa_topk; `scores` is written
+ *   either way (the fused path's fallback reads it).
+ *   ws  device workspace of at least dsa_indexer_topk_workspace_size(...) bytes, 256-byte
+ *       aligned; contents on entry do not matter.
+ */
+size_t dsa_indexer_topk_workspace_size(const dsa_seqs_t* seqs, int32_t H_I, int32_t d_I,
+                                       dsa_dtype_t qk_dtype, int32_t k);
+dsa_status_t dsa_indexer_topk(const dsa_seqs_t* seqs, int32_t H_I, int32_t d_I, dsa_dtype_t qk_dtype,
+                              const void* q_idx, const void* k_idx, const float* w, float* scores,
+                              int64_t ld_scores, int32_t k, int32_t* indices, void* ws,
+                              size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------- step 3: sparse MLA attention
  * For each row r (sequence b) and head h, over the selected set S = { s in indices[r, :] :

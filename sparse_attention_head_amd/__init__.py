@@ -77,6 +77,11 @@ _c_indexer_s = _proto("dsa_indexer_scores_scaled", ctypes.c_int,
 _c_topk_ws = _proto("dsa_topk_workspace_size", ctypes.c_size_t, [ctypes.POINTER(_Seqs), ctypes.c_int32])
 _c_topk = _proto("dsa_topk", ctypes.c_int,
                  [ctypes.POINTER(_Seqs), _vp, ctypes.c_int64, ctypes.c_int32, _vp, _vp, ctypes.c_size_t, _vp])
+_c_itk_ws = _proto("dsa_indexer_topk_workspace_size", ctypes.c_size_t,
+                   [ctypes.POINTER(_Seqs), ctypes.c_int32, ctypes.c_int32, ctypes.c_int, ctypes.c_int32])
+_c_itk = _proto("dsa_indexer_topk", ctypes.c_int,
+                [ctypes.POINTER(_Seqs), ctypes.c_int32, ctypes.c_int32, ctypes.c_int, _vp, _vp, _vp, _vp,
+                 ctypes.c_int64, ctypes.c_int32, _vp, _vp, ctypes.c_size_t, _vp])
 _c_attn_ws = _proto("dsa_sparse_mla_attn_workspace_size", ctypes.c_size_t,
                     [ctypes.POINTER(_Seqs), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                      ctypes.c_int])
@@ -94,7 +99,8 @@ _c_last = _proto("dsa_last_error", ctypes.c_char_p, [])
 _c_abi = _proto("dsa_abi_version", ctypes.c_int32, [])
 
 EXPORTS = ("dsa_indexer_workspace_size", "dsa_indexer_scores", "dsa_indexer_scaled_workspace_size",
-           "dsa_indexer_scores_scaled", "dsa_topk_workspace_size", "dsa_topk", "dsa_sparse_mla_attn_workspace_size",
+           "dsa_indexer_scores_scaled", "dsa_topk_workspace_size", "dsa_topk", "dsa_indexer_topk_workspace_size",
+           "dsa_indexer_topk", "dsa_sparse_mla_attn_workspace_size",
            "dsa_sparse_mla_attn", "dsa_forward_workspace_size", "dsa_forward", "dsa_indexer_alignment",
            "dsa_status_string",
            "dsa_last_error", "dsa_abi_version")
@@ -348,6 +354,41 @@ def topk(seqs: Seqs, scores, k: int, indices=None, stream=None):
     _check(_c_topk(ctypes.byref(cs), _ptr(scores), int(scores.stride(0)), k, _ptr(indices), _ptr(ws), wsz,
                    _stream(stream)), "dsa_topk")
     return indices
+
+
+def indexer_topk_workspace_size(seqs: Seqs, H_I: int, d_I: int, qk_dtype: int, k: int) -> int:
+    cs = seqs.c()
+    return int(_c_itk_ws(ctypes.byref(cs), H_I, d_I, qk_dtype, k))
+
+
+def indexer_topk(seqs: Seqs, q_idx, k_idx, w, k: int, scores=None, indices=None, ws=None, stream=None):
+    """Indexer scores and top-k in one call (the selection fused into the indexer for decode
+    batches); returns (scores [T, ld] fp32, indices [T, k] int32), identical to indexer_scores
+    followed by topk."""
+    torch = _torch()
+    H_I, d_I = _check_indexer_args(seqs, q_idx, k_idx, w)
+    if scores is not None:
+        _need_scores("scores", scores, seqs)
+    if indices is not None:
+        _need("indices", indices, ("i32",), (seqs.T, k))
+    _need_ws("ws", ws)
+    _same_device(seqs, ("q_idx", q_idx), ("k_idx", k_idx), ("w", w), ("scores", scores), ("indices", indices),
+                 ("ws", ws))
+    dev = q_idx.device
+    if scores is None:
+        scores = torch.empty((seqs.T, scores_ld(seqs.max_n)), dtype=torch.float32, device=dev)
+    if indices is None:
+        indices = torch.empty((seqs.T, k), dtype=torch.int32, device=dev)
+    cs = seqs.c()
+    dt = _dtype_code(q_idx)
+    wsz = int(_c_itk_ws(ctypes.byref(cs), H_I, d_I, dt, k))
+    if ws is None:
+        ws = torch.empty(max(wsz, 1), dtype=torch.uint8, device=dev)
+    else:
+        wsz = int(ws.numel())
+    _check(_c_itk(ctypes.byref(cs), H_I, d_I, dt, _ptr(q_idx), _ptr(k_idx), _ptr(w), _ptr(scores),
+                  int(scores.stride(0)), k, _ptr(indices), _ptr(ws), wsz, _stream(stream)), "dsa_indexer_topk")
+    return scores, indices
 
 
 def attn_workspace_size(seqs: Seqs, H: int, d_qk: int, d_v: int, k: int, dtype: int) -> int:

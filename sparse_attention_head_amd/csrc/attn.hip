@@ -156,35 +156,6 @@ __device__ __forceinline__ int kv_swz(int s16) {
   return b0 | (b1 << 1) | (b2 << 2);
 }
 
-// One 16-byte-per-lane LDS DMA (buffer_load_dwordx4 ... lds): lane i's 16 bytes at voffset +
-// soff of the resource land at LDS byte address lds_base + lds_off + 16 i (lds_base, lds_off and
-// soff wave-uniform). Written as inline assembly so that the compiler does not track it: its
-// waits for LDS DMA are per LDS variable and cannot tell the two block buffers apart for the
-// transposing reads, so the value product of the current block would wait for the next block's
-// gather (an HBM round trip in decode). The callers wait (vmcnt(0)) and synchronise before
-// reading a buffer the DMA wrote. M0 is saved and restored around it, one wait state after
-// its write (the hazard the compiler observes for its own LDS DMA) and one before its restore.
-__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds_base, int lds_off,
-                                          int voff, int soff) {
-  int saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_add_u32 m0, %1, %2\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dwordx4 %3, %4, %5 offen lds\n\t"
-      "s_nop 0\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(lds_base), "s"(lds_off), "v"(voff), "s"(rsrc), "s"(soff)
-      : "memory", "scc");
-}
-
-// LDS byte address of a shared-memory pointer, wave-uniform.
-__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
-  return __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p);
-}
-
 // One gather instruction, untracked (UT: inline assembly, lds_dma16) or through the builtin,
 // which the compiler tracks. The untracked form pays in decode, where the value product would
 // otherwise wait for the next block's gather from HBM; the single-split prefill launch keeps the

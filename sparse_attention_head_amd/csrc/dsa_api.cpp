@@ -91,6 +91,8 @@ dsa_status_t check_indexer(const dsa::SeqInfo& s, int32_t H_I, int32_t d_I, dsa_
     return fail(DSA_ERR_ALIGN, "indexer tensors must be 16-byte aligned");
   if (dt == DSA_FP8_E4M3 && !(H_I == 64 && d_I == 128))
     return fail(DSA_ERR_UNSUPPORTED, "FP8 indexer needs H_I = 64, d_I = 128 (got %d, %d)", H_I, d_I);
+  if (dt == DSA_FP8_E4M3 && (int64_t)s.max_n * d_I > INT32_MAX)
+    return fail(DSA_ERR_UNSUPPORTED, "FP8 indexer needs max_seqlen_k * 128 < 2^31 (got %d keys)", s.max_n);
   if (dt == DSA_F32 && (H_I > 128 || d_I > 256 || H_I * d_I > 16384))
     return fail(DSA_ERR_UNSUPPORTED, "fp32 indexer supports H_I <= 128, d_I <= 256, H_I*d_I <= 16384");
   return ok();
@@ -143,10 +145,22 @@ size_t indexer_scaled_ws_bytes(const dsa::SeqInfo& s, int32_t H_I, dsa_dtype_t d
   return align_up(indexer_ws_bytes(s, dt)) + align_up((size_t)s.T * H_I * sizeof(float));
 }
 
+// The fused indexer -> top-k takes the fused path (chunk candidates + merge) for FP8 decode
+// batches; its workspace is the indexer's, then the candidates or the top-k's.
+bool indexer_topk_fused(const dsa::SeqInfo& s, int32_t H_I, int32_t d_I, dsa_dtype_t dt, int32_t k) {
+  return dt == DSA_FP8_E4M3 && H_I == 64 && d_I == 128 && dsa::decode_fused_topk_ok(s, k);
+}
+size_t indexer_topk_ws_bytes(const dsa::SeqInfo& s, int32_t H_I, int32_t d_I, dsa_dtype_t dt, int32_t k) {
+  return align_up(indexer_ws_bytes(s, dt)) +
+         (indexer_topk_fused(s, H_I, d_I, dt, k) ? dsa::decode_cand_bytes(s, k) : dsa::topk_workspace_bytes(s, k));
+}
+
 // qscale [T, H_I] / kscale [Nk]: optional positive scales of the indexer queries and keys.
+// cand: the fused decode top-k's candidate buffers (FP8 decode batches only), or NULL.
 dsa_status_t run_indexer(const dsa::SeqInfo& s, int32_t H_I, int32_t d_I, dsa_dtype_t dt,
                          const void* q, const float* qscale, const void* k, const float* kscale,
-                         const float* w, float* scores, int64_t ld, void* ws, hipStream_t st) {
+                         const float* w, float* scores, int64_t ld, void* ws, hipStream_t st,
+                         const dsa::DecodeCand* cand = nullptr) {
   if (s.T == 0) return ok();
   hipError_t e;
   if (qscale) {   // fold the query scales into the head weights
@@ -160,7 +174,7 @@ dsa_status_t run_indexer(const dsa::SeqInfo& s, int32_t H_I, int32_t d_I, dsa_dt
                                 static_cast<const float*>(k), w, kscale, scores, ld, st);
   else if (s.max_m == 1)
     e = dsa::launch_indexer_fp8_decode(s, static_cast<const uint8_t*>(q),
-                                       static_cast<const uint8_t*>(k), w, kscale, scores, ld, st);
+                                       static_cast<const uint8_t*>(k), w, kscale, scores, ld, cand, st);
   else
     e = dsa::launch_indexer_fp8_prefill(s, static_cast<const uint8_t*>(q),
                                         static_cast<const uint8_t*>(k), w, kscale, scores, ld, ws,
@@ -306,6 +320,50 @@ dsa_status_t dsa_topk(const dsa_seqs_t* seqs, const float* scores, int64_t ld_sc
   if (s.T == 0) return ok();
   return hip_status(dsa::launch_topk(s, scores, ld_scores, k, indices, ws, ws_bytes,
                                      static_cast<hipStream_t>(stream)),
+                    "top-k launch");
+}
+
+size_t dsa_indexer_topk_workspace_size(const dsa_seqs_t* seqs, int32_t H_I, int32_t d_I,
+                                       dsa_dtype_t qk_dtype, int32_t k) {
+  dsa::SeqInfo s;
+  if (check_seqs(seqs, s) != DSA_OK || s.B == 0 || H_I <= 0 || d_I <= 0 || k < 1) return 0;
+  return indexer_topk_ws_bytes(s, H_I, d_I, qk_dtype, k);
+}
+
+dsa_status_t dsa_indexer_topk(const dsa_seqs_t* seqs, int32_t H_I, int32_t d_I, dsa_dtype_t qk_dtype,
+                              const void* q_idx, const void* k_idx, const float* w, float* scores,
+                              int64_t ld_scores, int32_t k, int32_t* indices, void* ws, size_t ws_bytes,
+                              void* stream) {
+  dsa::SeqInfo s;
+  dsa_status_t st = check_seqs(seqs, s);
+  if (st != DSA_OK) return st;
+  if (s.B == 0) return ok();
+  st = check_indexer(s, H_I, d_I, qk_dtype, q_idx, k_idx, w, scores, ld_scores);
+  if (st != DSA_OK) return st;
+  st = check_topk(s, scores, ld_scores, k, indices);
+  if (st != DSA_OK) return st;
+  const size_t need = indexer_topk_ws_bytes(s, H_I, d_I, qk_dtype, k);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(DSA_ERR_WORKSPACE, "indexer top-k workspace needs %zu bytes, got %zu", need, ws_bytes);
+  if (ws && (reinterpret_cast<uintptr_t>(ws) % kAlign) != 0)
+    return fail(DSA_ERR_ALIGN, "indexer top-k workspace must be %zu-byte aligned", kAlign);
+  if (s.T == 0) return ok();
+  char* base = static_cast<char*>(ws);
+  const size_t iws = align_up(indexer_ws_bytes(s, qk_dtype));
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (indexer_topk_fused(s, H_I, d_I, qk_dtype, k)) {
+    const dsa::DecodeCand cand = dsa::decode_cand_layout(s, k, base + iws);
+    st = run_indexer(s, H_I, d_I, qk_dtype, q_idx, nullptr, k_idx, nullptr, w, scores, ld_scores,
+                     iws ? base : nullptr, hs, &cand);
+    if (st != DSA_OK) return st;
+    return hip_status(dsa::launch_topk_merge_decode(s, scores, ld_scores, k, indices, cand, hs),
+                      "top-k merge launch");
+  }
+  st = run_indexer(s, H_I, d_I, qk_dtype, q_idx, nullptr, k_idx, nullptr, w, scores, ld_scores,
+                   iws ? base : nullptr, hs);
+  if (st != DSA_OK) return st;
+  const size_t tws = dsa::topk_workspace_bytes(s, k);
+  return hip_status(dsa::launch_topk(s, scores, ld_scores, k, indices, tws ? base + iws : nullptr, tws, hs),
                     "top-k launch");
 }
 

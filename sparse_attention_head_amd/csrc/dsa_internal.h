@@ -30,9 +30,48 @@ size_t indexer_workspace_bytes(const SeqInfo& s, bool fp8);
 hipError_t launch_indexer_fp8_prefill(const SeqInfo& s, const uint8_t* q, const uint8_t* k,
                                       const float* w, const float* kscale, float* scores,
                                       int64_t ld, void* ws, hipStream_t st);
+// Decode batches (every sequence has at most one query row): each workgroup scores one chunk of
+// kDecodeChunk keys of one row.
+constexpr int kDecodeChunk = 1024;
+
+// Fused top-k of decode rows (the indexer keeps candidates, a merge selects; see topk.hip).
+// For a row of n > k keys, each chunk keeps every key at or above a cut chosen so that at least
+// decode_chunk_target(n, k) of its keys pass: the chunk's expected share mu = k * chunk / n of
+// the row's top k plus six standard deviations (sqrt(mu)) and 8, at most a whole chunk. The merge
+// is exact whenever no chunk holds more of the row's top k than it kept, and falls back to the
+// exact selection over the score row otherwise.
+__host__ __device__ inline int decode_chunk_target(int n, int k) {
+  const int mu = (int)(((int64_t)k * kDecodeChunk + n - 1) / n);
+  int r = 0;
+  while (r * r < mu) ++r;   // ceil(sqrt(mu)); mu <= kDecodeChunk when n > k
+  const int c = mu + 6 * r + 8;
+  return c < kDecodeChunk ? c : kDecodeChunk;
+}
+// Candidate slots per chunk: the target plus 64 (keys that share the cut's bin).
+__host__ __device__ inline int decode_chunk_capacity(int n, int k) {
+  const int c = decode_chunk_target(n, k) + 64;
+  return c < kDecodeChunk ? c : kDecodeChunk;
+}
+
+struct DecodeCand {
+  uint32_t* key;    // [T][nch][stride] order-preserving score keys
+  uint32_t* pos;    // [T][nch][stride] sequence-local positions
+  uint32_t* meta;   // [T][nch][4]: count, cut key, flags (bit 0: every key kept; bit 1: overflow)
+  int nch;          // chunks per row (ceil(max_seqlen_k / kDecodeChunk))
+  int stride;       // candidate slots per chunk (capacity of the row with the fewest keys)
+  int k;
+};
+// Layout of the candidate buffers inside a workspace of decode_cand_bytes(s, k) bytes.
+size_t decode_cand_bytes(const SeqInfo& s, int k);
+DecodeCand decode_cand_layout(const SeqInfo& s, int k, void* ws);
+// Whether the fused decode top-k covers this batch (decode rows, k <= 2048, rows up to 131072).
+bool decode_fused_topk_ok(const SeqInfo& s, int k);
+
+// Decode indexer: scores of every row into `scores`; with cand != NULL the chunks also keep their
+// top-k candidates (fused top-k).
 hipError_t launch_indexer_fp8_decode(const SeqInfo& s, const uint8_t* q, const uint8_t* k,
                                      const float* w, const float* kscale, float* scores,
-                                     int64_t ld, hipStream_t st);
+                                     int64_t ld, const DecodeCand* cand, hipStream_t st);
 // weff = w * qscale elementwise ([T, H_I]).
 hipError_t launch_indexer_scale_weights(const SeqInfo& s, int H_I, const float* w, const float* qscale,
                                         float* weff, hipStream_t st);
@@ -41,6 +80,10 @@ hipError_t launch_indexer_scale_weights(const SeqInfo& s, int H_I, const float* 
 size_t topk_workspace_bytes(const SeqInfo& s, int k);
 hipError_t launch_topk(const SeqInfo& s, const float* scores, int64_t ld, int k, int32_t* idx,
                        void* ws, size_t ws_bytes, hipStream_t st);
+// Second half of the fused decode top-k: per row, the exact top k of the chunks' candidates (or
+// of the score row, when the candidates cannot prove it), ascending, -1 padded.
+hipError_t launch_topk_merge_decode(const SeqInfo& s, const float* scores, int64_t ld, int k,
+                                    int32_t* idx, const DecodeCand& cand, hipStream_t st);
 
 // ---------------------------------------------------------------- attention
 size_t attn_workspace_bytes(const SeqInfo& s, int H, int d_qk, int d_v, int k, bool bf16);

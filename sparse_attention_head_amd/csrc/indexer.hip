@@ -149,121 +149,6 @@ __device__ __forceinline__ float score_block(const v8i (&a)[4 * RW], const v8i& 
   return (acc[0] + acc[1]) + (acc[2] + acc[3]);
 }
 
-// Loads this lane's 32-byte slice (bytes 32*(l/16) .. +32) of a 128-byte FP8 vector.
-__device__ __forceinline__ v8i load_slice(const uint8_t* __restrict__ base, int64_t row, int g) {
-  return *reinterpret_cast<const v8i*>(base + row * kDI + g * 32);
-}
-
-// Prefill: one workgroup = W waves x RW rows of one sequence against a chunk of KC keys; all waves
-// walk the same keys. Decode (m_b == 1 everywhere): one workgroup = one row and a chunk of keys that
-// the W waves split in interleaved 16-key blocks.
-// KS: every score is multiplied by the per-key scale kscale[key row] (positive).
-template <int RW, int W, bool DECODE, int PF, bool KS>
-__global__ void __launch_bounds__(W * 64, 2)
-indexer_fp8_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
-                   const uint8_t* __restrict__ q, const uint8_t* __restrict__ k,
-                   const float* __restrict__ w, const float* __restrict__ kscale,
-                   float* __restrict__ scores, int64_t ld, int KC) {
-  constexpr int HPM = 16 / RW;      // heads of one row inside a 16x16 tile
-  constexpr int NMF = 4 * RW;       // tiles (MFMAs) per 16-key block
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int g = lane >> 4, c = lane & 15;
-
-  int b, chunk, i_base;
-  if (DECODE) {
-    b = blockIdx.y;
-    chunk = blockIdx.x;
-    i_base = 0;
-  } else {
-    b = blockIdx.z;
-    chunk = blockIdx.y;
-    i_base = blockIdx.x * (W * RW);
-  }
-  const int q0 = cu_q[b], m = cu_q[b + 1] - q0;
-  const int k0 = cu_k[b], n = cu_k[b + 1] - k0;
-  if (i_base >= m) return;
-  const int tile_last = min(m, i_base + W * RW) - 1;
-  const int kbeg = chunk * KC;
-  if (kbeg > n - m + tile_last) return;  // chunk entirely beyond the causal limit of the tile
-
-  // rows of this wave (prefill) or the single row (decode)
-  const int wrow0 = DECODE ? i_base : i_base + wave * RW;
-  if (wrow0 >= m) return;                // no barrier below: waves may leave independently
-  const int wrow_last = min(m, wrow0 + RW) - 1;
-  const int kend = min(kbeg + KC, n - m + wrow_last + 1);
-  if (kbeg >= kend) return;
-
-  // A operand: M index c -> (row c / HPM, head mm*HPM + c % HPM), K bytes of lane group g
-  v8i a[NMF];
-  {
-    const int ar = min(wrow0 + c / HPM, m - 1);
-    const uint8_t* qrow = q + (int64_t)(q0 + ar) * (kHI * kDI) + (c % HPM) * kDI + g * 32;
-#pragma unroll
-    for (int mm = 0; mm < NMF; ++mm) a[mm] = *reinterpret_cast<const v8i*>(qrow + mm * HPM * kDI);
-    // the query tiles are only ever read by the matrix instructions: keep them in the
-    // accumulation registers so the architectural ones hold the weights and the tile results
-#pragma unroll
-    for (int mm = 0; mm < NMF; ++mm) asm volatile("" : "+a"(a[mm]));
-  }
-  // head weights for this lane's outputs: D row 4g+v -> (row (4g+v)/HPM, head mm*HPM + (4g+v)%HPM)
-  const int my_i = wrow0 + (4 * g) / HPM;      // all 4 v of a lane share the row
-  float wv[16 * RW];
-  {
-    const float* wr = w + (int64_t)(q0 + min(my_i, m - 1)) * kHI;
-#pragma unroll
-    for (int mm = 0; mm < NMF; ++mm)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) wv[4 * mm + v] = wr[mm * HPM + (4 * g + v) % HPM];
-  }
-  const bool row_ok = my_i < m;
-  const int my_pos = n - m + my_i;
-  float* srow = scores + (int64_t)(q0 + min(my_i, m - 1)) * ld;
-
-  // key blocks: prefill walks every block of [kbeg, kend); decode wave w takes blocks w, w+W, ...
-  const int step = DECODE ? 16 * W : 16;
-  const int first = DECODE ? kbeg + 16 * wave : kbeg;
-  // two register sets of PF key slices used in turn (no register copies, so each block waits
-  // for its own loads only): blocks of one set are scored while the other set's loads are in
-  // flight
-  v8i ra[PF], rb[PF];
-  float ka[PF], kb_[PF];   // the lanes' key scales, loaded with the keys (KS only)
-  auto load_set = [&](int base, v8i (&r)[PF], float (&ks)[PF]) {
-#pragma unroll
-    for (int p = 0; p < PF; ++p) {
-      const int key = k0 + min(base + p * step + c, n - 1);
-      r[p] = load_slice(k, key, g);
-      if (KS) ks[p] = kscale[key];
-    }
-  };
-  auto score_set = [&](int base, const v8i (&r)[PF], const float (&ks)[PF]) {
-#pragma unroll
-    for (int p = 0; p < PF; ++p) {
-      const int kb = base + p * step;
-      if (kb < kend) {
-        float acc = score_block<RW>(a, r[p], wv);
-        // keep the epilogue in this block (it would otherwise sink into the store's branch and
-        // lose its interleaving with the matrix instructions)
-        asm volatile("" ::"v"(acc));
-        if (RW <= 2) acc += __shfl_xor(acc, 16);
-        if (RW == 1) acc += __shfl_xor(acc, 32);
-        if (KS) acc *= ks[p];
-        const int s = kb + c;
-        const bool owner = (RW == 4) || (RW == 2 ? (g & 1) == 0 : g == 0);
-        if (owner && row_ok && s <= my_pos && s < kend) srow[s] = acc;
-      }
-    }
-  };
-  load_set(first, ra, ka);
-  for (int kb0 = first; kb0 < kend; kb0 += 2 * PF * step) {
-    load_set(kb0 + PF * step, rb, kb_);
-    score_set(kb0, ra, ka);
-    if (kb0 + PF * step >= kend) break;
-    load_set(kb0 + 2 * PF * step, ra, ka);
-    score_set(kb0 + PF * step, rb, kb_);
-  }
-}
-
 // ---------------------------------------------------------------------------- prefill, LDS-staged keys
 // The epilogue above costs two vector instructions (max, fma) per (row, head, key), as much vector
 // time as the matrix instruction that produced the 4 values takes, so it, not the matrix core,
@@ -664,19 +549,272 @@ hipError_t launch_indexer_fp8_prefill(const SeqInfo& s, const uint8_t* q, const 
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------- decode
+// One query row per sequence. Workgroup = 4 waves, one row, one chunk of kDecodeChunk keys; wave w
+// scores the chunk's 16-key blocks w, w + 4, ... The keys reach LDS by DMA, each instruction
+// copying 8 whole 128-byte key rows (1 KB contiguous in memory), into a ring of DK_NR block
+// slots per wave (no cross-wave synchronisation: a wave waits for its own DMAs only); the block's
+// operand is read back in the prefill kernel's swizzled layout, free of bank conflicts. The
+// queries are the A operand (M index c -> head 16 mm + c), four matrix instructions per block, the
+// ReLU and weighted head sum on the vector unit (score_block). The scores collect in LDS and go
+// out at the end as whole lines. With a candidate buffer (fused top-k), the workgroup then keeps
+// every key at or above a cut chosen from a histogram of the chunk's scores so that at least
+// decode_chunk_target(n, k) keys pass, and records the count, the cut and flags.
+constexpr int DK_W = 4;                 // waves per workgroup
+constexpr int DK_NR = 6;                // block slots per wave
+constexpr int DK_BLK = 16 * kDI;        // bytes of a 16-key block
+constexpr int DK_THREADS = DK_W * 64;
+
+// s_waitcnt vmcnt(n), n rounded down to an even value <= 2 DK_NR
+__device__ __forceinline__ void vm_wait_even(int n) {
+  static_assert(DK_NR <= 6, "vm_wait_even covers up to 12 outstanding operations");
+  switch (n) {
+    case 12: case 13: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
+    case 10: case 11: asm volatile("s_waitcnt vmcnt(10)" ::: "memory"); break;
+    case 8: case 9: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+    case 6: case 7: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
+    case 4: case 5: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+    case 2: case 3: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+  }
+}
+
+template <bool FUSED, bool KS>
+__global__ void __launch_bounds__(DK_THREADS, 2)
+indexer_fp8_decode_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
+                          const uint8_t* __restrict__ q, const uint8_t* __restrict__ k,
+                          const float* __restrict__ w, const float* __restrict__ kscale,
+                          float* __restrict__ scores, int64_t ld, DecodeCand cand) {
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[DK_W][DK_NR][DK_BLK];
+  __shared__ __attribute__((aligned(1024))) uint8_t qt[kHI * kDI + 1024];   // query tile, then weights
+  __shared__ __attribute__((aligned(16))) float sc[kDecodeChunk];
+  __shared__ uint32_t hist[FUSED ? 2048 : 1];
+  __shared__ uint32_t s_digit, s_above, s_cnt;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, c = lane & 15;
+  const int b = blockIdx.y, chunk = blockIdx.x;
+  const int r = cu_q[b];
+  if (cu_q[b + 1] == r) return;                    // a sequence without a query row
+  const int k0 = cu_k[b], n = cu_k[b + 1] - k0;    // the row sits at position n - 1
+  const int kbeg = chunk * kDecodeChunk;
+  if (kbeg >= n) return;                           // uniform over the workgroup
+  const int cnt = min(kDecodeChunk, n - kbeg);
+  const int nblk = (cnt + 15) >> 4;
+  const int nmine = nblk > wave ? (nblk - wave + DK_W - 1) / DK_W : 0;
+
+  // the sequence's keys as a buffer (n * 128 < 2^31 is checked on the host). DMA of the wave's
+  // block jb (chunk block wave + 4 jb) into slot jb % DK_NR: instruction i copies keys 8i .. 8i + 7
+  // of the block; lane l reads key 8i + l/8 (clamped to the last key; such rows are never stored),
+  // logical 16-byte chunk (l % 8) ^ key_swz(8i + l/8), which lands at physical chunk l % 8.
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(k + (int64_t)k0 * kDI), (short)0, n * kDI, 0x00020000);
+  const uint32_t ring_base = lds_addr(&ring[wave][0][0]);
+  const int ch0 = ((lane & 7) ^ key_swz(lane >> 3)) * 16, ch1 = ((lane & 7) ^ key_swz(8 | (lane >> 3))) * 16;
+  auto dma = [&](int jb) {
+    const int key0 = kbeg + (wave + DK_W * jb) * 16 + (lane >> 3);
+    const int slot = (jb % DK_NR) * DK_BLK;
+    lds_dma16(rs, ring_base, slot, min(key0, n - 1) * kDI + ch0, 0);
+    lds_dma16(rs, ring_base, slot + 1024, min(key0 + 8, n - 1) * kDI + ch1, 0);
+  };
+  // The row's query tile (8 KB) and head weights (256 B) come in by DMA too, before the keys:
+  // every vector memory operation of the main loop is then one of ours, counted exactly (a plain
+  // load would make the compiler wait for all outstanding ones inside the loop).
+  {
+    const __amdgpu_buffer_rsrc_t qs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(q + (int64_t)r * (kHI * kDI)), (short)0, kHI * kDI, 0x00020000);
+    const uint32_t qt_base = lds_addr(qt);
+    lds_dma16(qs, qt_base, (2 * wave) * 1024, lane * 16, (2 * wave) * 1024);
+    lds_dma16(qs, qt_base, (2 * wave + 1) * 1024, lane * 16, (2 * wave + 1) * 1024);
+    if (wave == 0) {   // lanes past the 256 weight bytes read zeros (outside the buffer)
+      const __amdgpu_buffer_rsrc_t wsr = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<float*>(w + (int64_t)r * kHI), (short)0, kHI * 4, 0x00020000);
+      lds_dma16(wsr, qt_base, kHI * kDI, lane * 16, 0);
+    }
+  }
+#pragma unroll
+  for (int jb = 0; jb < DK_NR; ++jb)
+    if (jb < nmine) dma(jb);
+  // the query tile and weights have landed once only the key DMAs issued after them are in flight
+  vm_wait_even(2 * min(DK_NR, nmine));
+  __syncthreads();
+
+  // A operand: M index c -> head 16 mm + c, K bytes of lane group g; weights of the lane's
+  // outputs (D row 4g + v -> head 16 mm + 4g + v)
+  v8i a[4];
+  {
+    const uint8_t* qrow = qt + c * kDI + g * 32;
+#pragma unroll
+    for (int mm = 0; mm < 4; ++mm) {
+      const v4i lo = *reinterpret_cast<const v4i*>(qrow + mm * 16 * kDI);
+      const v4i hi = *reinterpret_cast<const v4i*>(qrow + mm * 16 * kDI + 16);
+      a[mm] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+#pragma unroll
+    for (int mm = 0; mm < 4; ++mm) asm volatile("" : "+a"(a[mm]));
+  }
+  float wv[16];
+  {
+    const float* wr = reinterpret_cast<const float*>(qt + kHI * kDI);
+#pragma unroll
+    for (int mm = 0; mm < 4; ++mm)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) wv[4 * mm + v] = wr[mm * 16 + 4 * g + v];
+  }
+  // B operand of a block: lane (g, c) takes logical chunks 2g, 2g + 1 of key c
+  const int bx0 = ((2 * g) ^ key_swz(c)) * 16, bx1 = ((2 * g + 1) ^ key_swz(c)) * 16;
+  for (int jb = 0; jb < nmine; ++jb) {
+    // block jb has landed once at most the DMAs of the (up to DK_NR - 1) later blocks are in flight
+    vm_wait_even(2 * min(DK_NR - 1, nmine - 1 - jb));
+    const uint8_t* rowp = &ring[wave][jb % DK_NR][0] + c * kDI;
+    const v4i lo = *reinterpret_cast<const v4i*>(rowp + bx0);
+    const v4i hi = *reinterpret_cast<const v4i*>(rowp + bx1);
+    float acc = score_block<1>(a, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), wv);
+    acc += __shfl_xor(acc, 16);
+    acc += __shfl_xor(acc, 32);
+    if (g == 0) sc[(wave + DK_W * jb) * 16 + c] = acc;
+    if (jb + DK_NR < nmine) {   // refill this slot: its reads have completed
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      dma(jb + DK_NR);
+    }
+  }
+  __syncthreads();   // the chunk's scores are in LDS
+
+  // scores out as whole lines (entries past the row's end land in the part of the row that is
+  // left unspecified: ld >= round_up(n, 4)); per-key scales applied here
+  float* srow = scores + (int64_t)r * ld + kbeg;
+  for (int i = 4 * tid; i < cnt; i += 4 * DK_THREADS) {
+    float4 v = *reinterpret_cast<const float4*>(&sc[i]);
+    if (KS) {
+      const float* ks = kscale + k0 + kbeg + i;
+      v.x *= ks[0];
+      if (i + 1 < cnt) v.y *= ks[1];
+      if (i + 2 < cnt) v.z *= ks[2];
+      if (i + 3 < cnt) v.w *= ks[3];
+      *reinterpret_cast<float4*>(&sc[i]) = v;
+    }
+    *reinterpret_cast<float4*>(srow + i) = v;
+  }
+  if constexpr (FUSED) {
+    if (n <= cand.k) return;   // uniform: every candidate of the row is selected
+    const int target = decode_chunk_target(n, cand.k);
+    const int cap = decode_chunk_capacity(n, cand.k);
+    const int64_t cell = (int64_t)r * cand.nch + chunk;
+    uint32_t* mrow = cand.meta + cell * 4;
+    uint32_t* krow = cand.key + cell * cand.stride;
+    uint32_t* prow = cand.pos + cell * cand.stride;
+    if (KS) __syncthreads();   // the scaled scores are in LDS
+    if (cnt <= target) {       // uniform: keep every key
+      for (int i = tid; i < cnt; i += DK_THREADS) {
+        krow[i] = float_to_ordered(sc[i]);
+        prow[i] = (uint32_t)(kbeg + i);
+      }
+      if (tid == 0) {
+        mrow[0] = (uint32_t)cnt;
+        mrow[1] = 0u;
+        mrow[2] = 1u;
+      }
+      return;
+    }
+    // the bin of the top 11 key bits holding the target-th largest key; if that keeps more than
+    // 16 keys beyond the target, the bin of the next 11 bits inside it (keeping the merge's list
+    // short); more than `cap` even then (ties) marks the chunk as overflowing
+    for (int i = tid; i < 2048; i += DK_THREADS) hist[i] = 0;
+    __syncthreads();
+    for (int i = tid; i < cnt; i += DK_THREADS) atomicAdd(&hist[float_to_ordered(sc[i]) >> 21], 1u);
+    __syncthreads();
+    select_bin(hist, 2048, (uint32_t)target, &s_digit, &s_above);
+    const uint32_t d1 = s_digit, above1 = s_above;
+    uint32_t cut = d1 << 21, keep = above1 + hist[d1];
+    if (keep > (uint32_t)target + 16u) {   // uniform
+      __syncthreads();            // every thread has read hist[d1]
+      for (int i = tid; i < 2048; i += DK_THREADS) hist[i] = 0;
+      __syncthreads();
+      for (int i = tid; i < cnt; i += DK_THREADS) {
+        const uint32_t u = float_to_ordered(sc[i]);
+        if ((u >> 21) == d1) atomicAdd(&hist[(u >> 10) & 2047u], 1u);
+      }
+      __syncthreads();
+      select_bin(hist, 2048, (uint32_t)target - above1, &s_digit, &s_above);
+      cut |= s_digit << 10;
+      keep = above1 + s_above + hist[s_digit];
+    }
+    const bool over = keep > (uint32_t)cap;
+    if (tid == 0) s_cnt = 0;
+    __syncthreads();
+    if (!over) {
+      for (int i = tid; i < cnt; i += DK_THREADS) {
+        const uint32_t u = float_to_ordered(sc[i]);
+        if (u >= cut) {
+          const uint32_t at = atomicAdd(&s_cnt, 1u);   // < keep <= cap <= stride
+          krow[at] = u;
+          prow[at] = (uint32_t)(kbeg + i);
+        }
+      }
+    }
+    if (tid == 0) {
+      mrow[0] = over ? 0u : keep;
+      mrow[1] = cut;
+      mrow[2] = over ? 2u : 0u;
+    }
+  }
+}
+
+bool decode_fused_topk_ok(const SeqInfo& s, int k) {
+  return s.max_m == 1 && k <= 2048 && s.max_n <= 131072;
+}
+
+// Candidate slots per chunk: the capacity of the row with the fewest keys among those with more
+// than k (the capacity shrinks as rows grow).
+static int decode_cand_stride(const SeqInfo& s, int k) {
+  int nmin = 0;
+  for (int b = 0; b < s.B; ++b) {
+    const int m = s.cu_q_host[b + 1] - s.cu_q_host[b], n = s.cu_k_host[b + 1] - s.cu_k_host[b];
+    if (m > 0 && n > k && (nmin == 0 || n < nmin)) nmin = n;
+  }
+  return nmin ? decode_chunk_capacity(nmin, k) : 1;
+}
+
+static size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
+size_t decode_cand_bytes(const SeqInfo& s, int k) {
+  const size_t nch = (size_t)(s.max_n + kDecodeChunk - 1) / kDecodeChunk;
+  const size_t cells = (size_t)s.T * nch;
+  return 2 * round256(cells * decode_cand_stride(s, k) * sizeof(uint32_t)) + round256(cells * 16);
+}
+
+DecodeCand decode_cand_layout(const SeqInfo& s, int k, void* ws) {
+  DecodeCand d;
+  d.nch = (s.max_n + kDecodeChunk - 1) / kDecodeChunk;
+  d.stride = decode_cand_stride(s, k);
+  d.k = k;
+  const size_t cells = (size_t)s.T * d.nch;
+  const size_t kb = round256(cells * d.stride * sizeof(uint32_t));
+  char* p = static_cast<char*>(ws);
+  d.key = reinterpret_cast<uint32_t*>(p);
+  d.pos = reinterpret_cast<uint32_t*>(p + kb);
+  d.meta = reinterpret_cast<uint32_t*>(p + 2 * kb);
+  return d;
+}
+
 hipError_t launch_indexer_fp8_decode(const SeqInfo& s, const uint8_t* q, const uint8_t* k,
                                      const float* w, const float* kscale, float* scores,
-                                     int64_t ld, hipStream_t st) {
+                                     int64_t ld, const DecodeCand* cand, hipStream_t st) {
   if (s.T == 0 || s.max_n == 0) return hipSuccess;
-  constexpr int W = 4;
-  const int kc = 2048;
-  dim3 grid((s.max_n + kc - 1) / kc, s.B);
-  if (kscale)
-    hipLaunchKernelGGL((indexer_fp8_kernel<1, W, true, 4, true>), grid, dim3(W * 64), 0, st, s.B,
-                       s.cu_q, s.cu_k, q, k, w, kscale, scores, ld, kc);
+  const dim3 grid((s.max_n + kDecodeChunk - 1) / kDecodeChunk, s.B), block(DK_THREADS);
+  const DecodeCand cd = cand ? *cand : DecodeCand{};
+  if (cand && kscale)
+    hipLaunchKernelGGL((indexer_fp8_decode_kernel<true, true>), grid, block, 0, st, s.B, s.cu_q, s.cu_k, q, k,
+                       w, kscale, scores, ld, cd);
+  else if (cand)
+    hipLaunchKernelGGL((indexer_fp8_decode_kernel<true, false>), grid, block, 0, st, s.B, s.cu_q, s.cu_k, q, k,
+                       w, kscale, scores, ld, cd);
+  else if (kscale)
+    hipLaunchKernelGGL((indexer_fp8_decode_kernel<false, true>), grid, block, 0, st, s.B, s.cu_q, s.cu_k, q,
+                       k, w, kscale, scores, ld, cd);
   else
-    hipLaunchKernelGGL((indexer_fp8_kernel<1, W, true, 4, false>), grid, dim3(W * 64), 0, st, s.B,
-                       s.cu_q, s.cu_k, q, k, w, kscale, scores, ld, kc);
+    hipLaunchKernelGGL((indexer_fp8_decode_kernel<false, false>), grid, block, 0, st, s.B, s.cu_q, s.cu_k, q,
+                       k, w, kscale, scores, ld, cd);
   return hipGetLastError();
 }
 

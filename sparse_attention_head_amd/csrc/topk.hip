@@ -24,60 +24,6 @@ namespace dsa {
 constexpr int TK_THREADS = 1024;
 constexpr int TK_WAVES = TK_THREADS / 64;
 
-__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
-  const int lane = threadIdx.x & 63;
-  return (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
-}
-
-// Inclusive prefix sum over the 64 lanes of a wave: four shifts within each row of 16 lanes,
-// then each row's total broadcast into the rows above it (GCN data-parallel primitives).
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
-  x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xF, 0xF, false);   // row_shr:1
-  x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xF, 0xF, false);   // row_shr:2
-  x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xF, 0xF, false);   // row_shr:4
-  x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xF, 0xF, false);   // row_shr:8
-  x += __builtin_amdgcn_update_dpp(0u, x, 0x142, 0xA, 0xF, false);   // row_bcast:15 -> rows 1, 3
-  x += __builtin_amdgcn_update_dpp(0u, x, 0x143, 0xC, 0xF, false);   // row_bcast:31 -> rows 2, 3
-  return x;
-}
-
-// Finds the bin holding the need-th largest key among the counted ones (nb bins, a power of two
-// <= 2048; suffix sums from the top bin down). Called by all threads; wave 0 does the work: lane l
-// sums bins l*per .. l*per + per - 1 (read in a lane-rotated order, which spreads the lanes over
-// the banks), suffix sums across lanes (total minus a prefix scan) find the lane whose run holds
-// the need-th largest key, and a second scan over that run's bins (one bin per lane) finds the
-// bin.
-__device__ __forceinline__ void select_bin(const uint32_t* hist, int nb, uint32_t need,
-                                           uint32_t* s_digit, uint32_t* s_above) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (wave == 0) {
-    const int per = nb >= 64 ? nb >> 6 : 1;
-    uint32_t sum = 0;
-    if (lane * per < nb)
-      for (int j = 0; j < per; ++j) sum += hist[lane * per + ((j + lane) & (per - 1))];
-    const uint32_t pre = wave_incl_scan(sum);
-    const uint32_t total = __builtin_amdgcn_readlane(pre, 63);
-    const uint32_t suf = total - pre + sum;   // bins of this lane and above
-    const uint32_t above_lane = suf - sum;
-    // the crossing lane: its run holds the need-th largest key
-    const uint64_t hit = __ballot(suf >= need && above_lane < need);
-    const int cl = __builtin_amdgcn_readfirstlane(hit ? (int)(__ffsll((unsigned long long)hit) - 1) : 0);
-    const uint32_t above = __builtin_amdgcn_readlane(above_lane, cl);
-    // bins of that run, one per lane (lane j: bin cl*per + j), suffix sums within the run
-    const int bin = cl * per + lane;
-    const uint32_t h = (lane < per && bin < nb) ? hist[bin] : 0u;
-    const uint32_t pre2 = wave_incl_scan(h);
-    const uint32_t rs = __builtin_amdgcn_readlane(pre2, 63) - pre2 + h;
-    // the bin: above + (bins of the run above it) < need <= above + rs
-    const uint64_t hb = __ballot(lane < per && above + rs >= need && above + rs - h < need);
-    if (hb && lane == (int)(__ffsll((unsigned long long)hb) - 1)) {
-      *s_digit = (uint32_t)bin;
-      *s_above = above + rs - h;
-    }
-  }
-  __syncthreads();
-}
-
 // Exact selection for one row straight from global memory with NTH threads: three histogram
 // passes (key bits 31..21, 20..10, 9..0) find the k-th largest key T and how many keys equal to T
 // are taken (`need`); then an ordered compaction in position order keeps every key > T and the
@@ -200,9 +146,6 @@ constexpr int TK_TILE = 4 * TK_THREADS;      // positions per tile (one float4 p
 constexpr int TK_CHUNK_TILES = 2;              // tiles per staged chunk (32 KB)
 constexpr int TK_RING = 4;                     // staged chunks in flight
 
-__device__ __forceinline__ uint32_t lanes_below_count(uint64_t m) {
-  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-}
 
 // Register-resident selection for rows of up to 4096 * NT candidates (one workgroup per row).
 //  1. The row streams through LDS (4 chunks of 32 KB in flight, DMA) into registers: thread t
@@ -617,6 +560,62 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t x) {
   return __builtin_amdgcn_readlane(x, 63);
 }
 
+// Marks the selection among `total` listed keys (ckey, positions cpos < 32 nw) -- every key above
+// T and the `need` lowest positions among the keys equal to T -- in the row's bitmap (nw words,
+// cleared by the caller), then writes the marked positions in ascending order to out[0..).
+// Returns false (uniform, with nothing written to out) if more than TS_MAXEQ keys equal T; the
+// caller then selects the row exactly instead. hist holds the tied positions (>= TS_MAXEQ
+// words), scratch the tie select's histogram (2048 words; the key list may serve), *s_eq is zero
+// on entry. Called by every thread; begins with a barrier.
+__device__ __forceinline__ bool mark_and_emit(const uint32_t* ckey, const uint32_t* cpos, uint32_t total, uint32_t T,
+                              uint32_t need, int nw, uint32_t* bmap, uint32_t* hist, uint32_t* scratch,
+                              uint32_t* s_eq, uint32_t* s_digit, uint32_t* s_above, uint32_t* xch1,
+                              int32_t* out) {
+  const int tid = threadIdx.x;
+  __syncthreads();   // the histogram space is reused for the tied positions
+  for (uint32_t c = tid; c < total; c += TS_THREADS) {
+    const uint32_t u = ckey[c], p = cpos[c];
+    if (u > T) {
+      atomicOr(&bmap[p >> 5], 1u << (p & 31));
+    } else if (u == T) {
+      const uint32_t e = atomicAdd(s_eq, 1u);
+      if (e < (uint32_t)TS_MAXEQ) hist[e] = ~p;   // inverted: the largest are the lowest positions
+    }
+  }
+  __syncthreads();
+  const uint32_t eqc = *s_eq;
+  if (eqc > (uint32_t)TS_MAXEQ) return false;
+  // the tied keys taken are the `need` lowest positions: ~pos >= the need-th largest ~pos
+  uint32_t cut = 0u;
+  if (eqc > need) {
+    uint32_t unused;
+    cut = lds_select(hist, eqc, need, 31, 0, 0u, 0u, scratch, s_digit, s_above, &unused);
+  }
+  for (uint32_t e = tid; e < eqc; e += TS_THREADS) {
+    const uint32_t ip = hist[e];
+    if (ip >= cut) {
+      const uint32_t p = ~ip;
+      atomicOr(&bmap[p >> 5], 1u << (p & 31));
+    }
+  }
+  __syncthreads();
+  // one scan over the bitmap, ascending output
+  const int per = (nw + TS_THREADS - 1) / TS_THREADS;
+  const int w0 = min(tid * per, nw), w1 = min(w0 + per, nw);
+  uint32_t cnt = 0;
+  for (int w = w0; w < w1; ++w) cnt += (uint32_t)__popc(bmap[w]);
+  uint32_t unused3;
+  uint32_t slot = block_excl_scan2(cnt, 0u, xch1, unused3);
+  for (int w = w0; w < w1; ++w) {
+    uint32_t sel = bmap[w];
+    while (sel) {
+      out[slot++] = w * 32 + (__ffs(sel) - 1);
+      sel &= sel - 1;
+    }
+  }
+  return true;
+}
+
 __global__ void __launch_bounds__(TS_THREADS)
 topk_stream_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
                    const float* __restrict__ scores, int64_t ld, int k, int32_t* __restrict__ idx) {
@@ -809,51 +808,102 @@ topk_stream_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __res
   const uint32_t common = h < 0 ? 0xFFFFFFFFu : ~((2u << h) - 1u);   // h = 31: no common bits
   const uint32_t T = lds_select(ckey, total, (uint32_t)k, h, 0, F & common, common, hist, &s_digit,
                                 &s_above, &need);
-  __syncthreads();   // the histogram space is reused for the tied positions
-  for (uint32_t c = tid; c < total; c += TS_THREADS) {
-    const uint32_t u = ckey[c], p = cpos[c];
-    if (u > T) {
-      atomicOr(&bmap[p >> 5], 1u << (p & 31));
-    } else if (u == T) {
-      const uint32_t e = atomicAdd(&s_eq, 1u);
-      if (e < (uint32_t)TS_MAXEQ) hist[e] = ~p;   // inverted: the largest are the lowest positions
-    }
+  // 6. marking and ascending output
+  if (!mark_and_emit(ckey, cpos, total, T, need, nw, bmap, hist, ckey, &s_eq, &s_digit, &s_above,
+                     &xch[1][0][0], out))
+    topk_row_exact<TS_THREADS>(row, n, k, out, hist, xch, &s_digit, &s_above);
+}
+
+// ------------------------------------------------------------------------------------------
+// Merge of the fused decode top-k. The decode indexer kept, for every chunk of kDecodeChunk keys
+// of a row, every key at or above a cut (all of them when the chunk is short), with the count,
+// the cut and flags in the chunk's metadata. One workgroup per row gathers the kept keys, finds
+// the k-th largest T among them and `need` as the streaming kernel does, and checks that no chunk
+// dropped a key that could rank: every chunk that dropped keys must have its cut at or below T
+// (its dropped keys are then below T, so the kept keys contain every key above T and every key
+// equal to T). If that fails, a chunk overflowed, or the kept keys do not fit in LDS, the row is
+// selected exactly from its scores instead.
+constexpr int TM_HCAP = 12288;                        // kept keys of a row held in LDS
+constexpr int TM_MAXCH = TS_MAXN / kDecodeChunk;      // chunks of a row (128)
+
+__global__ void __launch_bounds__(TS_THREADS)
+topk_merge_decode_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
+                         const float* __restrict__ scores, int64_t ld, int k, int32_t* __restrict__ idx,
+                         DecodeCand cand) {
+  __shared__ uint32_t hist[2048];
+  __shared__ __attribute__((aligned(16))) uint32_t ckey[TM_HCAP];
+  __shared__ uint32_t cpos[TM_HCAP];
+  __shared__ uint32_t bmap[TS_MAXN / 32];
+  __shared__ uint32_t c_off[TM_MAXCH], c_cnt[TM_MAXCH];
+  __shared__ uint32_t xch[2][TS_WAVES][2];
+  __shared__ uint32_t s_digit, s_above, s_eq, s_bad;
+  static_assert(TM_HCAP >= 2048, "the key list doubles as the tie select's histogram");
+
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const RowLoc L = locate_row(cu_q, cu_k, B, r);
+  const int n = L.pos + 1;
+  int32_t* out = idx + (int64_t)r * k;
+  const float* row = scores + (int64_t)r * ld;
+  if (n <= k) {
+    for (int i = tid; i < k; i += TS_THREADS) out[i] = i < n ? i : -1;
+    return;
   }
-  __syncthreads();
-  const uint32_t eqc = s_eq;
-  if (eqc > (uint32_t)TS_MAXEQ) {
+  const int nch = (n + kDecodeChunk - 1) / kDecodeChunk;   // <= TM_MAXCH (n <= TS_MAXN)
+  const uint32_t* meta = cand.meta + (int64_t)r * cand.nch * 4;
+  uint32_t cnt = 0, over = 0;
+  if (tid < nch) {
+    cnt = meta[4 * tid];
+    over = (meta[4 * tid + 2] >> 1) & 1u;
+  }
+  uint32_t unused;
+  const uint32_t off = block_excl_scan2(cnt, over, &xch[0][0][0], unused);
+  uint32_t total = 0, overflow = 0;
+  for (int w = 0; w < TS_WAVES; ++w) {
+    total += xch[0][w][0];
+    overflow += xch[0][w][1];
+  }
+  if (overflow || total > (uint32_t)TM_HCAP || total < (uint32_t)k) {   // uniform
+    __syncthreads();   // the fallback reuses xch
     topk_row_exact<TS_THREADS>(row, n, k, out, hist, xch, &s_digit, &s_above);
     return;
   }
-  // the tied keys taken are the `need` lowest positions: ~pos >= the need-th largest ~pos
-  uint32_t cut = 0u;
-  if (eqc > need) {
-    uint32_t unused2;
-    cut = lds_select(hist, eqc, need, 31, 0, 0u, 0u, ckey, &s_digit, &s_above, &unused2);   // ckey is free now
+  if (tid < nch) {
+    c_off[tid] = off;
+    c_cnt[tid] = cnt;
   }
-  for (uint32_t e = tid; e < eqc; e += TS_THREADS) {
-    const uint32_t ip = hist[e];
-    if (ip >= cut) {
-      const uint32_t p = ~ip;
-      atomicOr(&bmap[p >> 5], 1u << (p & 31));
-    }
+  const int nw = (n + 31) >> 5;
+  for (int i = tid; i < nw; i += TS_THREADS) bmap[i] = 0;
+  if (tid == 0) {
+    s_eq = 0;
+    s_bad = 0;
   }
   __syncthreads();
-
-  // 6. one scan over the bitmap, ascending output
-  const int per = (nw + TS_THREADS - 1) / TS_THREADS;
-  const int w0 = min(tid * per, nw), w1 = min(w0 + per, nw);
-  uint32_t cnt = 0;
-  for (int w = w0; w < w1; ++w) cnt += (uint32_t)__popc(bmap[w]);
-  uint32_t unused3;
-  uint32_t slot = block_excl_scan2(cnt, 0u, &xch[1][0][0], unused3);
-  for (int w = w0; w < w1; ++w) {
-    uint32_t sel = bmap[w];
-    while (sel) {
-      out[slot++] = w * 32 + (__ffs(sel) - 1);
-      sel &= sel - 1;
+  // gather: wave w copies the kept keys of chunks w, w + 16, ...
+  for (int ch = wave; ch < nch; ch += TS_WAVES) {
+    const int64_t src = ((int64_t)r * cand.nch + ch) * cand.stride;
+    const uint32_t o = c_off[ch], cc = c_cnt[ch];
+    for (uint32_t j = lane; j < cc; j += 64) {
+      ckey[o + j] = cand.key[src + j];
+      cpos[o + j] = cand.pos[src + j];
     }
   }
+  // (lds_select starts with a barrier)
+  uint32_t need;
+  const uint32_t T = lds_select(ckey, total, (uint32_t)k, 31, 0, 0u, 0u, hist, &s_digit, &s_above, &need);
+  if (tid < nch && (meta[4 * tid + 2] & 1u) == 0 && meta[4 * tid + 1] > T) s_bad = 1;
+  __syncthreads();
+  if (s_bad || !mark_and_emit(ckey, cpos, total, T, need, nw, bmap, hist, ckey, &s_eq, &s_digit, &s_above,
+                              &xch[1][0][0], out))
+    topk_row_exact<TS_THREADS>(row, n, k, out, hist, xch, &s_digit, &s_above);
+}
+
+hipError_t launch_topk_merge_decode(const SeqInfo& s, const float* scores, int64_t ld, int k,
+                                    int32_t* idx, const DecodeCand& cand, hipStream_t st) {
+  if (s.T == 0) return hipSuccess;
+  hipLaunchKernelGGL(topk_merge_decode_kernel, dim3(s.T), dim3(TS_THREADS), 0, st, s.B, s.cu_q, s.cu_k,
+                     scores, ld, k, idx, cand);
+  return hipGetLastError();
 }
 
 size_t topk_workspace_bytes(const SeqInfo&, int) { return 0; }

@@ -43,6 +43,12 @@ def to_np_bf16(t):
     return t.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
+def _same_causal_scores(wl, a, b):
+    """Score rows equal on their causal part (entries past a row's position are unspecified)."""
+    _, pos = wl.row_positions()
+    return all(np.array_equal(a[r, :p + 1], b[r, :p + 1]) for r, p in enumerate(pos))
+
+
 def run_all(gpu, wl, x):
     seqs = gpu.Seqs(wl.cu_seqlens_q, wl.cu_seqlens_k)
     T = {k: dev(v) for k, v in x.items() if k not in ("cu_seqlens_q", "cu_seqlens_k")}
@@ -52,6 +58,11 @@ def run_all(gpu, wl, x):
     fwd = gpu.Forward(seqs, T["qI"], T["kI"], T["w"], T["q"], T["kv"], wl.k, wl.scale, wl.d_v,
                       keep_scores=True, keep_indices=True)
     fout, flse = fwd()
+    if wl.idx_dtype == "fp8" or wl.max_seqlen_q == 1:   # the fused indexer -> top-k call
+        tsc, tidx = gpu.indexer_topk(seqs, T["qI"], T["kI"], T["w"], wl.k)
+        torch.cuda.synchronize()
+        assert np.array_equal(tidx.cpu().numpy(), idx.cpu().numpy()), "indexer_topk indices differ"
+        assert _same_causal_scores(wl, tsc.cpu().numpy(), scores.cpu().numpy()), "indexer_topk scores differ"
     torch.cuda.synchronize()
     return dict(scores=scores.cpu().numpy(), idx=idx.cpu().numpy(), out=out, lse=lse.cpu().numpy(),
                 fscores=fwd.scores.cpu().numpy(), fidx=fwd.indices.cpu().numpy(), fout=fout,
@@ -141,6 +152,60 @@ def test_indexer_linear_split_exact(gpu, shape):
     x = dict(dg.gen_inputs(wl, "normal", seed=2, parts=("attn",)), **dg.gen_linear_split(wl, seed=2))
     res = run_all(gpu, wl, x)
     check_rows(wl, x, res, range(wl.T), "split", None)
+
+
+def _fused_decode_indices(gpu, wl, x):
+    """Indices of the fused indexer -> top-k call (decode batches: the indexer keeps per-chunk
+    candidates and a merge selects) and of the separate indexer + top-k calls on the same inputs."""
+    seqs = gpu.Seqs(wl.cu_seqlens_q, wl.cu_seqlens_k)
+    T = {kk: dev(v) for kk, v in x.items() if kk in ("qI", "kI", "w")}
+    fsc, fidx = gpu.indexer_topk(seqs, T["qI"], T["kI"], T["w"], wl.k)
+    scores = gpu.indexer_scores(seqs, T["qI"], T["kI"], T["w"])
+    idx = gpu.topk(seqs, scores, wl.k)
+    torch.cuda.synchronize()
+    assert _same_causal_scores(wl, fsc.cpu().numpy(), scores.cpu().numpy()), "fused and separate scores differ"
+    return fidx.cpu().numpy(), idx.cpu().numpy(), fsc.cpu().numpy()
+
+
+@pytest.mark.parametrize("k", [2048, 64])
+def test_decode_fused_topk_rows(gpu, k):
+    """The fused decode top-k on integer inputs (exact scores) against the oracle, bit for bit:
+    rows of k + 1 keys up to the longest supported (131072), with ordinary rows and rows built to
+    defeat the per-chunk candidates -- the top scores all in one chunk (the merge must detect that
+    the chunk dropped keys above the threshold and select exactly from the scores), all scores
+    equal (every chunk overflows on ties), and scores with only a few distinct values (many ties
+    at the threshold across chunks, lowest positions first)."""
+    lens = [k + 1, 3000, 5000, 32768, 65537, 131072, 40000, 40000, 40000, 1, 17]
+    wl = dg.custom(name="fused_decode", seqlens_q=[1] * len(lens), seqlens_k=lens, H_I=64, d_I=128, k=k,
+                   H=128, d_qk=576, d_v=512, idx_dtype="fp8", attn_dtype="bf16", wid=38)
+    x = dg.gen_inputs(wl, "int", seed=11, parts=("idx",))
+    cu_k = wl.cu_seqlens_k
+    qI, kI, w = x["qI"], x["kI"].copy(), x["w"].copy()
+    three = dg.to_fp8_e4m3fn_bytes(np.full(1, 3.0, np.float32))[0]
+    # row 6: keys 5000..6023 (one chunk) score far above every other key
+    qI = qI.copy()
+    qI[6] = three
+    w[6] = 1.0
+    kI[cu_k[6] + 5000:cu_k[6] + 6024] = three
+    # row 7: all scores zero
+    w[7] = 0.0
+    # row 8: ternary keys and queries, one head: scores take a few values only
+    t = dg.gen_ternary(wl, seed=3)
+    qI[8] = t["qI"][8]
+    kI[cu_k[8]:cu_k[9]] = t["kI"][cu_k[8]:cu_k[9]]
+    w[8] = 0.0
+    w[8, 5] = 0.5
+    x.update(qI=qI, kI=kI, w=w)
+    fidx, sidx, fsc = _fused_decode_indices(gpu, wl, x)
+    sq = Seqs(wl.cu_seqlens_q, wl.cu_seqlens_k)
+    for r in range(wl.T):
+        ref_sc = oracle.indexer_scores_row(sq, x["qI"], x["kI"], x["w"], r)
+        _, pos, _, _ = sq.locate(r)
+        assert np.array_equal(fsc[r, :pos + 1].astype(np.float64), ref_sc), f"row {r}: scores"
+        ref = oracle.topk_row(ref_sc, k)
+        assert fidx[r].tolist() == ref.tolist(), f"row {r} (n = {lens[r]}): fused top-k differs from the oracle"
+        assert np.array_equal(sidx[r], fidx[r]), f"row {r}: fused and separate top-k differ"
+    assert fidx[7, :k].tolist() == list(range(k))
 
 
 @pytest.mark.parametrize("variant", ["int", "normal"])
