@@ -244,6 +244,24 @@ size_t dsa_forward_workspace_size(const dsa_seqs_t* seqs, const dsa_forward_args
 dsa_status_t dsa_forward(const dsa_seqs_t* seqs, const dsa_forward_args_t* args, void* ws,
                          size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------- fused forward, no allocation
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid it): dsa_forward with the workspace taken from a static device
+ * array of DSA_NOALLOC_SCRATCH_BYTES inside the library instead of a caller buffer. The call
+ * allocates nothing (no hipMalloc, hipFree or allocating library routine).
+ *   - Runs on the current device, whose own copy of the array it uses; `stream` must belong to
+ *     that device. The array's address is looked up once per device (hipGetSymbolAddress).
+ *   - Batches whose dsa_forward_workspace_size exceeds DSA_NOALLOC_SCRATCH_BYTES are rejected
+ *     with DSA_ERR_WORKSPACE before anything is enqueued (decode batches of up to 128 rows of
+ *     128K keys fit; long prefills do not).
+ *   - Every call on a device shares that device's array: calls that overlap in time on one
+ *     device (different streams, or threads) race and give wrong results; serialise them. The
+ *     array keeps the last call's contents; nothing in it needs to start at zero.
+ * Results are identical to dsa_forward's on the same arguments.
+ */
+#define DSA_NOALLOC_SCRATCH_BYTES (128ull << 20)
+dsa_status_t dsa_forward_noalloc(const dsa_seqs_t* seqs, const dsa_forward_args_t* args, void* stream);
+
 /* ---------------------------------------------------------------- indexer-alignment target
  * The training signal of the indexer (paper digest page, "Key claims", paper section 2.1.1,
  * Eq. 3-4, and "Method": a KL loss pulls the indexer's output towards the main attention's

@@ -91,6 +91,7 @@ _c_attn = _proto("dsa_sparse_mla_attn", ctypes.c_int,
 _c_fwd_ws = _proto("dsa_forward_workspace_size", ctypes.c_size_t, [ctypes.POINTER(_Seqs), ctypes.POINTER(_FwdArgs)])
 _c_fwd = _proto("dsa_forward", ctypes.c_int,
                 [ctypes.POINTER(_Seqs), ctypes.POINTER(_FwdArgs), _vp, ctypes.c_size_t, _vp])
+_c_fwd_na = _proto("dsa_forward_noalloc", ctypes.c_int, [ctypes.POINTER(_Seqs), ctypes.POINTER(_FwdArgs), _vp])
 _c_align = _proto("dsa_indexer_alignment", ctypes.c_int,
                   [ctypes.POINTER(_Seqs), ctypes.c_int32, ctypes.c_int32, ctypes.c_int, _vp, _vp, _vp,
                    ctypes.c_int32, ctypes.c_float, _vp, _vp, ctypes.c_int64, _vp, _vp, _vp])
@@ -101,7 +102,8 @@ _c_abi = _proto("dsa_abi_version", ctypes.c_int32, [])
 EXPORTS = ("dsa_indexer_workspace_size", "dsa_indexer_scores", "dsa_indexer_scaled_workspace_size",
            "dsa_indexer_scores_scaled", "dsa_topk_workspace_size", "dsa_topk", "dsa_indexer_topk_workspace_size",
            "dsa_indexer_topk", "dsa_sparse_mla_attn_workspace_size",
-           "dsa_sparse_mla_attn", "dsa_forward_workspace_size", "dsa_forward", "dsa_indexer_alignment",
+           "dsa_sparse_mla_attn", "dsa_forward_workspace_size", "dsa_forward", "dsa_forward_noalloc",
+           "dsa_indexer_alignment",
            "dsa_status_string",
            "dsa_last_error", "dsa_abi_version")
 
@@ -452,11 +454,19 @@ def indexer_alignment(seqs: Seqs, q, kv, indices, scale: float, lse, scores, wit
     return target, kl
 
 
+NOALLOC_SCRATCH_BYTES = 128 << 20
+
+
 class Forward:
-    """Fused indexer -> top-k -> attention with a reusable workspace (one allocation per shape)."""
+    """Fused indexer -> top-k -> attention with a reusable workspace (one allocation per shape).
+
+    With noalloc=True the calls go to dsa_forward_noalloc, whose workspace is the library's
+    static device scratch (no workspace is allocated here; outputs still are, once, at
+    construction)."""
 
     def __init__(self, seqs: Seqs, q_idx, k_idx, w, q, kv, k: int, scale: float, d_v: int = None,
-                 keep_scores=False, keep_indices=False, with_lse=True, q_idx_scale=None, k_idx_scale=None):
+                 keep_scores=False, keep_indices=False, with_lse=True, q_idx_scale=None, k_idx_scale=None,
+                 noalloc=False):
         torch = _torch()
         self.seqs = seqs
         H_I, d_I = _check_indexer_args(seqs, q_idx, k_idx, w)
@@ -496,11 +506,16 @@ class Forward:
         self._cs = seqs.c()
         wsz = int(_c_fwd_ws(ctypes.byref(self._cs), ctypes.byref(a)))
         self.ws_bytes = wsz
-        self.ws = torch.empty(max(wsz, 1), dtype=torch.uint8, device=dev)
+        self.noalloc = bool(noalloc)
+        self.ws = None if self.noalloc else torch.empty(max(wsz, 1), dtype=torch.uint8, device=dev)
 
     def __call__(self, stream=None):
-        _check(_c_fwd(ctypes.byref(self._cs), ctypes.byref(self._args), _ptr(self.ws), self.ws_bytes,
-                      _stream(stream)), "dsa_forward")
+        if self.noalloc:
+            _check(_c_fwd_na(ctypes.byref(self._cs), ctypes.byref(self._args), _stream(stream)),
+                   "dsa_forward_noalloc")
+        else:
+            _check(_c_fwd(ctypes.byref(self._cs), ctypes.byref(self._args), _ptr(self.ws), self.ws_bytes,
+                          _stream(stream)), "dsa_forward")
         return self.out, self.lse
 
 

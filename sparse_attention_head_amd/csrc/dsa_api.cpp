@@ -7,6 +7,7 @@
 #include <climits>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 
 #include "dsa_internal.h"
 
@@ -241,6 +242,34 @@ ForwardPlan plan_forward(const dsa::SeqInfo& s, const dsa_forward_args_t* a) {
   return p;
 }
 
+// ---------------------------------------------------------------- scratch of dsa_forward_noalloc
+// One static device array per GPU (each device that loads the library holds its own copy until
+// the process ends). In host code `scratch` only names the symbol: its device address comes from
+// hipGetSymbolAddress, once per device with that device current, and only that address is ever
+// passed to kernels.
+static __device__ __align__(256) uint8_t scratch[DSA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+dsa_status_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(DSA_ERR_UNSUPPORTED, "device index %d >= %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(DSA_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ok();
+}
+
 }  // namespace
 
 
@@ -445,6 +474,25 @@ dsa_status_t dsa_forward(const dsa_seqs_t* seqs, const dsa_forward_args_t* a, vo
   return run_attn(s, a->H, a->d_qk, a->d_v, a->dtype, a->q, a->kv, p.implicit_idx ? nullptr : idx,
                   a->k, a->softmax_scale, a->out, a->lse, p.attn_bytes ? base + p.attn_off : nullptr,
                   p.attn_bytes, hs);
+}
+
+dsa_status_t dsa_forward_noalloc(const dsa_seqs_t* seqs, const dsa_forward_args_t* args, void* stream) {
+  dsa::SeqInfo s;
+  dsa_status_t st = check_seqs(seqs, s);
+  if (st != DSA_OK) return st;
+  if (!args) return fail(DSA_ERR_NULL, "args is NULL");
+  if (s.B == 0) return ok();
+  const size_t need = plan_forward(s, args).total;
+  if (need > DSA_NOALLOC_SCRATCH_BYTES)
+    return fail(DSA_ERR_WORKSPACE, "dsa_forward_noalloc: this batch needs %zu bytes of workspace, more than "
+                "the %llu-byte scratch (use dsa_forward with a caller workspace)", need,
+                (unsigned long long)DSA_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (need > 0) {
+    st = scratch_address(&ws);
+    if (st != DSA_OK) return st;
+  }
+  return dsa_forward(seqs, args, ws, need, stream);
 }
 
 dsa_status_t dsa_indexer_alignment(const dsa_seqs_t* seqs, int32_t H, int32_t d_qk, dsa_dtype_t dtype,

@@ -113,6 +113,15 @@ int main(void) {
   a.softmax_scale = 0.0f;
   EXPECT(dsa_forward(&s, &a, p, fws, NULL), DSA_ERR_SHAPE);
   if (dsa_forward_workspace_size(NULL, &a) != 0 || dsa_forward_workspace_size(&s, NULL) != 0) ++failures;
+  /* the no-allocation variant rejects a batch beyond its scratch before touching a device */
+  const int32_t cqp[] = {0, 6000}, ckp[] = {0, 6000};
+  dsa_seqs_t pre = make_seqs(cqp, ckp, 1, 6000, 6000);
+  a.softmax_scale = 0.04f;
+  a.k = 2048;
+  if (dsa_forward_workspace_size(&pre, &a) <= DSA_NOALLOC_SCRATCH_BYTES) ++failures;
+  EXPECT(dsa_forward_noalloc(&pre, &a, NULL), DSA_ERR_WORKSPACE);
+  EXPECT(dsa_forward_noalloc(&pre, NULL, NULL), DSA_ERR_NULL);
+  EXPECT(dsa_forward_noalloc(&empty, &a, NULL), DSA_OK);
 
   /* alignment target */
   EXPECT(dsa_indexer_alignment(&s, 128, 576, DSA_F32, p, p, p, 64, 0.04f, (const float*)p, (const float*)p,

@@ -306,3 +306,24 @@ def test_binding_rejects_bad_forward_arguments(dsa):
         dsa.Forward(seqs, x["qI"], x["kI"], x["w"], x["q"], x["kv"], 64, 0.04, k_idx_scale=torch.ones(5))
     with pytest.raises(ValueError, match="GPU"):
         dsa.Forward(seqs, x["qI"], x["kI"], x["w"], x["q"], x["kv"], 64, 0.04)
+
+
+def test_noalloc_forward_rejects_oversized_batches_without_a_device(dsa):
+    """dsa_forward_noalloc checks the batch's workspace against its static scratch before touching
+    a device: a 5000-row prefill (scores 100 MB and indices 41 MB, more than the scratch) is rejected
+    with DSA_ERR_WORKSPACE, and B = 0 is a no-op."""
+    sq = FakeSeqs(dsa, [0, 5000], [0, 5000])
+    keep, p = buf(64)
+    a = dsa._FwdArgs()
+    a.H_I, a.d_I, a.qk_dtype = 64, 128, dsa.DSA_FP8_E4M3
+    a.q_idx = a.k_idx = a.w = p
+    a.k = 2048
+    a.H, a.d_qk, a.d_v, a.dtype = 128, 576, 512, dsa.DSA_BF16
+    a.q = a.kv = a.out = a.lse = p
+    a.softmax_scale = 0.04
+    assert dsa._c_fwd_ws(sq.ref, ctypes.byref(a)) > dsa.NOALLOC_SCRATCH_BYTES
+    assert dsa._c_fwd_na(sq.ref, ctypes.byref(a), None) == dsa.DSA_ERR_WORKSPACE
+    assert b"scratch" in dsa._c_last()
+    assert dsa._c_fwd_na(sq.ref, None, None) == dsa.DSA_ERR_NULL
+    empty = FakeSeqs(dsa, [0], [0], max_m=0, max_n=0)
+    assert dsa._c_fwd_na(empty.ref, ctypes.byref(a), None) == dsa.DSA_OK
