@@ -379,7 +379,8 @@ constexpr int PF_RW = 4;                // rows per wave
 constexpr int PF_ROWS = PF_W * PF_RW;   // 32
 constexpr int PF_SK = 256;              // keys per stage
 constexpr int PF_NR = 3;                // stages in the ring
-constexpr int PF_KC_MAX = 8192;         // keys per workgroup (chunk) at most
+constexpr int PF_KC_MAX = 8192;         // keys per workgroup (chunk) at most with key scales (twice that without)
+constexpr int PF_STW = PF_SK + 16;      // words per staged score row
 
 // KS: every score is multiplied by the per-key scale kscale[key row] (positive); the chunk's
 // scales sit in LDS (32 KB more).
@@ -392,6 +393,10 @@ indexer_fp8_prefill_kernel(int B, const int32_t* __restrict__ cu_q, const int32_
                            float* __restrict__ scores, int64_t ld, int KC) {
   __shared__ __attribute__((aligned(1024))) uint8_t kst[PF_NR][PF_SK * kDI];
   __shared__ float ksc[KS ? PF_KC_MAX : 1];
+  // unscaled kernel: each wave's 4 rows x 256 scores of a whole stage collect here (rows padded to
+  // PF_STW words: the pipeline's writes and the row reads are free of bank conflicts) and leave as
+  // four 1 KB row stores, so that every 128-byte line of a score row is written whole at once
+  __shared__ __attribute__((aligned(16))) float stw[KS ? 1 : PF_W * PF_RW * PF_STW];
   constexpr int HPM = 4, NMF = 16;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
@@ -474,17 +479,22 @@ indexer_fp8_prefill_kernel(int B, const int32_t* __restrict__ cu_q, const int32_
   };
 
   // Vector memory operations complete in issue order, so the wait for stage st's DMA may leave
-  // the operations issued after it in flight: the score stores of a whole stage (16 per wave),
-  // the next stage's DMA (4), the stores of the stage after. `fast1`/`fast2`: stage st-1 / st-2
-  // ran the whole-stage path, whose 16 stores are certain (other stages count as 0).
+  // the operations issued after it in flight: the score stores of a whole stage (4 row stores
+  // per wave, 16 direct stores in the scaled kernel), the next stage's DMA (4), the stores of the
+  // stage after. `fast1`/`fast2`: stage st-1 / st-2 ran the whole-stage path, whose stores are
+  // certain (other stages count as 0).
+  constexpr int SPS = KS ? 16 : PF_RW;   // stores per whole stage and wave
+  float* const stw_wave = stw + (KS ? 0 : wave * PF_RW * PF_STW);
   bool fast1 = false, fast2 = false;
   for (int st = 0; st < nst; ++st) {
-    const int after = (st == 0) ? 0 : 16 * fast2 + 16 * fast1 + 4 * (st + 1 < nst);
+    const int after = (st == 0) ? 0 : SPS * fast2 + SPS * fast1 + 4 * (st + 1 < nst);
     switch (after) {
       case 36: asm volatile("s_waitcnt vmcnt(36)" ::: "memory"); break;
       case 32: asm volatile("s_waitcnt vmcnt(32)" ::: "memory"); break;
       case 20: asm volatile("s_waitcnt vmcnt(20)" ::: "memory"); break;
       case 16: asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); break;
+      case 12: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
+      case 8: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
       case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
       default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
     }
@@ -500,8 +510,19 @@ indexer_fp8_prefill_kernel(int B, const int32_t* __restrict__ cu_q, const int32_
     if (fast) {
       // whole stage for 4 valid rows: every score lands below wkend <= n <= ld (keys past a row's
       // own position fall in the part of the row the interface leaves unspecified)
-      stage_pipeline<PF_SK / 16, KS>(buf + c * kDI, bx0, bx1, a, al, wt, lsc, hi2, hi1,
-                                     srow + sbase + kofs, ksc + (sbase - kbeg) + kofs);
+      if constexpr (KS) {
+        stage_pipeline<PF_SK / 16, KS>(buf + c * kDI, bx0, bx1, a, al, wt, lsc, hi2, hi1,
+                                       srow + sbase + kofs, ksc + (sbase - kbeg) + kofs);
+      } else {
+        stage_pipeline<PF_SK / 16, KS>(buf + c * kDI, bx0, bx1, a, al, wt, lsc, hi2, hi1,
+                                       stw_wave + (c >> 2) * PF_STW + kofs, nullptr);
+        // (one wave writes and reads its own rows: its LDS operations complete in order)
+#pragma unroll
+        for (int rr = 0; rr < PF_RW; ++rr) {
+          const float4 v = *reinterpret_cast<const float4*>(stw_wave + rr * PF_STW + 4 * lane);
+          *reinterpret_cast<float4*>(scores + (int64_t)(q0 + wrow0 + rr) * ld + sbase + 4 * lane) = v;
+        }
+      }
     } else {
       const int nblk = min(PF_SK, wkend - sbase) > 0 ? (min(PF_SK, wkend - sbase) + 15) / 16 : 0;
       for (int blk = 0; blk < nblk; ++blk) {
@@ -520,10 +541,12 @@ size_t indexer_workspace_bytes(const SeqInfo& s, bool fp8) {
   return (size_t)s.T * LIN_BYTES + ((size_t)s.T * sizeof(float) + 255) / 256 * 256;
 }
 
-// Key-chunk length: long enough to amortise loading the query tile, short enough to give
-// several workgroups per compute unit.
-static int pick_chunk(int64_t tiles, int max_n, int cus, int align) {
-  int kc = 8192;
+// Key-chunk length: long enough to amortise loading the query tile (each chunk reads it again:
+// 16384-key chunks halve the query re-reads of 8192-key ones at the 128K chunk), short enough to
+// give several workgroups per compute unit. The scaled kernel keeps its chunk's key scales in LDS
+// and stays at 8192.
+static int pick_chunk(int64_t tiles, int max_n, int cus, int align, int kc_max) {
+  int kc = kc_max;
   while (kc > 512 && tiles * ((max_n + kc - 1) / kc) < 4LL * cus) kc >>= 1;
   return (kc / align) * align;
 }
@@ -537,9 +560,8 @@ hipError_t launch_indexer_fp8_prefill(const SeqInfo& s, const uint8_t* q, const 
   hipLaunchKernelGGL(indexer_fp8_linear_kernel, dim3((s.T + 3) / 4), dim3(256), 0, st, s.T, q, w,
                      pieces, piece_exp);
   const int tiles = (s.max_m + PF_ROWS - 1) / PF_ROWS;
-  const int kc = pick_chunk((int64_t)tiles * s.B, s.max_n, kTargetCUs, PF_SK);
+  const int kc = pick_chunk((int64_t)tiles * s.B, s.max_n, kTargetCUs, PF_SK, kscale ? PF_KC_MAX : 2 * PF_KC_MAX);
   dim3 grid(tiles, (s.max_n + kc - 1) / kc, s.B);
-  static_assert(PF_KC_MAX >= 8192, "pick_chunk returns at most 8192 keys");
   if (kscale)
     hipLaunchKernelGGL(indexer_fp8_prefill_kernel<true>, grid, dim3(PF_W * 64), 0, st, s.B, s.cu_q,
                        s.cu_k, q, k, w, pieces, piece_exp, kscale, scores, ld, kc);

@@ -469,12 +469,12 @@ topk_reg_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restri
 // speed, and workgroups of sixteen waves with 76 KB of LDS, two per compute unit (the full 32
 // waves), so that the selection work of one row overlaps the streaming of another and the
 // latency-bound selection phases run on more threads.
-//  1. A sample of the row (all of it up to 8192 positions, else 8 evenly spaced runs of 256, 512
-//     or 1024 positions, about n/16 in all) is
-//     kept in LDS; two radix digits (22 key bits) locate its `want`-th largest key and the floor F
-//     is that 22-bit bin's lower edge. With the whole row as sample want = k, so at least k keys
-//     reach F; otherwise want = 1.3 k S / n aims at about 1.3 k keys (3 sigma above k and about
-//     4 sigma below the list's capacity for independent scores).
+//  0. Rows of at most 8192 positions are read into LDS whole and selected there directly: three
+//     radix digits give the k-th largest key, then steps 5 and 6 below run on that copy.
+//  1. Longer rows: a sample of 8 evenly spaced runs of 256, 512 or 1024 positions (about n/16 in
+//     all) is kept in LDS; two radix digits (22 key bits) locate its `want`-th largest key and the
+//     floor F is that 22-bit bin's lower edge; want = 1.3 k S / n aims at about 1.3 k keys (3
+//     sigma above k and about 4 sigma below the list's capacity for independent scores).
 //  2. The stream works on groups of 4 consecutive scores (one float4 per lane): a group whose
 //     maximum reaches F is appended whole, with its position, to a list in LDS (structure of
 //     arrays). Per batch of 4 groups per lane one atomic per wave reserves the slots; each lane
@@ -560,7 +560,8 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t x) {
   return __builtin_amdgcn_readlane(x, 63);
 }
 
-// Marks the selection among `total` listed keys (ckey, positions cpos < 32 nw) -- every key above
+// Marks the selection among `total` listed keys (ckey, positions cpos < 32 nw, or the list index
+// when cpos is NULL: a whole row) -- every key above
 // T and the `need` lowest positions among the keys equal to T -- in the row's bitmap (nw words,
 // cleared by the caller), then writes the marked positions in ascending order to out[0..).
 // Returns false (uniform, with nothing written to out) if more than TS_MAXEQ keys equal T; the
@@ -574,7 +575,7 @@ __device__ __forceinline__ bool mark_and_emit(const uint32_t* ckey, const uint32
   const int tid = threadIdx.x;
   __syncthreads();   // the histogram space is reused for the tied positions
   for (uint32_t c = tid; c < total; c += TS_THREADS) {
-    const uint32_t u = ckey[c], p = cpos[c];
+    const uint32_t u = ckey[c], p = cpos ? cpos[c] : c;
     if (u > T) {
       atomicOr(&bmap[p >> 5], 1u << (p & 31));
     } else if (u == T) {
@@ -661,8 +662,20 @@ topk_stream_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __res
     s_max = 0;
   }
   __syncthreads();
-  const uint32_t want = whole ? (uint32_t)k
-                              : (uint32_t)max<int64_t>(1, min<int64_t>(S, (13 * (int64_t)k * S + 10 * (int64_t)n - 1) / (10 * (int64_t)n)));
+  if (whole) {
+    // the whole row is in LDS: select the k-th largest key exactly (three digits), mark and write
+    // straight from this copy (region[n..) and the bitmap past 2 TS_HCAP words do not overlap)
+    for (int i = tid; i < nw; i += TS_THREADS) region[2 * TS_HCAP + i] = 0;
+    uint32_t need;   // (lds_select starts with a barrier)
+    const uint32_t T = lds_select(region, (uint32_t)n, (uint32_t)k, 31, 0, 0u, 0u, hist, &s_digit, &s_above,
+                                  &need);
+    if (!mark_and_emit(region, nullptr, (uint32_t)n, T, need, nw, region + 2 * TS_HCAP, hist, region, &s_eq,
+                       &s_digit, &s_above, &xch[1][0][0], out))
+      topk_row_exact<TS_THREADS>(row, n, k, out, hist, xch, &s_digit, &s_above);
+    return;
+  }
+  static_assert(TS_SAMPLE <= 2 * TS_HCAP, "a whole-row sample stays below the bitmap");
+  const uint32_t want = (uint32_t)max<int64_t>(1, min<int64_t>(S, (13 * (int64_t)k * S + 10 * (int64_t)n - 1) / (10 * (int64_t)n)));
   uint32_t unused;
   const uint32_t F = lds_select(region, (uint32_t)S, want, 31, 10, 0u, 0u, hist, &s_digit, &s_above, &unused);
   __syncthreads();   // every thread has F before the group arrays overwrite the sample
