@@ -54,16 +54,6 @@ __device__ __forceinline__ uint32_t float_to_ordered(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Maps a block index so that consecutive logical tiles land on the same XCD: the hardware
-// dispatches workgroup i to XCD i % 8, so logical tile = xcd * per_xcd + slot.
-__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
-  constexpr int NX = 8;
-  int per = nblocks / NX, rem = nblocks % NX;
-  int xcd = bid % NX, slot = bid / NX;
-  // the first `rem` XCDs get one extra tile
-  return (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + slot;
-}
-
 // ---------------------------------------------------------------------------- wave / block primitives
 
 __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
