@@ -138,6 +138,24 @@ __device__ __forceinline__ v16f mfma_bf16_32x32x16(const bf16x8& a, const bf16x8
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// The attention's logits product written out, so that its accumulator lives in the architectural
+// registers: the output accumulators take all 256 accumulation registers, and a logits
+// accumulator among them makes the compiler move one output tile in and out every half block.
+// The compiler's hazard tracking does not see these instructions: a chain of them accumulates in
+// place (back-to-back accumulation into the same registers needs no wait), the first one starts
+// from zero (the destination is early-clobber: it must not overlap the sources), and
+// logits_ready() supplies the wait states between the last one and any vector instruction that
+// touches the accumulator.
+__device__ __forceinline__ void logits_first(v16f& d, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void logits_acc(v16f& d, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void logits_ready(v16f& d) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(d));
+}
+
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -236,7 +254,7 @@ __device__ __forceinline__ bool attend_half(const uint8_t* buf, int kbase, uint3
   auto kop = [&](int t) -> bf16x8 {
     return *reinterpret_cast<const bf16x8*>(kb[t & 3] + (t >> 2) * 8192);
   };
-  v16f s = {};
+  v16f s;
   {
     bf16x8 ka[KRING];
 #pragma unroll
@@ -244,56 +262,49 @@ __device__ __forceinline__ bool attend_half(const uint8_t* buf, int kbase, uint3
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
       if (t + KRING - 1 < MT) ka[(t + KRING - 1) % KRING] = kop(t + KRING - 1);
-      s = mfma_bf16_32x32x16(ka[t % KRING], qreg[t], s);
+      if (t == 0) logits_first(s, ka[0], qreg[0]);
+      else logits_acc(s, ka[t % KRING], qreg[t]);
       // gather load i = t/2 of the next block (key group 2*wave + i/9, chunk group i%9) every
       // other matrix instruction
       if ((t & 1) == 0 && gdst)
         gather16<UT>(gseq, gdst, ((t / 2) / 9) * 1024 + ((t / 2) % 9) * 8192,
                      (t / 2) / 9 ? gvoff1 : gvoff0, ((t / 2) % 9) * 128);
     }
+    logits_ready(s);
   }
   // Softmax weights against the fixed reference st.m (log2 domain): p = 2^(sl2 * s - m). The
   // first half with a valid key in a pass sets the reference to its maximum; no maximum is taken
   // after that. A half whose weights in some lane sum past 2^60 (or overflow) asks for a restart
   // and records its own maximum, which the restarted pass takes as the reference.
-  const bool partial = vmask != 0xFFFFFFFFu;   // uniform: only partly valid halves pay for masking
-  const uint32_t mlane = vmask >> (4 * g);     // bit 8(i/4) + (i%4) <-> this lane's key i
-  auto key_ok = [&](int i) { return ((mlane >> (8 * (i >> 2) + (i & 3))) & 1u) != 0; };
-  auto half_max = [&]() -> float {   // masked entries are -inf by then or excluded here
+  // Masked keys first get logit -inf (weight 0, and no part in a maximum; the scale is positive),
+  // so the mask bits are only extracted for partly valid halves.
+  if (vmask != 0xFFFFFFFFu) {   // uniform
+    const uint32_t mlane = vmask >> (4 * g);   // bit 8(i/4) + (i%4) <-> this lane's key i
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (((mlane >> (8 * (i >> 2) + (i & 3))) & 1u) == 0) s[i] = -INFINITY;
+  }
+  if (st.m == -INFINITY) {
     float bm = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      if (!partial || key_ok(i)) bm = fmaxf(bm, s[i] * sl2);
-    return fmaxf(bm, __shfl_xor(bm, 32));   // both lanes of a head
-  };
-  if (st.m == -INFINITY) {
-    st.m = half_max();
+    for (int i = 0; i < 16; ++i) bm = fmaxf(bm, s[i] * sl2);
+    st.m = fmaxf(bm, __shfl_xor(bm, 32));   // both lanes of a head
     st.seen = fmaxf(st.seen, st.m);
   }
-  if (partial) {   // masked keys: exponent -inf (the scale is positive), weight 0
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      if (!key_ok(i)) s[i] = -INFINITY;
-  }
+  // The weights of the first K step of the value product (the lane's values i = 0..7) come
+  // first; those of the second K step (i = 8..15), and the lane's logit maximum that a restart
+  // needs, are computed between the first step's matrix instructions, and the overflow test
+  // follows that step: a row that restarts discards its accumulators, so the first step's
+  // products need not wait for the test.
   bf16x8 pb[2];
-  float lsum = 0.f;
+  float lsum = 0.f, smax = -INFINITY;
   const float nm = -st.m;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < 8; ++i) {
     const float p = __builtin_amdgcn_exp2f(fmaf(s[i], sl2, nm));
     lsum += p;
-    pb[i >> 3][i & 7] = (__bf16)p;
+    pb[0][i] = (__bf16)p;
   }
-  const bool over = !(lsum <= 0x1p60f);
-  if (__any(over)) {
-    const float hm = half_max();
-    st.seen = fmaxf(st.seen, hm);
-    // with finite logits an overflowing lane always has a larger maximum to restart from, and
-    // each restart raises some head's reference; NaN or infinite logits have none, and their
-    // pass goes on (its output is then not finite) instead of restarting forever
-    if (__any(over && hm > st.m)) return true;
-  }
-  st.l += lsum;
   // O^T[v, head] += V^T[v, keys] P^T[keys, head]. K step j covers keys 16j + 8h + 4g + jj
   // (h = 0, 1; jj = 0..3): the lane's P values i = 8j + 4h + jj. The V^T operand comes from two
   // transposing reads: lane (4jj + q) of each 16-lane group points at value dims
@@ -327,6 +338,26 @@ __device__ __forceinline__ bool attend_half(const uint8_t* buf, int kbase, uint3
     if (step + VRING - 1 < NSTEP) va[(step + VRING - 1) % VRING] = vop(step + VRING - 1);
     const int j = step / (MDV / 32), vt = step % (MDV / 32);
     acc_o[vt] = mfma_bf16_32x32x16(va[step % VRING], pb[j], acc_o[vt]);
+    if (step < 8) {   // second K step's weight i = 8 + step, running logit maximum
+      const float p = __builtin_amdgcn_exp2f(fmaf(s[8 + step], sl2, nm));
+      lsum += p;
+      pb[1][step] = (__bf16)p;
+      smax = fmaxf(smax, fmaxf(s[step], s[8 + step]));
+    }
+    if (step == MDV / 32 - 1) {
+      const bool over = !(lsum <= 0x1p60f);
+      if (__any(over)) {
+        // the lane's maximum of sl2 * s (sl2 > 0: the product of the maximum, NaN ignored)
+        const float lm = smax * sl2;
+        const float hm = fmaxf(lm, __shfl_xor(lm, 32));
+        st.seen = fmaxf(st.seen, hm);
+        // with finite logits an overflowing lane always has a larger maximum to restart from,
+        // and each restart raises some head's reference; NaN or infinite logits have none, and
+        // their pass goes on (its output is then not finite) instead of restarting forever
+        if (__any(over && hm > st.m)) return true;
+      }
+      st.l += lsum;
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
   return false;
