@@ -516,29 +516,73 @@ __device__ __forceinline__ float max4(float4 v) {
   return r;
 }
 
+// The bin holding the need-th largest of the counted keys (nb bins, a power of two <= 2048;
+// counts from the top bin down), found by the whole workgroup of TS_THREADS: thread t owns the run
+// of nb / TS_THREADS bins (at least one; threads past nb own none) that starts t runs below the
+// top, so the keys above a thread's run are an exclusive prefix sum in thread order: a scan within
+// each wave plus the totals of the waves before it (wsum, TS_WAVES words). The thread whose run
+// holds the need-th key walks its bins and writes *s_digit and *s_above (keys in higher bins).
+// Every thread then clears the bins it owns, so the histogram is zero again when the call
+// returns. Called by all threads; ends with a barrier.
+__device__ __forceinline__ void select_bin_block(uint32_t* hist, int nb, uint32_t need, uint32_t* wsum,
+                                                 uint32_t* s_digit, uint32_t* s_above) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int per = nb >= TS_THREADS ? nb / TS_THREADS : 1;   // 1 or 2
+  const int b_hi = nb - 1 - tid * per;                      // the run's top bin (b_hi - per < b <= b_hi)
+  uint32_t h0 = 0, h1 = 0;
+  if (b_hi >= 0) {
+    h0 = hist[b_hi];
+    if (per == 2) h1 = hist[b_hi - 1];
+  }
+  const uint32_t sum = h0 + h1;
+  const uint32_t incl = wave_incl_scan(sum);
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  // totals of the waves before this one: lane i < wave reads wave i's, one sum across the lanes
+  const uint32_t before = wave_incl_scan(lane < wave ? wsum[lane] : 0u);
+  const uint32_t above = incl - sum + (uint32_t)__builtin_amdgcn_readlane((int)before, 63);
+  if (b_hi >= 0) {
+    if (above < need && above + h0 >= need) {
+      *s_digit = (uint32_t)b_hi;
+      *s_above = above;
+    } else if (per == 2 && above + h0 < need && above + sum >= need) {
+      *s_digit = (uint32_t)(b_hi - 1);
+      *s_above = above + h0;
+    }
+    hist[b_hi] = 0;
+    if (per == 2) hist[b_hi - 1] = 0;
+  }
+  __syncthreads();
+}
+
 // Radix select over `count` keys in LDS that all share `prefix` on the bits of `pmask`: digits of
 // at most 11 bits resolve key bits hi..lo, most significant first. Returns the key prefix of the
 // want-th largest key (bits below lo zero; the key itself when lo = 0) and how many of the keys
-// with that prefix rank within the first `want` (*need_out). hist: 2048 words.
+// with that prefix rank within the first `want` (*need_out). hist: 2048 words; wsum: TS_WAVES
+// words. The histogram is cleared once; each pass's bin search leaves it zero for the next (whose
+// digit is never wider).
 __device__ __forceinline__ uint32_t lds_select(const uint32_t* keys, uint32_t count, uint32_t want,
                                                int hi, int lo, uint32_t prefix, uint32_t pmask,
-                                               uint32_t* hist, uint32_t* s_digit,
+                                               uint32_t* hist, uint32_t* wsum, uint32_t* s_digit,
                                                uint32_t* s_above, uint32_t* need_out) {
   const int tid = threadIdx.x;
   uint32_t need = want;
+  if (hi >= lo) {
+    const int nb0 = 1 << min(11, hi - lo + 1);
+    for (int i = tid; i < nb0; i += TS_THREADS) hist[i] = 0;
+    __syncthreads();
+  }
 #pragma unroll 1
   for (int top = hi; top >= lo;) {
     const int width = min(11, top - lo + 1);
     const int shift = top + 1 - width;
     const int nb = 1 << width;
-    for (int i = tid; i < nb; i += TS_THREADS) hist[i] = 0;
-    __syncthreads();
     for (uint32_t c = tid; c < count; c += TS_THREADS) {
       const uint32_t u = keys[c];
       if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & (nb - 1)], 1u);
     }
     __syncthreads();
-    select_bin(hist, nb, need, s_digit, s_above);
+    select_bin_block(hist, nb, need, wsum, s_digit, s_above);
     prefix |= *s_digit << shift;
     pmask |= (uint32_t)(nb - 1) << shift;
     need -= *s_above;
@@ -590,7 +634,7 @@ __device__ __forceinline__ bool mark_and_emit(const uint32_t* ckey, const uint32
   uint32_t cut = 0u;
   if (eqc > need) {
     uint32_t unused;
-    cut = lds_select(hist, eqc, need, 31, 0, 0u, 0u, scratch, s_digit, s_above, &unused);
+    cut = lds_select(hist, eqc, need, 31, 0, 0u, 0u, scratch, xch1, s_digit, s_above, &unused);
   }
   for (uint32_t e = tid; e < eqc; e += TS_THREADS) {
     const uint32_t ip = hist[e];
@@ -667,7 +711,7 @@ topk_stream_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __res
     // straight from this copy (region[n..) and the bitmap past 2 TS_HCAP words do not overlap)
     for (int i = tid; i < nw; i += TS_THREADS) region[2 * TS_HCAP + i] = 0;
     uint32_t need;   // (lds_select starts with a barrier)
-    const uint32_t T = lds_select(region, (uint32_t)n, (uint32_t)k, 31, 0, 0u, 0u, hist, &s_digit, &s_above,
+    const uint32_t T = lds_select(region, (uint32_t)n, (uint32_t)k, 31, 0, 0u, 0u, hist, &xch[0][0][0], &s_digit, &s_above,
                                   &need);
     if (!mark_and_emit(region, nullptr, (uint32_t)n, T, need, nw, region + 2 * TS_HCAP, hist, region, &s_eq,
                        &s_digit, &s_above, &xch[1][0][0], out))
@@ -677,7 +721,8 @@ topk_stream_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __res
   static_assert(TS_SAMPLE <= 2 * TS_HCAP, "a whole-row sample stays below the bitmap");
   const uint32_t want = (uint32_t)max<int64_t>(1, min<int64_t>(S, (13 * (int64_t)k * S + 10 * (int64_t)n - 1) / (10 * (int64_t)n)));
   uint32_t unused;
-  const uint32_t F = lds_select(region, (uint32_t)S, want, 31, 10, 0u, 0u, hist, &s_digit, &s_above, &unused);
+  const uint32_t F = lds_select(region, (uint32_t)S, want, 31, 10, 0u, 0u, hist, &xch[0][0][0], &s_digit, &s_above,
+                                &unused);
   __syncthreads();   // every thread has F before the group arrays overwrite the sample
 
   // 2. stream. Scores are compared as floats: the order-preserving key map is monotone and folds
@@ -818,8 +863,12 @@ topk_stream_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __res
   // the digits start below them
   const uint32_t M = s_max;
   const int h = (M == F) ? -1 : 31 - __clz(M ^ F);
-  const uint32_t common = h < 0 ? 0xFFFFFFFFu : ~((2u << h) - 1u);   // h = 31: no common bits
-  const uint32_t T = lds_select(ckey, total, (uint32_t)k, h, 0, F & common, common, hist, &s_digit,
+  // the bits above h (all bits for h = -1, none for h = 31), as one 64-bit shift: a select between
+  // all-ones and the 32-bit form was merged by the compiler into a test of the shifted value, which
+  // is zero for h = 31 as for h = -1, and gave all-ones for h = 31 (a floor below zero with a
+  // maximum above it)
+  const uint32_t common = (uint32_t)(~0ull << (h + 1));
+  const uint32_t T = lds_select(ckey, total, (uint32_t)k, h, 0, F & common, common, hist, &xch[0][0][0], &s_digit,
                                 &s_above, &need);
   // 6. marking and ascending output
   if (!mark_and_emit(ckey, cpos, total, T, need, nw, bmap, hist, ckey, &s_eq, &s_digit, &s_above,
@@ -903,7 +952,8 @@ topk_merge_decode_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t*
   }
   // (lds_select starts with a barrier)
   uint32_t need;
-  const uint32_t T = lds_select(ckey, total, (uint32_t)k, 31, 0, 0u, 0u, hist, &s_digit, &s_above, &need);
+  const uint32_t T = lds_select(ckey, total, (uint32_t)k, 31, 0, 0u, 0u, hist, &xch[0][0][0], &s_digit, &s_above,
+                                &need);
   if (tid < nch && (meta[4 * tid + 2] & 1u) == 0 && meta[4 * tid + 1] > T) s_bad = 1;
   __syncthreads();
   if (s_bad || !mark_and_emit(ckey, cpos, total, T, need, nw, bmap, hist, ckey, &s_eq, &s_digit, &s_above,

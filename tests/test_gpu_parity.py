@@ -521,22 +521,26 @@ def test_topk_ties_and_zeros(gpu):
 
 
 @pytest.mark.parametrize("rows,k", [(5, 2048), (600, 2048), (5, 4096)])
-@pytest.mark.parametrize("n", [5000, 30000, 131072, 140000])
+@pytest.mark.parametrize("n", [5000, 8200, 30000, 32768, 131072, 140000])
 def test_topk_row_lengths_and_degenerate_rows(gpu, n, rows, k):
     """Every top-k code path: the streaming kernel with its exact fallback (k <= 2048, rows up to
     131072, small and large batches), register-resident rows of 1, 2..8, 9..32 tiles of 4096
     (larger k), the multi-pass kernel beyond 131072 -- each with degenerate rows: all equal,
-    all +-0, one distinct value, integer ties, random floats, and a row whose largest values all
-    sit outside the sampled runs."""
+    all +-0, one distinct value, integer ties, random floats, a row whose largest values all
+    sit outside the sampled runs, and a row whose selection crosses zero."""
     rng = np.random.default_rng(n + rows)
     late = rng.standard_normal(n).astype(np.float32)
     late[n - 3000:] += 50.0   # the top scores cluster in one stretch of the row
+    # the selection crosses zero: 700 positive scores, the rest negative, so the floor of the
+    # candidate list is negative and its maximum positive (their keys differ in the top bit)
+    cross = -np.abs(rng.standard_normal(n)).astype(np.float32)
+    cross[rng.choice(n - 10, 700, replace=False)] = rng.uniform(1.0, 2.0, 700).astype(np.float32)
     pats = [np.full(n, 1.5, np.float32),
             np.where(rng.random(n) < 0.5, 0.0, -0.0).astype(np.float32),
             np.concatenate([np.full(n - 1, -2.0, np.float32), [3.0]]).astype(np.float32),
             rng.integers(-4, 5, size=n).astype(np.float32),
             rng.standard_normal(n).astype(np.float32),
-            late]
+            late, cross]
     T = max(rows, len(pats))
     sc = np.empty((T, n), np.float32)
     for r in range(T):
