@@ -244,8 +244,8 @@ def cpu_baseline(wl, x, seconds):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="chunk128k")
     ap.add_argument("--secondary", default="prefill8k,decode32k,ragged,short2k",
                     help="comma-separated extra workloads reported under 'secondary' ('' for none)")

@@ -664,6 +664,10 @@ __device__ __forceinline__ bool mark_and_emit(const uint32_t* ckey, const uint32
 // At most 64 scalar registers: with the 83 the compiler otherwise takes, the hardware placed one
 // workgroup per compute unit instead of two (measured: per-workgroup CU ids and timestamps), and
 // the 128K-chunk selection took 586 instead of 454 us.
+// PF (batches of at most one row per compute unit, where the kernel's register count no longer
+// decides its residency): the first two stream batches are requested right after the sample, so
+// their latency hides behind the floor select.
+template <bool PF>
 __global__ void __launch_bounds__(TS_THREADS) __attribute__((amdgpu_num_sgpr(64)))
 topk_stream_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
                    const float* __restrict__ scores, int64_t ld, int k, int32_t* __restrict__ idx) {
@@ -687,6 +691,23 @@ topk_stream_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __res
     return;
   }
   const int nw = (n + 31) >> 5;
+  const int n4 = n & ~3;
+  // batches of TS_UNROLL float4 per lane, double-buffered (two register sets used in turn): the
+  // next batch is in flight while the current one is scanned. Buffer loads: one resource per
+  // batch (starting at the batch, covering the whole groups left in the row) and fixed lane
+  // offsets, so no per-load address arithmetic; groups past the end read as zero (scan_batch then
+  // sets them to -inf), so every batch issues the same TS_UNROLL loads.
+  constexpr int BATCH = TS_THREADS * 4 * TS_UNROLL;
+  auto load_batch = [&](int base, float4 (&v)[TS_UNROLL]) {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(row) + base, (short)0, max(n4 - base, 0) * 4, 0x00020000);
+#pragma unroll
+    for (int u = 0; u < TS_UNROLL; ++u) {
+      const auto t = __builtin_amdgcn_raw_buffer_load_b128(rs, (u * TS_THREADS + tid) * 16, 0, 0);
+      v[u] = make_float4(__uint_as_float(t[0]), __uint_as_float(t[1]), __uint_as_float(t[2]), __uint_as_float(t[3]));
+    }
+  };
+  float4 va[TS_UNROLL], vb[TS_UNROLL];
 
   // 1. sample and floor
   const bool whole = n <= TS_SAMPLE;
@@ -697,10 +718,26 @@ topk_stream_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __res
   if (whole) {
     for (int i = tid; i < n; i += TS_THREADS) region[i] = float_to_ordered(row[i]);
   } else {
-    for (int i = tid; i < S; i += TS_THREADS) {
-      const int j = i / seg, o = i - j * seg;
-      const int start = (int)((int64_t)j * (n - seg) / (TS_SEGS - 1));
-      region[i] = float_to_ordered(row[start + o]);
+    // every sample load is issued before the first one is used; the PF batches after them, so
+    // the sample arrives first and the batches stream in during the floor select
+    float sv[TS_SAMPLE / TS_THREADS];
+#pragma unroll
+    for (int u = 0; u < TS_SAMPLE / TS_THREADS; ++u) {
+      const int i = tid + u * TS_THREADS;
+      if (i < S) {
+        const int j = i / seg, o = i - j * seg;
+        const int start = (int)((int64_t)j * (n - seg) / (TS_SEGS - 1));
+        sv[u] = row[start + o];
+      }
+    }
+    if constexpr (PF) {
+      load_batch(0, va);
+      load_batch(BATCH, vb);
+    }
+#pragma unroll
+    for (int u = 0; u < TS_SAMPLE / TS_THREADS; ++u) {
+      const int i = tid + u * TS_THREADS;
+      if (i < S) region[i] = float_to_ordered(sv[u]);
     }
   }
   if (tid == 0) {
@@ -731,7 +768,6 @@ topk_stream_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __res
   // 2. stream. Scores are compared as floats: the order-preserving key map is monotone and folds
   // -0 onto +0, which the float comparison treats as equal too.
   const float Ff = __uint_as_float((F & 0x80000000u) ? (F & 0x7FFFFFFFu) : ~F);
-  const int n4 = n & ~3;
   // group arrays; a lane's slot address is its word index * 4, the arrays follow at multiples of
   // TS_GSTRIDE words
   const uint32_t spare4 = 4u * (uint32_t)(TS_GCAP + lane);
@@ -742,21 +778,6 @@ topk_stream_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __res
     a[2 * TS_GSTRIDE] = __float_as_uint(v.z);
     a[3 * TS_GSTRIDE] = __float_as_uint(v.w);
     a[4 * TS_GSTRIDE] = p;
-  };
-  // batches of TS_UNROLL float4 per lane, double-buffered (two register sets used in turn): the
-  // next batch is in flight while the current one is scanned. Buffer loads: one resource per
-  // batch (starting at the batch, covering the whole groups left in the row) and fixed lane
-  // offsets, so no per-load address arithmetic; groups past the end read as zero (scan_batch then
-  // sets them to -inf), so every batch issues the same TS_UNROLL loads.
-  constexpr int BATCH = TS_THREADS * 4 * TS_UNROLL;
-  auto load_batch = [&](int base, float4 (&v)[TS_UNROLL]) {
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float*>(row) + base, (short)0, max(n4 - base, 0) * 4, 0x00020000);
-#pragma unroll
-    for (int u = 0; u < TS_UNROLL; ++u) {
-      const auto t = __builtin_amdgcn_raw_buffer_load_b128(rs, (u * TS_THREADS + tid) * 16, 0, 0);
-      v[u] = make_float4(__uint_as_float(t[0]), __uint_as_float(t[1]), __uint_as_float(t[2]), __uint_as_float(t[3]));
-    }
   };
   auto scan_batch = [&](int base, float4 (&v)[TS_UNROLL]) {
     if (base + BATCH > n4) {   // uniform: the partial batch
@@ -790,10 +811,9 @@ topk_stream_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __res
   };
   const int nb = (n4 + BATCH - 1) / BATCH;
   if (nb > 0) {   // n4 >= 4
-    float4 va[TS_UNROLL], vb[TS_UNROLL];
-    load_batch(0, va);
+    if constexpr (!PF) load_batch(0, va);
     for (int j = 0;;) {
-      load_batch((j + 1) * BATCH, vb);
+      if (!PF || j > 0) load_batch((j + 1) * BATCH, vb);   // (PF: batch 1 is already in flight)
       scan_batch(j * BATCH, va);
       if (++j >= nb) break;
       load_batch((j + 1) * BATCH, va);
@@ -983,8 +1003,14 @@ hipError_t launch_topk(const SeqInfo& s, const float* scores, int64_t ld, int k,
   // alike (it also finishes a lone row sooner than the register-resident kernel); the others for
   // larger k and longer rows
   if (k <= TS_MAXK && s.max_n <= TS_MAXN)
-    hipLaunchKernelGGL(topk_stream_kernel, grid, dim3(TS_THREADS), 0, st, s.B, s.cu_q, s.cu_k, scores, ld,
-                       k, idx);
+  {
+    if (s.T <= kTargetCUs)
+      hipLaunchKernelGGL(topk_stream_kernel<true>, grid, dim3(TS_THREADS), 0, st, s.B, s.cu_q, s.cu_k, scores,
+                         ld, k, idx);
+    else
+      hipLaunchKernelGGL(topk_stream_kernel<false>, grid, dim3(TS_THREADS), 0, st, s.B, s.cu_q, s.cu_k, scores,
+                         ld, k, idx);
+  }
   else if (tiles <= 2)
     hipLaunchKernelGGL(topk_reg_kernel<2>, grid, block, 0, st, s.B, s.cu_q, s.cu_k, scores, ld, k, idx);
   else if (tiles <= 8)
