@@ -616,11 +616,12 @@ indexer_fp8_decode_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, c = lane & 15;
   const int b = blockIdx.y, chunk = blockIdx.x;
-  const int r = cu_q[b];
-  if (cu_q[b + 1] == r) return;                    // a sequence without a query row
+  // all four offsets are requested before either test, so that a workgroup past its row's end
+  // (half of a ragged batch's grid) leaves after one memory round trip
+  const int r = cu_q[b], r1 = cu_q[b + 1];
   const int k0 = cu_k[b], n = cu_k[b + 1] - k0;    // the row sits at position n - 1
   const int kbeg = chunk * kDecodeChunk;
-  if (kbeg >= n) return;                           // uniform over the workgroup
+  if (r1 == r || kbeg >= n) return;                // no query row, or a chunk past the row's end
   const int cnt = min(kDecodeChunk, n - kbeg);
   const int nblk = (cnt + 15) >> 4;
   const int nmine = nblk > wave ? (nblk - wave + DK_W - 1) / DK_W : 0;
