@@ -444,11 +444,15 @@ attn_bf16_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restr
   const int g = lane >> 5, c32 = lane & 31;
   const RowLoc L = locate_row(cu_q, cu_k, B, r);
   const int split = blockIdx.y, nsplit = gridDim.y;
-  const int nblk_row = (k + MBLK - 1) / MBLK;
+  // entries that can be valid: all k of an index list; without one, entry e is candidate e and
+  // only e <= pos exist, so the row's blocks end at its position (a short row of a dense batch
+  // would otherwise pass through k / 64 blocks, most of them empty)
+  const int kr = idx ? k : max(0, min(k, L.pos + 1));
+  const int nblk_row = (kr + MBLK - 1) / MBLK;
   const int b0 = split * nblk_row / nsplit, b1 = (split + 1) * nblk_row / nsplit;
   // this split's entries; without an index list, entry e of the row is candidate e (e <= pos)
   const int32_t* ir = idx ? idx + (int64_t)r * k + b0 * MBLK : nullptr;
-  const int kk = min(k - b0 * MBLK, (b1 - b0) * MBLK);
+  const int kk = min(kr - b0 * MBLK, (b1 - b0) * MBLK);
   const int nblk = b1 - b0;
 
   // lane l's key of block blk is entry blk*64 + l of the index row
@@ -529,10 +533,11 @@ attn_bf16_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restr
       ++step;
       vm_cur = vm_next;
     }
-    // a request made during the last step is visible after one more barrier
+    // a request made during the last step is visible after one more barrier (a split without a
+    // block, step 0, has made none: the flags' initial -1 must not read as step -1's request)
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (!restart && s_flag[(step - 1) & 1] == step - 1) restart = true;
+    if (!restart && step > 0 && s_flag[(step - 1) & 1] == step - 1) restart = true;
     if (!restart) break;
     // restart: gather the first block again
     prep(load_idx(0), ra, rb, vm_cur);
