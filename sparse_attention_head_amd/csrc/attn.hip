@@ -431,7 +431,7 @@ attn_bf16_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restr
                  const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv,
                  const int32_t* __restrict__ idx, int k, float scale, uint16_t* __restrict__ out,
                  float* __restrict__ lse, int T, uint16_t* __restrict__ part_o,
-                 float* __restrict__ part_lse) {
+                 float* __restrict__ part_lse, int prefix_rows) {
   __shared__ __attribute__((aligned(1024))) uint8_t buf0[MBUF];
   __shared__ __attribute__((aligned(1024))) uint8_t buf1[MBUF];
   // restart requests: slot (step & 1) holds the id of the last step that asked for one
@@ -444,14 +444,16 @@ attn_bf16_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restr
   const int g = lane >> 5, c32 = lane & 31;
   const RowLoc L = locate_row(cu_q, cu_k, B, r);
   const int split = blockIdx.y, nsplit = gridDim.y;
-  // entries that can be valid: all k of an index list; without one, entry e is candidate e and
-  // only e <= pos exist, so the row's blocks end at its position (a short row of a dense batch
-  // would otherwise pass through k / 64 blocks, most of them empty)
-  const int kr = idx ? k : max(0, min(k, L.pos + 1));
+  // Without an index list, entry e of a row is candidate e (e <= pos). With prefix_rows, a row
+  // whose causal candidates all fit in k holds the list 0..pos, -1, ... (the selection of such a
+  // row is every candidate, in ascending order) and is walked the same way. Such a row's blocks
+  // end at its position; with an arbitrary list all k entries can be valid.
+  const bool implicit = !idx || (prefix_rows && L.pos + 1 <= k);
+  const int kr = implicit ? max(0, min(k, L.pos + 1)) : k;
   const int nblk_row = (kr + MBLK - 1) / MBLK;
   const int b0 = split * nblk_row / nsplit, b1 = (split + 1) * nblk_row / nsplit;
-  // this split's entries; without an index list, entry e of the row is candidate e (e <= pos)
-  const int32_t* ir = idx ? idx + (int64_t)r * k + b0 * MBLK : nullptr;
+  // this split's entries
+  const int32_t* ir = implicit ? nullptr : idx + (int64_t)r * k + b0 * MBLK;
   const int kk = min(kr - b0 * MBLK, (b1 - b0) * MBLK);
   const int nblk = b1 - b0;
 
@@ -867,7 +869,7 @@ size_t attn_workspace_bytes(const SeqInfo& s, int, int, int, int k, bool bf16) {
 
 hipError_t launch_attn_bf16(const SeqInfo& s, const uint16_t* q, const uint16_t* kv,
                             const int32_t* idx, int k, float scale, uint16_t* out, float* lse,
-                            void* ws, size_t, hipStream_t st) {
+                            void* ws, size_t, bool prefix_rows, hipStream_t st) {
   if (s.T == 0) return hipSuccess;
   const int ns = attn_splits(s, k);
   uint16_t* part_o = ns > 1 ? static_cast<uint16_t*>(ws) : nullptr;
@@ -875,11 +877,11 @@ hipError_t launch_attn_bf16(const SeqInfo& s, const uint16_t* q, const uint16_t*
   if (ns > 1)
     hipLaunchKernelGGL(attn_bf16_kernel<true>, dim3(s.T, ns), dim3(256), 0, st, s.B, s.cu_q, s.cu_k, q,
                        reinterpret_cast<const uint8_t*>(kv), idx, k, scale, out, lse, s.T, part_o,
-                       part_lse);
+                       part_lse, prefix_rows ? 1 : 0);
   else
     hipLaunchKernelGGL(attn_bf16_kernel<false>, dim3(s.T, ns), dim3(256), 0, st, s.B, s.cu_q, s.cu_k, q,
                        reinterpret_cast<const uint8_t*>(kv), idx, k, scale, out, lse, s.T, part_o,
-                       part_lse);
+                       part_lse, prefix_rows ? 1 : 0);
   if (ns > 1)
     hipLaunchKernelGGL(attn_combine_kernel, dim3((s.T * MH + 3) / 4), dim3(256), 0, st, s.T, ns,
                        part_o, part_lse, out, lse);

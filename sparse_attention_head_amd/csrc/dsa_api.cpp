@@ -183,9 +183,11 @@ dsa_status_t run_indexer(const dsa::SeqInfo& s, int32_t H_I, int32_t d_I, dsa_dt
   return hip_status(e, "indexer launch");
 }
 
+// prefix_rows: idx was written by this library's top-k in the same call (see launch_attn_bf16).
 dsa_status_t run_attn(const dsa::SeqInfo& s, int32_t H, int32_t d_qk, int32_t d_v, dsa_dtype_t dt,
                       const void* q, const void* kv, const int32_t* idx, int32_t k, float scale,
-                      void* out, float* lse, void* ws, size_t ws_bytes, hipStream_t st) {
+                      void* out, float* lse, void* ws, size_t ws_bytes, hipStream_t st,
+                      bool prefix_rows = false) {
   if (s.T == 0) return ok();
   hipError_t e;
   if (dt == DSA_F32)
@@ -194,7 +196,8 @@ dsa_status_t run_attn(const dsa::SeqInfo& s, int32_t H, int32_t d_qk, int32_t d_
                              static_cast<float*>(out), lse, st);
   else
     e = dsa::launch_attn_bf16(s, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kv),
-                              idx, k, scale, static_cast<uint16_t*>(out), lse, ws, ws_bytes, st);
+                              idx, k, scale, static_cast<uint16_t*>(out), lse, ws, ws_bytes, prefix_rows,
+                              st);
   return hip_status(e, "attention launch");
 }
 
@@ -473,7 +476,7 @@ dsa_status_t dsa_forward(const dsa_seqs_t* seqs, const dsa_forward_args_t* a, vo
   }
   return run_attn(s, a->H, a->d_qk, a->d_v, a->dtype, a->q, a->kv, p.implicit_idx ? nullptr : idx,
                   a->k, a->softmax_scale, a->out, a->lse, p.attn_bytes ? base + p.attn_off : nullptr,
-                  p.attn_bytes, hs);
+                  p.attn_bytes, hs, p.run_topk);
 }
 
 dsa_status_t dsa_forward_noalloc(const dsa_seqs_t* seqs, const dsa_forward_args_t* args, void* stream) {

@@ -90,9 +90,11 @@ size_t attn_workspace_bytes(const SeqInfo& s, int H, int d_qk, int d_v, int k, b
 hipError_t launch_attn_f32(const SeqInfo& s, int H, int d_qk, int d_v, const float* q,
                            const float* kv, const int32_t* idx, int k, float scale, float* out,
                            float* lse, hipStream_t st);
+// prefix_rows: idx comes from this library's top-k, so a row whose causal candidates all fit in k
+// holds 0..pos then -1 (the attention then stops at the row's last block).
 hipError_t launch_attn_bf16(const SeqInfo& s, const uint16_t* q, const uint16_t* kv,
                             const int32_t* idx, int k, float scale, uint16_t* out, float* lse,
-                            void* ws, size_t ws_bytes, hipStream_t st);
+                            void* ws, size_t ws_bytes, bool prefix_rows, hipStream_t st);
 
 // Indexer-alignment target p [T, k] (or NULL) and KL [T] for the bf16 (128, 576) shapes.
 hipError_t launch_align_bf16(const SeqInfo& s, const uint16_t* q, const uint16_t* kv,
