@@ -281,13 +281,12 @@ struct PipeState {
   int lsc;              // E8M0 column scale of the linear tile
   bool hi2, hi1;
   float* sp;            // this lane's first score of the stage
-  const float* ks;      // this lane's first key scale of the stage (LDS; scaled kernel only)
   v8i key[2];
   v4f d[4];
   float acc[4], red[4], n0, n1, kk, ss;
 };
 
-template <int NB, int T, bool KS>
+template <int NB, int T>
 __device__ __forceinline__ void pipe_step(PipeState& P) {
   constexpr int NM = 17, LAG = 3, TOT = NB * NM;
   if constexpr (T < TOT) {
@@ -333,21 +332,18 @@ __device__ __forceinline__ void pipe_step(PipeState& P) {
   }
   if constexpr (f >= 3 && (f - 3) % NM == 0 && (f - 3) / NM < NB) {
     constexpr int blk = (f - 3) / NM;
-    float v = P.kk + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(P.ss), 0xB1, 0xF, 0xF, true));
-    if constexpr (KS) v *= P.ks[blk * 16];
-    P.sp[blk * 16] = v;
+    P.sp[blk * 16] = P.kk + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(P.ss), 0xB1, 0xF, 0xF, true));
   }
   __builtin_amdgcn_sched_barrier(0);
-  if constexpr (T + 1 < TOT + LAG + 3) pipe_step<NB, T + 1, KS>(P);
+  if constexpr (T + 1 < TOT + LAG + 3) pipe_step<NB, T + 1>(P);
 }
 
-template <int NB, bool KS>
+template <int NB>
 __device__ __forceinline__ void stage_pipeline(const uint8_t* __restrict__ buf, int kb0, int kb1,
                                                const v8i (&qa)[16], const v8i& ql,
                                                const float (&wt)[16], int lsc, bool hi2, bool hi1,
-                                               float* __restrict__ sp, const float* ks) {
+                                               float* __restrict__ sp) {
   PipeState P;
-  P.ks = ks;
   P.buf = buf;
   P.kb0 = kb0;
   P.kb1 = kb1;
@@ -363,7 +359,7 @@ __device__ __forceinline__ void stage_pipeline(const uint8_t* __restrict__ buf, 
     const v4i hi = *reinterpret_cast<const v4i*>(buf + kb1);
     P.key[0] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   }
-  pipe_step<NB, 0, KS>(P);
+  pipe_step<NB, 0>(P);
 }
 
 // Workgroup = 8 waves x 4 rows = 32 query rows of one sequence against a chunk of keys. The keys
@@ -379,11 +375,12 @@ constexpr int PF_RW = 4;                // rows per wave
 constexpr int PF_ROWS = PF_W * PF_RW;   // 32
 constexpr int PF_SK = 256;              // keys per stage
 constexpr int PF_NR = 3;                // stages in the ring
-constexpr int PF_KC_MAX = 8192;         // keys per workgroup (chunk) at most with key scales (twice that without)
+constexpr int PF_KC_MAX = 16384;        // keys per workgroup (chunk) at most
 constexpr int PF_STW = PF_SK + 16;      // words per staged score row
 
-// KS: every score is multiplied by the per-key scale kscale[key row] (positive); the chunk's
-// scales sit in LDS (32 KB more).
+// KS: every score is multiplied by the per-key scale kscale[key row] (positive), as a stage's
+// staged rows leave (each lane's four keys share one 16-byte load of scales, requested before the
+// stage's pipeline).
 template <bool KS>
 __global__ void __launch_bounds__(PF_W * 64, 1)
 indexer_fp8_prefill_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
@@ -392,11 +389,10 @@ indexer_fp8_prefill_kernel(int B, const int32_t* __restrict__ cu_q, const int32_
                            const int32_t* __restrict__ piece_exp, const float* __restrict__ kscale,
                            float* __restrict__ scores, int64_t ld, int KC) {
   __shared__ __attribute__((aligned(1024))) uint8_t kst[PF_NR][PF_SK * kDI];
-  __shared__ float ksc[KS ? PF_KC_MAX : 1];
-  // unscaled kernel: each wave's 4 rows x 256 scores of a whole stage collect here (rows padded to
-  // PF_STW words: the pipeline's writes and the row reads are free of bank conflicts) and leave as
-  // four 1 KB row stores, so that every 128-byte line of a score row is written whole at once
-  __shared__ __attribute__((aligned(16))) float stw[KS ? 1 : PF_W * PF_RW * PF_STW];
+  // each wave's 4 rows x 256 scores of a whole stage collect here (rows padded to PF_STW words:
+  // the pipeline's writes and the row reads are free of bank conflicts) and leave as four 1 KB row
+  // stores, so that every 128-byte line of a score row is written whole at once
+  __shared__ __attribute__((aligned(16))) float stw[PF_W * PF_RW * PF_STW];
   constexpr int HPM = 4, NMF = 16;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
@@ -420,10 +416,6 @@ indexer_fp8_prefill_kernel(int B, const int32_t* __restrict__ cu_q, const int32_
   // DMA of stage st: 32 instructions of 1 KB (8 keys each), 4 per wave; lane l of instruction i
   // covers key (i*8 + l/8) of the stage, whose 16 mod 16 is 8*(i%2) + l/8, and writes physical
   // chunk l%8, i.e. logical chunk (l%8) ^ key_swz(key % 16).
-  if (KS) {   // the chunk's key scales, before any DMA (the first stage wait is vmcnt(0))
-    for (int i = threadIdx.x; i < kend - kbeg; i += PF_W * 64) ksc[i] = kscale[k0 + kbeg + i];
-    __syncthreads();
-  }
   const int dch0 = ((lane & 7) ^ key_swz(lane >> 3)) * 16;
   const int dch1 = ((lane & 7) ^ key_swz(8 | (lane >> 3))) * 16;
   auto issue = [&](int st) {
@@ -479,49 +471,46 @@ indexer_fp8_prefill_kernel(int B, const int32_t* __restrict__ cu_q, const int32_
   };
 
   // Vector memory operations complete in issue order, so the wait for stage st's DMA may leave
-  // the operations issued after it in flight: the score stores of a whole stage (4 row stores
-  // per wave, 16 direct stores in the scaled kernel), the next stage's DMA (4), the stores of the
-  // stage after. `fast1`/`fast2`: stage st-1 / st-2 ran the whole-stage path, whose stores are
-  // certain (other stages count as 0).
-  constexpr int SPS = KS ? 16 : PF_RW;   // stores per whole stage and wave
-  float* const stw_wave = stw + (KS ? 0 : wave * PF_RW * PF_STW);
+  // the operations issued after it in flight: a whole stage's 4 row stores per wave (and, in the
+  // scaled kernel, its scale load, issued before the DMA of stage st+2), the next stage's DMA (4),
+  // the stores of the stage after. `fast1`/`fast2`: stage st-1 / st-2 ran the whole-stage path,
+  // whose operations are certain (other stages count as 0).
+  float* const stw_wave = stw + wave * PF_RW * PF_STW;
   bool fast1 = false, fast2 = false;
   for (int st = 0; st < nst; ++st) {
-    const int after = (st == 0) ? 0 : SPS * fast2 + SPS * fast1 + 4 * (st + 1 < nst);
+    const int after = (st == 0) ? 0 : PF_RW * fast2 + (PF_RW + (KS ? 1 : 0)) * fast1 + 4 * (st + 1 < nst);
     switch (after) {
-      case 36: asm volatile("s_waitcnt vmcnt(36)" ::: "memory"); break;
-      case 32: asm volatile("s_waitcnt vmcnt(32)" ::: "memory"); break;
-      case 20: asm volatile("s_waitcnt vmcnt(20)" ::: "memory"); break;
-      case 16: asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); break;
+      case 13: asm volatile("s_waitcnt vmcnt(13)" ::: "memory"); break;
       case 12: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
+      case 9: asm volatile("s_waitcnt vmcnt(9)" ::: "memory"); break;
       case 8: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+      case 5: asm volatile("s_waitcnt vmcnt(5)" ::: "memory"); break;
       case 4: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
       default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
     }
     // stage st landed in every wave's part; every wave is done with the buffer the next DMA
     // refills (its reads were consumed by its matrix instructions)
     __builtin_amdgcn_s_barrier();
-    if (st + PF_NR - 1 < nst) issue(st + PF_NR - 1);
-    const uint8_t* buf = kst[st % PF_NR];
     const int sbase = kbeg + st * PF_SK;
     const bool fast = all_rows && sbase + PF_SK <= wkend;
+    // the scales of this lane's four keys of the stage (a whole stage lies inside the row)
+    float4 sc4 = make_float4(1.f, 1.f, 1.f, 1.f);
+    if (KS && fast) sc4 = *reinterpret_cast<const float4*>(kscale + k0 + sbase + 4 * lane);
+    if (st + PF_NR - 1 < nst) issue(st + PF_NR - 1);
+    const uint8_t* buf = kst[st % PF_NR];
     fast2 = fast1;
     fast1 = fast;
     if (fast) {
       // whole stage for 4 valid rows: every score lands below wkend <= n <= ld (keys past a row's
       // own position fall in the part of the row the interface leaves unspecified)
-      if constexpr (KS) {
-        stage_pipeline<PF_SK / 16, KS>(buf + c * kDI, bx0, bx1, a, al, wt, lsc, hi2, hi1,
-                                       srow + sbase + kofs, ksc + (sbase - kbeg) + kofs);
-      } else {
-        stage_pipeline<PF_SK / 16, KS>(buf + c * kDI, bx0, bx1, a, al, wt, lsc, hi2, hi1,
-                                       stw_wave + (c >> 2) * PF_STW + kofs, nullptr);
-        // (one wave writes and reads its own rows: its LDS operations complete in order)
+      stage_pipeline<PF_SK / 16>(buf + c * kDI, bx0, bx1, a, al, wt, lsc, hi2, hi1,
+                                 stw_wave + (c >> 2) * PF_STW + kofs);
+      // (one wave writes and reads its own rows: its LDS operations complete in order)
 #pragma unroll
-        for (int rr = 0; rr < PF_RW; ++rr) {
-          const float4 v = *reinterpret_cast<const float4*>(stw_wave + rr * PF_STW + 4 * lane);
-          *reinterpret_cast<float4*>(scores + (int64_t)(q0 + wrow0 + rr) * ld + sbase + 4 * lane) = v;
-        }
+      for (int rr = 0; rr < PF_RW; ++rr) {
+        float4 v = *reinterpret_cast<const float4*>(stw_wave + rr * PF_STW + 4 * lane);
+        if constexpr (KS) v = make_float4(v.x * sc4.x, v.y * sc4.y, v.z * sc4.z, v.w * sc4.w);
+        *reinterpret_cast<float4*>(scores + (int64_t)(q0 + wrow0 + rr) * ld + sbase + 4 * lane) = v;
       }
     } else {
       const int nblk = min(PF_SK, wkend - sbase) > 0 ? (min(PF_SK, wkend - sbase) + 15) / 16 : 0;
@@ -529,7 +518,7 @@ indexer_fp8_prefill_kernel(int B, const int32_t* __restrict__ cu_q, const int32_
         float acc = score_block_t(a, al, load_b(buf, blk * 16), wt, lsc, hi2, hi1);
         asm volatile("" ::"v"(acc));
         const int s = sbase + blk * 16 + kofs;
-        if (KS) acc *= ksc[min(s - kbeg, KC - 1)];
+        if (KS) acc *= kscale[k0 + min(s, n - 1)];
         if (row_ok && s <= my_pos && s < wkend) srow[s] = acc;
       }
     }
@@ -560,7 +549,7 @@ hipError_t launch_indexer_fp8_prefill(const SeqInfo& s, const uint8_t* q, const 
   hipLaunchKernelGGL(indexer_fp8_linear_kernel, dim3((s.T + 3) / 4), dim3(256), 0, st, s.T, q, w,
                      pieces, piece_exp);
   const int tiles = (s.max_m + PF_ROWS - 1) / PF_ROWS;
-  const int kc = pick_chunk((int64_t)tiles * s.B, s.max_n, kTargetCUs, PF_SK, kscale ? PF_KC_MAX : 2 * PF_KC_MAX);
+  const int kc = pick_chunk((int64_t)tiles * s.B, s.max_n, kTargetCUs, PF_SK, PF_KC_MAX);
   dim3 grid(tiles, (s.max_n + kc - 1) / kc, s.B);
   if (kscale)
     hipLaunchKernelGGL(indexer_fp8_prefill_kernel<true>, grid, dim3(PF_W * 64), 0, st, s.B, s.cu_q,
