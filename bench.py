@@ -77,8 +77,11 @@ def algorithmic(wl):
     # decode-style HBM bytes: indexer keys + gathered latent rows + per-query vectors
     vec_bytes = T * (wl.H_I * wl.d_I * 1 + wl.H_I * 4 + wl.H * wl.d_qk * 2 + wl.H * wl.d_v * 2 + wl.H * 4)
     dec_bytes = float(sum(wl.seqlens_k)) * wl.d_I + sel * wl.d_qk * 2.0 + vec_bytes
+    # latent rows the attention and the alignment target gather: one d_qk-dim bf16 row per
+    # selected entry (their other roofline besides the matrix core)
+    gather_bytes = sel * wl.d_qk * 2.0
     return dict(pairs=pairs, selected=sel, indexer_flop=idx_flop, attn_flop=attn_flop,
-                topk_bytes=topk_bytes, decode_bytes=dec_bytes)
+                topk_bytes=topk_bytes, decode_bytes=dec_bytes, gather_bytes=gather_bytes)
 
 
 def to_dev(torch, a):
@@ -189,6 +192,12 @@ def measure(torch, dsa, timer, wl, T, seqs, steps, warmup, scales=None, fused_on
     return res
 
 
+def gather_rate(alg, t):
+    """The gathered latent rows per second of a stage, against the HBM peak."""
+    gbs = alg["gather_bytes"] / (t["median"] / 1e3) / 1e9
+    return {"gather_gbs": gbs, "gather_frac_hbm": gbs / PEAK_HBM_GBS}
+
+
 def stage_report(wl, tm):
     """Per-stage rates against the MI355X peaks (median times; min-time rates alongside)."""
     alg = algorithmic(wl)
@@ -203,6 +212,7 @@ def stage_report(wl, tm):
         out["indexer"] = rate(alg["indexer_flop"], tm["indexer"], PEAK_FP8_TFLOPS, "tflops", "frac_fp8")
         out["topk"] = rate(alg["topk_bytes"], tm["topk"], PEAK_HBM_GBS, "gbs", "frac_hbm")
         out["attention"] = rate(alg["attn_flop"], tm["attention"], PEAK_BF16_TFLOPS, "tflops", "frac_bf16")
+        out["attention"].update(gather_rate(alg, tm["attention"]))
     if "indexer_topk" in tm:   # one call for both steps; against the two calls' medians
         sep = tm["indexer"]["median"] + tm["topk"]["median"]
         out["indexer_topk"] = {"ms": tm["indexer_topk"]["median"], "ms_min": tm["indexer_topk"]["min"],
@@ -211,6 +221,7 @@ def stage_report(wl, tm):
     if "alignment" in tm:   # logits of every selected entry again: 2 H d_qk flop each
         out["alignment"] = rate(2.0 * wl.H * wl.d_qk * alg["selected"], tm["alignment"], PEAK_BF16_TFLOPS,
                                 "tflops", "frac_bf16")
+        out["alignment"].update(gather_rate(alg, tm["alignment"]))
     if "indexer_scaled" in tm:
         out["indexer_scaled"] = rate(alg["indexer_flop"], tm["indexer_scaled"], PEAK_FP8_TFLOPS, "tflops",
                                      "frac_fp8")
