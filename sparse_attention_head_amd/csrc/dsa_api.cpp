@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cstdarg>
 #include <cstdio>
@@ -212,10 +213,12 @@ struct ForwardPlan {
   size_t total;
 };
 
+// Row stride of the scores the fused call keeps in its workspace: max_seqlen_k rounded up to 4.
+int64_t default_ld(const dsa::SeqInfo& s) { return std::max<int64_t>(4, ((int64_t)s.max_n + 3) / 4 * 4); }
+
 ForwardPlan plan_forward(const dsa::SeqInfo& s, const dsa_forward_args_t* a) {
   ForwardPlan p{};
-  p.ld = ((int64_t)s.max_n + 3) / 4 * 4;
-  if (p.ld == 0) p.ld = 4;
+  p.ld = default_ld(s);
   // Short contexts: with at most k keys per sequence every row selects all its candidates, so
   // the scores are only computed when the caller asks for them, and the bf16 attention walks the
   // candidates without an index list (top-k only runs to fill indices_out, or for the fp32 path).
@@ -243,6 +246,22 @@ ForwardPlan plan_forward(const dsa::SeqInfo& s, const dsa_forward_args_t* a) {
   off += p.attn_bytes;
   p.total = off;
   return p;
+}
+
+// Argument checks of the fused call, before any workspace planning (the plan's sizes assume them).
+dsa_status_t check_forward(const dsa::SeqInfo& s, const dsa_forward_args_t* a) {
+  const int64_t ld = a->scores_out ? a->ld_scores_out : default_ld(s);
+  dsa_status_t st = check_indexer(s, a->H_I, a->d_I, a->qk_dtype, a->q_idx, a->k_idx, a->w, a->scores_out,
+                                  ld, a->scores_out == nullptr);
+  if (st != DSA_OK) return st;
+  st = check_attn(s, a->H, a->d_qk, a->d_v, a->dtype, a->q, a->kv, a->indices_out, a->k, a->out,
+                  a->lse, a->indices_out == nullptr);
+  if (st != DSA_OK) return st;
+  if (!(a->softmax_scale > 0.f) || a->softmax_scale > 3.0e38f)
+    return fail(DSA_ERR_SHAPE, "softmax_scale must be positive and finite (got %g)", a->softmax_scale);
+  if ((a->q_idx_scale && !aligned16(a->q_idx_scale)) || (a->k_idx_scale && !aligned16(a->k_idx_scale)))
+    return fail(DSA_ERR_ALIGN, "scale arrays must be 16-byte aligned");
+  return ok();
 }
 
 // ---------------------------------------------------------------- scratch of dsa_forward_noalloc
@@ -439,18 +458,10 @@ dsa_status_t dsa_forward(const dsa_seqs_t* seqs, const dsa_forward_args_t* a, vo
   if (st != DSA_OK) return st;
   if (!a) return fail(DSA_ERR_NULL, "args is NULL");
   if (s.B == 0) return ok();
+  st = check_forward(s, a);
+  if (st != DSA_OK) return st;
   const ForwardPlan p = plan_forward(s, a);
   const int64_t ld = a->scores_out ? a->ld_scores_out : p.ld;
-  st = check_indexer(s, a->H_I, a->d_I, a->qk_dtype, a->q_idx, a->k_idx, a->w, a->scores_out,
-                     ld, a->scores_out == nullptr);
-  if (st != DSA_OK) return st;
-  st = check_attn(s, a->H, a->d_qk, a->d_v, a->dtype, a->q, a->kv, a->indices_out, a->k, a->out,
-                  a->lse, a->indices_out == nullptr);
-  if (st != DSA_OK) return st;
-  if (!(a->softmax_scale > 0.f) || a->softmax_scale > 3.0e38f)
-    return fail(DSA_ERR_SHAPE, "softmax_scale must be positive and finite (got %g)", a->softmax_scale);
-  if ((a->q_idx_scale && !aligned16(a->q_idx_scale)) || (a->k_idx_scale && !aligned16(a->k_idx_scale)))
-    return fail(DSA_ERR_ALIGN, "scale arrays must be 16-byte aligned");
   if (p.total > 0 && (!ws || ws_bytes < p.total))
     return fail(DSA_ERR_WORKSPACE, "forward workspace needs %zu bytes, got %zu", p.total, ws_bytes);
   if (ws && (reinterpret_cast<uintptr_t>(ws) % kAlign) != 0)
@@ -485,6 +496,8 @@ dsa_status_t dsa_forward_noalloc(const dsa_seqs_t* seqs, const dsa_forward_args_
   if (st != DSA_OK) return st;
   if (!args) return fail(DSA_ERR_NULL, "args is NULL");
   if (s.B == 0) return ok();
+  st = check_forward(s, args);
+  if (st != DSA_OK) return st;
   const size_t need = plan_forward(s, args).total;
   if (need > DSA_NOALLOC_SCRATCH_BYTES)
     return fail(DSA_ERR_WORKSPACE, "dsa_forward_noalloc: this batch needs %zu bytes of workspace, more than "

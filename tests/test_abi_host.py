@@ -327,3 +327,31 @@ def test_noalloc_forward_rejects_oversized_batches_without_a_device(dsa):
     assert dsa._c_fwd_na(sq.ref, None, None) == dsa.DSA_ERR_NULL
     empty = FakeSeqs(dsa, [0], [0], max_m=0, max_n=0)
     assert dsa._c_fwd_na(empty.ref, ctypes.byref(a), None) == dsa.DSA_OK
+
+
+def test_noalloc_forward_checks_arguments_before_sizing(dsa):
+    """Arguments are validated before the workspace is planned: on an oversized batch a bad k or
+    softmax scale is reported as such (not as a workspace shortfall) by both fused entry points,
+    still without touching a device."""
+    sq = FakeSeqs(dsa, [0, 5000], [0, 5000])
+    keep, p = buf(64)
+    a = dsa._FwdArgs()
+    a.H_I, a.d_I, a.qk_dtype = 64, 128, dsa.DSA_FP8_E4M3
+    a.q_idx = a.k_idx = a.w = p
+    a.H, a.d_qk, a.d_v, a.dtype = 128, 576, 512, dsa.DSA_BF16
+    a.q = a.kv = a.out = a.lse = p
+    a.softmax_scale = 0.04
+    for bad_k in (0, -5, 16385):
+        a.k = bad_k
+        assert dsa._c_fwd_na(sq.ref, ctypes.byref(a), None) == dsa.DSA_ERR_UNSUPPORTED
+        assert b"k = " in dsa._c_last()
+        assert dsa._c_fwd(sq.ref, ctypes.byref(a), None, 0, None) == dsa.DSA_ERR_UNSUPPORTED
+    a.k = 2048
+    a.softmax_scale = 0.0
+    assert dsa._c_fwd_na(sq.ref, ctypes.byref(a), None) == dsa.DSA_ERR_SHAPE
+    assert b"softmax_scale" in dsa._c_last()
+    a.softmax_scale = 0.04
+    a.H_I = -64
+    assert dsa._c_fwd_na(sq.ref, ctypes.byref(a), None) == dsa.DSA_ERR_SHAPE
+    a.H_I = 64
+    assert dsa._c_fwd_na(sq.ref, ctypes.byref(a), None) == dsa.DSA_ERR_WORKSPACE
