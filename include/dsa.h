@@ -213,6 +213,8 @@ dsa_status_t dsa_sparse_mla_attn(const dsa_seqs_t* seqs, int32_t H, int32_t d_qk
  * indexer runs only when scores_out is given, the top-k only when indices_out is given (or for
  * the fp32 attention), and the bf16 attention walks the candidates 0..pos directly (the pages'
  * dense short-context case). The indexer arguments are still validated.
+ * The call enqueues kernel launches only (no memset, copy or allocation), so it can be captured
+ * into a HIP graph with the workspace and buffers it was captured with.
  */
 typedef struct {
   /* indexer */
@@ -250,7 +252,10 @@ dsa_status_t dsa_forward(const dsa_seqs_t* seqs, const dsa_forward_args_t* args,
  * array of DSA_NOALLOC_SCRATCH_BYTES inside the library instead of a caller buffer. The call
  * allocates nothing (no hipMalloc, hipFree or allocating library routine).
  *   - Runs on the current device, whose own copy of the array it uses; `stream` must belong to
- *     that device. The array's address is looked up once per device (hipGetSymbolAddress).
+ *     that device. The array's address is looked up once per device (hipGetSymbolAddress), at
+ *     the first call there: make that call outside a graph capture. After it, the call enqueues
+ *     kernel launches only (no memset, copy or allocation) and can be captured into a HIP graph
+ *     and replayed; replays read the scratch's current contents like any later call.
  *   - Batches whose dsa_forward_workspace_size exceeds DSA_NOALLOC_SCRATCH_BYTES are rejected
  *     with DSA_ERR_WORKSPACE before anything is enqueued (decode batches of up to 128 rows of
  *     128K keys fit; long prefills do not).
