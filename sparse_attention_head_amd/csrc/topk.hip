@@ -125,19 +125,21 @@ topk_row_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __restri
 // with one block-wide exclusive scan in (tile, wave) order -- which is position order -- and
 // writes every selected position at its offset.
 
+// Exclusive prefix sums of a and b over the workgroup in thread order (b's in excl_b): a
+// data-parallel scan within each wave (lane moves, no LDS round trips), the wave totals through
+// sw (2 words per wave), then lane i < wave reads wave i's totals and one more wave scan adds
+// them up, so no thread walks the waves before it one by one. Begins the LDS exchange with a
+// barrier; every thread of the workgroup must call it.
 __device__ __forceinline__ uint32_t block_excl_scan2(uint32_t a, uint32_t b, uint32_t* sw,
                                                      uint32_t& excl_b) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t xa = a, xb = b;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t ta = __shfl_up(xa, off), tb = __shfl_up(xb, off);
-    if (lane >= off) { xa += ta; xb += tb; }
-  }
+  const uint32_t xa = wave_incl_scan(a), xb = wave_incl_scan(b);
   if (lane == 63) { sw[2 * wave] = xa; sw[2 * wave + 1] = xb; }
   __syncthreads();
-  uint32_t ba = 0, bb = 0;
-  for (int w = 0; w < wave; ++w) { ba += sw[2 * w]; bb += sw[2 * w + 1]; }
+  const uint32_t pa = wave_incl_scan(lane < wave ? sw[2 * lane] : 0u);
+  const uint32_t pb = wave_incl_scan(lane < wave ? sw[2 * lane + 1] : 0u);
+  const uint32_t ba = (uint32_t)__builtin_amdgcn_readlane((int)pa, 63);
+  const uint32_t bb = (uint32_t)__builtin_amdgcn_readlane((int)pb, 63);
   excl_b = bb + xb - b;
   return ba + xa - a;
 }
@@ -506,6 +508,7 @@ constexpr int TS_REGION = 5 * TS_GSTRIDE;  // sample | group arrays x, y, z, w, 
 static_assert(TS_SAMPLE <= TS_REGION, "the sample shares the region");
 static_assert(2 * TS_HCAP + TS_MAXN / 32 <= TS_REGION, "compacted list and bitmap share the region");
 constexpr int TS_UNROLL = 4;               // float4 loads per thread and batch (two batches in flight)
+constexpr int TS_UNROLL_PF = 8;            // the same with one workgroup per compute unit (PF launches)
 constexpr int TS_GPT = (TS_GCAP + TS_THREADS - 1) / TS_THREADS;   // groups per thread in the compaction
 
 // Largest of the four values (finite inputs: no NaN handling, which fmaxf would add per operand).
@@ -692,22 +695,25 @@ topk_stream_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __res
   }
   const int nw = (n + 31) >> 5;
   const int n4 = n & ~3;
-  // batches of TS_UNROLL float4 per lane, double-buffered (two register sets used in turn): the
-  // next batch is in flight while the current one is scanned. Buffer loads: one resource per
-  // batch (starting at the batch, covering the whole groups left in the row) and fixed lane
-  // offsets, so no per-load address arithmetic; groups past the end read as zero (scan_batch then
-  // sets them to -inf), so every batch issues the same TS_UNROLL loads.
-  constexpr int BATCH = TS_THREADS * 4 * TS_UNROLL;
-  auto load_batch = [&](int base, float4 (&v)[TS_UNROLL]) {
+  // batches of UNR float4 per lane, double-buffered (two register sets used in turn): the next
+  // batch is in flight while the current one is scanned. PF launches (one workgroup per compute
+  // unit, so registers to spare) take batches twice as large: there a long row's stream is bound
+  // by the bytes one compute unit keeps in flight. Buffer loads: one resource per batch (starting
+  // at the batch, covering the whole groups left in the row) and fixed lane offsets, so no
+  // per-load address arithmetic; groups past the end read as zero (scan_batch then sets them to
+  // -inf), so every batch issues the same UNR loads.
+  constexpr int UNR = PF ? TS_UNROLL_PF : TS_UNROLL;
+  constexpr int BATCH = TS_THREADS * 4 * UNR;
+  auto load_batch = [&](int base, float4 (&v)[UNR]) {
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float*>(row) + base, (short)0, max(n4 - base, 0) * 4, 0x00020000);
 #pragma unroll
-    for (int u = 0; u < TS_UNROLL; ++u) {
+    for (int u = 0; u < UNR; ++u) {
       const auto t = __builtin_amdgcn_raw_buffer_load_b128(rs, (u * TS_THREADS + tid) * 16, 0, 0);
       v[u] = make_float4(__uint_as_float(t[0]), __uint_as_float(t[1]), __uint_as_float(t[2]), __uint_as_float(t[3]));
     }
   };
-  float4 va[TS_UNROLL], vb[TS_UNROLL];
+  float4 va[UNR], vb[UNR];
 
   // 1. sample and floor
   const bool whole = n <= TS_SAMPLE;
@@ -779,17 +785,17 @@ topk_stream_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __res
     a[3 * TS_GSTRIDE] = __float_as_uint(v.w);
     a[4 * TS_GSTRIDE] = p;
   };
-  auto scan_batch = [&](int base, float4 (&v)[TS_UNROLL]) {
+  auto scan_batch = [&](int base, float4 (&v)[UNR]) {
     if (base + BATCH > n4) {   // uniform: the partial batch
 #pragma unroll
-      for (int u = 0; u < TS_UNROLL; ++u)
+      for (int u = 0; u < UNR; ++u)
         if (base + (u * TS_THREADS + tid) * 4 >= n4) v[u] = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
     }
-    bool sel[TS_UNROLL];      // group u reaches F
-    uint64_t m[TS_UNROLL];    // wave-uniform: the lanes where it does
+    bool sel[UNR];      // group u reaches F
+    uint64_t m[UNR];    // wave-uniform: the lanes where it does
     uint32_t hits = 0;
 #pragma unroll
-    for (int u = 0; u < TS_UNROLL; ++u) {
+    for (int u = 0; u < UNR; ++u) {
       sel[u] = max4(v[u]) >= Ff;
       m[u] = __ballot(sel[u]);
       hits += (uint32_t)__popcll(m[u]);
@@ -801,7 +807,7 @@ topk_stream_kernel(int B, const int32_t* __restrict__ cu_q, const int32_t* __res
       if (run + hits <= (uint32_t)TS_GCAP) {   // uniform; on overflow the row is redone exactly
         const uint32_t p0 = (uint32_t)(base + tid * 4);
 #pragma unroll
-        for (int u = 0; u < TS_UNROLL; ++u) {
+        for (int u = 0; u < UNR; ++u) {
           const uint32_t at4 = 4u * lanes_below_count(m[u]) + 4u * run;
           store_group(sel[u] ? at4 : spare4, v[u], p0 + (uint32_t)(u * TS_THREADS * 4));
           run += (uint32_t)__popcll(m[u]);
