@@ -808,6 +808,18 @@ attn_combine_kernel(int T, int nsplit, const uint16_t* __restrict__ part_o,
   const int64_t rh = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // row * H + head
   if (rh >= (int64_t)T * MH) return;
   const int64_t stride = (int64_t)T * MH;
+  // the first four splits' partial rows are requested together with the log2-sum-exps, before
+  // the weights are known: one memory round trip for up to four splits (every split writes its
+  // rows, an empty one zeros; steps past the last split re-read split 0 with weight 0)
+  auto load4 = [&](int sp, uint4 (&pk)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int s2 = sp + i < nsplit ? sp + i : 0;
+      pk[i] = *reinterpret_cast<const uint4*>(part_o + (s2 * stride + rh) * MDV + 8 * lane);
+    }
+  };
+  uint4 pk0[4];
+  load4(0, pk0);
   // lane s < nsplit holds split s's log2-sum-exp (nsplit <= 32)
   const float my_ls = lane < nsplit ? part_lse[lane * stride + rh] : -INFINITY;
   float M = my_ls;
@@ -817,17 +829,19 @@ attn_combine_kernel(int T, int nsplit, const uint16_t* __restrict__ part_o,
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
   if (M != -INFINITY) {
-    // four splits per step, their partial rows requested together (an empty split weighs
-    // 2^-inf = 0; steps past the last split re-read split 0 with weight 0)
+    // four splits per step (an empty split weighs 2^-inf = 0)
     for (int sp = 0; sp < nsplit; sp += 4) {
       uint4 pk[4];
       float w[4];
+      if (sp == 0) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int s2 = sp + i < nsplit ? sp + i : 0;
-        pk[i] = *reinterpret_cast<const uint4*>(part_o + (s2 * stride + rh) * MDV + 8 * lane);
-        w[i] = sp + i < nsplit ? __builtin_amdgcn_exp2f(__shfl(my_ls, sp + i) - M) : 0.f;
+        for (int i = 0; i < 4; ++i) pk[i] = pk0[i];
+      } else {
+        load4(sp, pk);
       }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        w[i] = sp + i < nsplit ? __builtin_amdgcn_exp2f(__shfl(my_ls, sp + i) - M) : 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         wsum += w[i];
