@@ -91,8 +91,10 @@ typedef struct {
  * for every query row r (sequence b, position pos) and s = 0..pos.
  * (paper digest page, "Key claims": paper section 2.1, Eq. 1; ReLU, few heads, FP8.)
  *
- *   qk_dtype  DSA_FP8_E4M3 (H_I = 64, d_I = 128: FP8 matrix-core path) or DSA_F32 (any
- *             1 <= H_I <= 128, 1 <= d_I <= 256: vector path). Accumulation is fp32.
+ *   qk_dtype  DSA_FP8_E4M3 (H_I = 64, d_I = 128: FP8 matrix-core path; at most 65535 sequences
+ *             per call) or DSA_F32 (any 1 <= H_I <= 128, 1 <= d_I <= 256, at most 65535 * 256
+ *             keys per sequence: vector path). Accumulation is fp32. Outside these limits the
+ *             call returns DSA_ERR_UNSUPPORTED.
  *   q_idx     [T, H_I, d_I] of qk_dtype        indexer queries
  *   k_idx     [Nk, d_I]     of qk_dtype        indexer keys, one per key token, shared by heads
  *   w         [T, H_I] fp32                    per-token head weights

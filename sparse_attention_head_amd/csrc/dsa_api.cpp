@@ -97,6 +97,13 @@ dsa_status_t check_indexer(const dsa::SeqInfo& s, int32_t H_I, int32_t d_I, dsa_
     return fail(DSA_ERR_UNSUPPORTED, "FP8 indexer needs max_seqlen_k * 128 < 2^31 (got %d keys)", s.max_n);
   if (dt == DSA_F32 && (H_I > 128 || d_I > 256 || H_I * d_I > 16384))
     return fail(DSA_ERR_UNSUPPORTED, "fp32 indexer supports H_I <= 128, d_I <= 256, H_I*d_I <= 16384");
+  // launch grids: the FP8 kernels give each sequence a grid layer, the fp32 kernel each 256-key
+  // slice of a row, and those grid dimensions hold at most 65535
+  if (dt == DSA_FP8_E4M3 && s.B > 65535)
+    return fail(DSA_ERR_UNSUPPORTED, "FP8 indexer takes at most 65535 sequences per call (got %d)", s.B);
+  if (dt == DSA_F32 && (s.max_n + 255) / 256 > 65535)
+    return fail(DSA_ERR_UNSUPPORTED, "fp32 indexer takes at most 65535 * 256 keys per sequence (got %d)",
+                s.max_n);
   return ok();
 }
 

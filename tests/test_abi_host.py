@@ -128,6 +128,17 @@ def test_seqs_validation(dsa):
     assert indexer(dsa, empty) == dsa.DSA_OK                            # B = 0: no-op
 
 
+def test_indexer_grid_limits(dsa):
+    """More sequences (FP8) or longer rows (fp32) than a launch grid dimension holds are refused
+    before any launch (only rejected shapes are tried here: an accepted call would launch on the
+    fake pointers)."""
+    many = np.arange(65537, dtype=np.int32)   # 65536 decode sequences of one key
+    assert indexer(dsa, FakeSeqs(dsa, many, many), ld=4) == dsa.DSA_ERR_UNSUPPORTED
+    long_k = 65535 * 256 + 1
+    assert indexer(dsa, FakeSeqs(dsa, [0, 1], [0, long_k]), dt=0, H_I=4, d_I=32,
+                   ld=(long_k + 3) // 4 * 4) == dsa.DSA_ERR_UNSUPPORTED
+
+
 def test_topk_and_attention_validation(dsa):
     sq = FakeSeqs(dsa, [0, 10], [0, 10])
     keep, p = buf(64)
