@@ -215,9 +215,6 @@ dsa_status_t dsa_sparse_mla_attn(const dsa_seqs_t* seqs, int32_t H, int32_t d_qk
  * indexer runs only when scores_out is given, the top-k only when indices_out is given (or for
  * the fp32 attention), and the bf16 attention walks the candidates 0..pos directly (the pages'
  * dense short-context case). The indexer arguments are still validated.
- * FP8 decode batches (every sequence at most one query row, k <= 2048, max_seqlen_k <= 131072)
- * select through the fused indexer -> top-k of dsa_indexer_topk (same indices as dsa_topk); the
- * workspace then holds its per-chunk candidates instead of the top-k's.
  * The call enqueues kernel launches only (no memset, copy or allocation), so it can be captured
  * into a HIP graph with the workspace and buffers it was captured with.
  */
@@ -261,10 +258,9 @@ dsa_status_t dsa_forward(const dsa_seqs_t* seqs, const dsa_forward_args_t* args,
  *     the first call there: make that call outside a graph capture. After it, the call enqueues
  *     kernel launches only (no memset, copy or allocation) and can be captured into a HIP graph
  *     and replayed; replays read the scratch's current contents like any later call.
- *   - A decode batch whose fused-selection candidates do not fit the array runs the separate
- *     indexer and top-k instead (same results); batches that need more than
- *     DSA_NOALLOC_SCRATCH_BYTES even then are rejected with DSA_ERR_WORKSPACE before anything
- *     is enqueued (decode batches of up to 128 rows of 128K keys fit; long prefills do not).
+ *   - Batches whose dsa_forward_workspace_size exceeds DSA_NOALLOC_SCRATCH_BYTES are rejected
+ *     with DSA_ERR_WORKSPACE before anything is enqueued (decode batches of up to 128 rows of
+ *     128K keys fit; long prefills do not).
  *   - Every call on a device shares that device's array: calls that overlap in time on one
  *     device (different streams, or threads) race and give wrong results; serialise them. The
  *     array keeps the last call's contents; nothing in it needs to start at zero.

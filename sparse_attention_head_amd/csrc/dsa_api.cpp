@@ -211,7 +211,7 @@ dsa_status_t run_attn(const dsa::SeqInfo& s, int32_t H, int32_t d_qk, int32_t d_
 
 struct ForwardPlan {
   int64_t ld;
-  bool dense, run_indexer, implicit_idx, run_topk, fused_topk;
+  bool dense, run_indexer, implicit_idx, run_topk;
   size_t index_off, index_bytes;
   size_t scores_off, scores_bytes;
   size_t idx_off, idx_bytes;
@@ -223,10 +223,7 @@ struct ForwardPlan {
 // Row stride of the scores the fused call keeps in its workspace: max_seqlen_k rounded up to 4.
 int64_t default_ld(const dsa::SeqInfo& s) { return std::max<int64_t>(4, ((int64_t)s.max_n + 3) / 4 * 4); }
 
-// fused: FP8 decode batches may select through the fused indexer -> top-k (the indexer keeps
-// each chunk's candidates, one merge per row: faster than the separate top-k on this GPU, same
-// indices); without it, the separate kernels, which need no candidate buffers.
-ForwardPlan plan_forward(const dsa::SeqInfo& s, const dsa_forward_args_t* a, bool fused = true) {
+ForwardPlan plan_forward(const dsa::SeqInfo& s, const dsa_forward_args_t* a) {
   ForwardPlan p{};
   p.ld = default_ld(s);
   // Short contexts: with at most k keys per sequence every row selects all its candidates, so
@@ -248,10 +245,7 @@ ForwardPlan plan_forward(const dsa::SeqInfo& s, const dsa_forward_args_t* a, boo
   p.idx_bytes = (a->indices_out || !p.run_topk) ? 0 : align_up((size_t)s.T * a->k * sizeof(int32_t));
   p.idx_off = off;
   off += p.idx_bytes;
-  p.fused_topk = fused && !p.dense && p.run_indexer && p.run_topk &&
-                 indexer_topk_fused(s, a->H_I, a->d_I, a->qk_dtype, a->k);
-  p.topk_bytes = !p.run_topk ? 0
-                 : align_up(p.fused_topk ? dsa::decode_cand_bytes(s, a->k) : dsa::topk_workspace_bytes(s, a->k));
+  p.topk_bytes = p.run_topk ? align_up(dsa::topk_workspace_bytes(s, a->k)) : 0;
   p.topk_off = off;
   off += p.topk_bytes;
   p.attn_bytes = align_up(dsa::attn_workspace_bytes(s, a->H, a->d_qk, a->d_v, a->k, a->dtype == DSA_BF16));
@@ -303,39 +297,6 @@ dsa_status_t scratch_address(void** out) {
   }
   *out = g_scratch_ptr[dev];
   return ok();
-}
-
-// The fused forward with plan p on workspace ws (arguments and workspace already validated).
-dsa_status_t forward_run(const dsa::SeqInfo& s, const dsa_forward_args_t* a, const ForwardPlan& p, void* ws,
-                         hipStream_t hs) {
-  dsa_status_t st;
-  const int64_t ld = a->scores_out ? a->ld_scores_out : p.ld;
-  char* base = static_cast<char*>(ws);
-  // (without the indexer, the top-k kernels never read the scores: every row has n <= k)
-  float* scores = a->scores_out ? a->scores_out
-                                : (p.scores_bytes ? reinterpret_cast<float*>(base + p.scores_off) : nullptr);
-  int32_t* idx = a->indices_out ? a->indices_out
-                                : (p.idx_bytes ? reinterpret_cast<int32_t*>(base + p.idx_off) : nullptr);
-  dsa::DecodeCand cand{};
-  if (p.fused_topk) cand = dsa::decode_cand_layout(s, a->k, base + p.topk_off);
-  if (p.run_indexer) {
-    st = run_indexer(s, a->H_I, a->d_I, a->qk_dtype, a->q_idx, a->q_idx_scale, a->k_idx,
-                     a->k_idx_scale, a->w, scores, ld, p.index_bytes ? base + p.index_off : nullptr, hs,
-                     p.fused_topk ? &cand : nullptr);
-    if (st != DSA_OK) return st;
-  }
-  if (p.fused_topk) {
-    st = hip_status(dsa::launch_topk_merge_decode(s, scores, ld, a->k, idx, cand, hs), "top-k merge launch");
-    if (st != DSA_OK) return st;
-  } else if (p.run_topk) {
-    st = hip_status(dsa::launch_topk(s, scores, ld, a->k, idx, p.topk_bytes ? base + p.topk_off : nullptr,
-                                     p.topk_bytes, hs),
-                    "top-k launch");
-    if (st != DSA_OK) return st;
-  }
-  return run_attn(s, a->H, a->d_qk, a->d_v, a->dtype, a->q, a->kv, p.implicit_idx ? nullptr : idx,
-                  a->k, a->softmax_scale, a->out, a->lse, p.attn_bytes ? base + p.attn_off : nullptr,
-                  p.attn_bytes, hs, p.run_topk);
 }
 
 }  // namespace
@@ -507,12 +468,33 @@ dsa_status_t dsa_forward(const dsa_seqs_t* seqs, const dsa_forward_args_t* a, vo
   st = check_forward(s, a);
   if (st != DSA_OK) return st;
   const ForwardPlan p = plan_forward(s, a);
+  const int64_t ld = a->scores_out ? a->ld_scores_out : p.ld;
   if (p.total > 0 && (!ws || ws_bytes < p.total))
     return fail(DSA_ERR_WORKSPACE, "forward workspace needs %zu bytes, got %zu", p.total, ws_bytes);
   if (ws && (reinterpret_cast<uintptr_t>(ws) % kAlign) != 0)
     return fail(DSA_ERR_ALIGN, "forward workspace must be %zu-byte aligned", kAlign);
   if (s.T == 0) return ok();
-  return forward_run(s, a, p, ws, static_cast<hipStream_t>(stream));
+  char* base = static_cast<char*>(ws);
+  // (without the indexer, the top-k kernels never read the scores: every row has n <= k)
+  float* scores = a->scores_out ? a->scores_out
+                                : (p.scores_bytes ? reinterpret_cast<float*>(base + p.scores_off) : nullptr);
+  int32_t* idx = a->indices_out ? a->indices_out
+                                : (p.idx_bytes ? reinterpret_cast<int32_t*>(base + p.idx_off) : nullptr);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (p.run_indexer) {
+    st = run_indexer(s, a->H_I, a->d_I, a->qk_dtype, a->q_idx, a->q_idx_scale, a->k_idx,
+                     a->k_idx_scale, a->w, scores, ld, p.index_bytes ? base + p.index_off : nullptr, hs);
+    if (st != DSA_OK) return st;
+  }
+  if (p.run_topk) {
+    st = hip_status(dsa::launch_topk(s, scores, ld, a->k, idx, p.topk_bytes ? base + p.topk_off : nullptr,
+                                     p.topk_bytes, hs),
+                    "top-k launch");
+    if (st != DSA_OK) return st;
+  }
+  return run_attn(s, a->H, a->d_qk, a->d_v, a->dtype, a->q, a->kv, p.implicit_idx ? nullptr : idx,
+                  a->k, a->softmax_scale, a->out, a->lse, p.attn_bytes ? base + p.attn_off : nullptr,
+                  p.attn_bytes, hs, p.run_topk);
 }
 
 dsa_status_t dsa_forward_noalloc(const dsa_seqs_t* seqs, const dsa_forward_args_t* args, void* stream) {
@@ -523,20 +505,17 @@ dsa_status_t dsa_forward_noalloc(const dsa_seqs_t* seqs, const dsa_forward_args_
   if (s.B == 0) return ok();
   st = check_forward(s, args);
   if (st != DSA_OK) return st;
-  // without room for the fused top-k's candidate buffers, the separate top-k (same indices)
-  ForwardPlan p = plan_forward(s, args);
-  if (p.total > DSA_NOALLOC_SCRATCH_BYTES) p = plan_forward(s, args, false);
-  if (p.total > DSA_NOALLOC_SCRATCH_BYTES)
+  const size_t need = plan_forward(s, args).total;
+  if (need > DSA_NOALLOC_SCRATCH_BYTES)
     return fail(DSA_ERR_WORKSPACE, "dsa_forward_noalloc: this batch needs %zu bytes of workspace, more than "
-                "the %llu-byte scratch (use dsa_forward with a caller workspace)", p.total,
+                "the %llu-byte scratch (use dsa_forward with a caller workspace)", need,
                 (unsigned long long)DSA_NOALLOC_SCRATCH_BYTES);
   void* ws = nullptr;
-  if (p.total > 0) {
+  if (need > 0) {
     st = scratch_address(&ws);
     if (st != DSA_OK) return st;
   }
-  if (s.T == 0) return ok();
-  return forward_run(s, args, p, ws, static_cast<hipStream_t>(stream));
+  return dsa_forward(seqs, args, ws, need, stream);
 }
 
 dsa_status_t dsa_indexer_alignment(const dsa_seqs_t* seqs, int32_t H, int32_t d_qk, dsa_dtype_t dtype,

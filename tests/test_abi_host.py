@@ -340,29 +340,6 @@ def test_noalloc_forward_rejects_oversized_batches_without_a_device(dsa):
     assert dsa._c_fwd_na(empty.ref, ctypes.byref(a), None) == dsa.DSA_OK
 
 
-@pytest.mark.skipif(os.path.exists("/dev/kfd"), reason="the accepted call would launch kernels on fake pointers")
-def test_noalloc_forward_falls_back_to_the_separate_topk(dsa):
-    """A decode batch whose fused-selection candidates do not fit the static scratch, while the
-    separate indexer and top-k do, is accepted by dsa_forward_noalloc: one row of 2100 keys makes
-    the candidate stride 1024 slots (67 MB for 64 rows of up to 128 chunks), which with the scores
-    and the split attention's partial rows exceeds the scratch. Without a GPU the call then stops
-    at the device query (DSA_ERR_HIP) instead of reporting a workspace shortfall."""
-    n = [2100] + [131072] * 63
-    sq = FakeSeqs(dsa, np.arange(65), np.concatenate([[0], np.cumsum(n)]))
-    keep, p = buf(64)
-    a = dsa._FwdArgs()
-    a.H_I, a.d_I, a.qk_dtype = 64, 128, dsa.DSA_FP8_E4M3
-    a.q_idx = a.k_idx = a.w = p
-    a.k = 2048
-    a.H, a.d_qk, a.d_v, a.dtype = 128, 576, 512, dsa.DSA_BF16
-    a.q = a.kv = a.out = a.lse = p
-    a.softmax_scale = 0.04
-    assert dsa._c_fwd_ws(sq.ref, ctypes.byref(a)) > dsa.NOALLOC_SCRATCH_BYTES
-    st = dsa._c_fwd_na(sq.ref, ctypes.byref(a), None)
-    assert st == dsa.DSA_ERR_HIP, dsa._c_last()
-    assert b"scratch" not in dsa._c_last()
-
-
 def test_noalloc_forward_checks_arguments_before_sizing(dsa):
     """Arguments are validated before the workspace is planned: on an oversized batch a bad k or
     softmax scale is reported as such (not as a workspace shortfall) by both fused entry points,
