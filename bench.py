@@ -14,7 +14,10 @@ and mean are reported beside it, and so is one back-to-back loop with warm cache
 step, each stage is timed alone the same way, and the dominant kernel's achieved rate is reported
 against the MI355X peak (roofline). The other workloads -- prefill8k, decode32k (64 x 32K),
 ragged (128 decode rows of 4K..128K keys) and short2k -- are timed the same way under `secondary`.
-The CPU oracle is timed on a bounded sample of the headline workload's rows (cpu_baseline).
+The CPU oracle is timed on a bounded sample of the headline workload's rows (cpu_baseline). A
+plain device copy of 256 MiB and of 1 GiB, timed the same way, goes under timing.plain_copy (bytes
+read plus written per second): what streaming reaches on this GPU, beside the datasheet peak the
+HBM-bound stages' fractions are quoted on.
 
 Progress goes to stderr; the result is one JSON line on stdout.
 """
@@ -135,6 +138,20 @@ class Timer:
             torch.cuda.synchronize()
             res["warm_mean"] = e0.elapsed_time(e1) / reps
         return res
+
+
+def copy_calibration(torch, timer, reps=7):
+    """What plain streaming reaches on this GPU (the context for the HBM-bound stages' fractions):
+    a device-to-device copy of 256 MiB and of 1 GiB, each rep after the usual cache flush, timed
+    with its own event pair; median rate of the bytes read plus written, GB/s, per size."""
+    out = {}
+    for nbytes in (256 << 20, 1 << 30):
+        src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        t = timer(lambda: dst.copy_(src), reps, 1)
+        out[f"{nbytes >> 20}MiB"] = {"ms": t["median"], "gbs": 2 * nbytes / (t["median"] / 1e3) / 1e9}
+        del src, dst
+    return out
 
 
 def setup(torch, dsa, dg, name, seed=0):
@@ -323,6 +340,9 @@ def main():
         secondary[name] = rec
         log(f"[bench] {name}: {json.dumps(rec)}")
 
+    copy_cal = copy_calibration(torch, timer)
+    log(f"[bench] plain copy: {json.dumps(copy_cal)}")
+
     if args.copy_calibration:
         a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         b = torch.empty_like(a)
@@ -344,7 +364,8 @@ def main():
                     H_I=wl.H_I, d_I=wl.d_I, k=wl.k, H=wl.H, d_qk=wl.d_qk, d_v=wl.d_v),
         timing=dict(protocol="cold cache: 1 GiB read before each step; one HIP event pair per step; "
                              "value and ms_per_step from the median step", ms_min=fused["min"],
-                    ms_mean=fused["mean"], ms_warm_loop=fused["warm_mean"]),
+                    ms_mean=fused["mean"], ms_warm_loop=fused["warm_mean"],
+                    plain_copy=copy_cal),
         roofline=roof, cpu_baseline=cpu, stages=stages, secondary=secondary,
     )
     print(json.dumps(res), flush=True)
