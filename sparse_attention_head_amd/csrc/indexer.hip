@@ -530,13 +530,26 @@ size_t indexer_workspace_bytes(const SeqInfo& s, bool fp8) {
   return (size_t)s.T * LIN_BYTES + ((size_t)s.T * sizeof(float) + 255) / 256 * 256;
 }
 
+// Workgroups of a launch with key chunks of kc that have keys to score: the tile of rows i0 ..
+// i0 + PF_ROWS - 1 of sequence b reaches position n_b - m_b + (its last row), so chunks 0 .. that
+// position / kc are scored and the rest of the grid column leaves at once (in a causal prefill
+// about half of the tile x chunk grid).
+static int64_t live_workgroups(const SeqInfo& s, int kc) {
+  int64_t total = 0;
+  for (int b = 0; b < s.B; ++b) {
+    const int m = s.cu_q_host[b + 1] - s.cu_q_host[b], n = s.cu_k_host[b + 1] - s.cu_k_host[b];
+    for (int i0 = 0; i0 < m; i0 += PF_ROWS) total += (n - m + min(m, i0 + PF_ROWS) - 1) / kc + 1;
+  }
+  return total;
+}
+
 // Key-chunk length: long enough to amortise loading the query tile (each chunk reads it again:
 // 16384-key chunks halve the query re-reads of 8192-key ones at the 128K chunk), short enough to
-// give several workgroups per compute unit. The scaled kernel keeps its chunk's key scales in LDS
-// and stays at 8192.
-static int pick_chunk(int64_t tiles, int max_n, int cus, int align, int kc_max) {
+// give several live workgroups per compute unit (counted over the causal part of the grid only:
+// the 8K prefill then takes 1024-key chunks, 1152 live workgroups, instead of 2048-key ones, 640).
+static int pick_chunk(const SeqInfo& s, int cus, int align, int kc_max) {
   int kc = kc_max;
-  while (kc > 512 && tiles * ((max_n + kc - 1) / kc) < 4LL * cus) kc >>= 1;
+  while (kc > 512 && live_workgroups(s, kc) < 4LL * cus) kc >>= 1;
   return (kc / align) * align;
 }
 
@@ -549,7 +562,7 @@ hipError_t launch_indexer_fp8_prefill(const SeqInfo& s, const uint8_t* q, const 
   hipLaunchKernelGGL(indexer_fp8_linear_kernel, dim3((s.T + 3) / 4), dim3(256), 0, st, s.T, q, w,
                      pieces, piece_exp);
   const int tiles = (s.max_m + PF_ROWS - 1) / PF_ROWS;
-  const int kc = pick_chunk((int64_t)tiles * s.B, s.max_n, kTargetCUs, PF_SK, PF_KC_MAX);
+  const int kc = pick_chunk(s, kTargetCUs, PF_SK, PF_KC_MAX);
   dim3 grid(tiles, (s.max_n + kc - 1) / kc, s.B);
   if (kscale)
     hipLaunchKernelGGL(indexer_fp8_prefill_kernel<true>, grid, dim3(PF_W * 64), 0, st, s.B, s.cu_q,
