@@ -121,6 +121,9 @@ SMALL = {
     "multiseq_k128": ([5, 37, 0, 130], [40, 37, 3, 700], 128),
     "decode_ragged_k2048": ([1, 1, 1, 1, 1], [1, 17, 300, 2100, 5000], 2048),
     "chunk_tail_k256": ([70], [1500], 256),
+    # k not a multiple of the attention's 64-entry blocks: the last block of a list is partial,
+    # and rows with at most k candidates (positions < 100) take the prefix-list path
+    "odd_k100": ([3, 150], [400, 150], 100),
 }
 
 
